@@ -1,0 +1,225 @@
+"""Benchmark of the decode hot path (and chunked prefill) on one MI355X.
+
+A step is one decode step of the 16-layer, 1,048,576-token workload ("long"
+in workloads.py): for every layer, rope the new query and the new key
+(YaRN x4), append the new key/value to the paged bf16 cache, and run split-K
+decode attention + merge over the 1,048,576 cached tokens.  All inputs are
+resident in HBM before the timed region starts.
+
+Prints one JSON line.  value = KV token-layers per second (16 x 1,048,576 per
+step / step time).  roofline = the decode attention launches (split + merge),
+timed with HIP events on the stream they run on, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KV_BYTES_PER_TOKEN_LAYER = 4096           # 4 KV heads x 256 x 2 B x (K, V)
+NVFP4_BYTES_PER_TOKEN_LAYER = 1152        # 4 x (128 code + 16 scale bytes) x (K, V)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes_per_launch(n_ctx, per_token):
+    # KV stream + q and out (24 heads x 256 x 2 B each) + the page table (4 B / 16 tokens)
+    return per_token * n_ctx + 2 * 24 * 256 * 2 + 4 * (n_ctx // 16)
+
+
+def build_step(W, Y, w, torch, dev):
+    """The 16 layers of a decode workload plus the per-step inputs."""
+    layers = []
+    for l in range(w.layers):
+        layers.append(W.build_decode_layer(w, l, device=dev, spare_page=True))
+        if l % 4 == 3:
+            log(f"{w.name}: built layer {l + 1}/{w.layers}")
+    N = w.n_ctx
+    L = w.layers
+    q_in = torch.empty((L, 24, 256), dtype=torch.bfloat16, device=dev)
+    k_in = torch.empty((L, 4, 256), dtype=torch.bfloat16, device=dev)
+    v_in = torch.empty((L, 4, 256), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        q_in[l:l + 1] = W.gen_q(w, l, 1, dev, token0=1)
+        W.gen_kv(w, l, 1, 1, k_in[l:l + 1], token0=N)
+        W.gen_kv(w, l, 2, 1, v_in[l:l + 1], token0=N)
+    q_work = torch.empty_like(q_in)
+    k_work = torch.empty_like(k_in)
+    outs, wss = zip(*[W.decode_outputs(w, dl, device=dev) for dl in layers])
+    pos_q = torch.full((L,), N, dtype=torch.int32, device=dev)
+    pos_new = torch.full((1,), N, dtype=torch.int32, device=dev)
+    yp = w.yarn()
+    ev = []
+
+    def step(timing=False):
+        q_work.copy_(q_in)
+        k_work.copy_(k_in)
+        Y.yarn_rope_apply(yp, q_work, pos_q)             # all layers' queries, one launch
+        Y.yarn_rope_apply(yp, k_work, pos_q)             # all layers' new keys
+        for l, dl in enumerate(layers):
+            Y.kv_append_quantize(dl.layer, k_work[l:l + 1], v_in[l:l + 1], dl.block_tables[0],
+                                 pos_new)
+            if timing:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            Y.decode_attention(dl.layer, q_work[l:l + 1], dl.block_tables, dl.seq_lens,
+                               dl.max_seq_len, outs[l], wss[l])
+            if timing:
+                e1.record()
+                ev.append((e0, e1))
+
+    return step, ev, layers
+
+
+def time_steps(step, ev, steps, warmup, torch):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev.clear()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(timing=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, sum(kern_ms) / len(kern_ms)
+
+
+def cpu_baseline(W, w):
+    """The oracle timed on one of the 16 layers (all 1,048,576 tokens, 24
+    query heads); inputs are prepared outside the timed call."""
+    import numpy as np
+    import oracle as O
+    import synth
+
+    N = w.n_ctx
+    t = O.yarn_table(original_max_position=w.orig)
+    q = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.Q), 0, 1, 24, 256), [N], t,
+               bf16_out=True)[0]
+    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, 4, 256),
+               np.arange(N), t, bf16_out=True)
+    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, 4, 256)
+    qf = O.bf16_to_f64(q)
+    t0 = time.perf_counter()
+    O.decode_attention(qf, k, v)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": N / dt, "unit": "KV token-layers/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 of 16 layers of the long workload: {N} cached tokens x 24 q heads, "
+                      f"fp64, {dt:.2f} s"}
+
+
+def bench_prefill(W, Y, torch, dev, reps):
+    w = W.WORKLOADS["prefill"]
+    case = W.build_prefill(w, device=dev)
+    out = torch.empty_like(case.q)
+    T = case.q.shape[0]
+    for _ in range(2):
+        Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = sum(case.q_start + i + 1 for i in range(T))
+    flops = 4.0 * 256 * pairs * 24
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "prefill: 8,192-token causal chunk at 1,040,384..1,048,575 over a "
+                        "1,048,576-token paged cache, 24 q / 4 KV heads",
+            "ms_per_chunk": ms, "tflops": tf, "flop_per_chunk": flops,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": None}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-nvfp4", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by KV head or by sequence range; no multi-GPU run "
+              "is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    import yarn_rope_kv_amd as Y
+
+    dev = "cuda:0"
+    w = W.WORKLOADS["long"]
+    log("building the 16-layer 1,048,576-token bf16 cache")
+    step, ev, layers = build_step(W, Y, w, torch, dev)
+    log("timing decode steps")
+    wall, kern_ms = time_steps(step, ev, args.steps, args.warmup, torch)
+    ms_step = wall / args.steps * 1e3
+    tokens = w.layers * w.n_ctx
+    value = tokens / (wall / args.steps)
+    bpl = decode_bytes_per_launch(w.n_ctx, KV_BYTES_PER_TOKEN_LAYER)
+    achieved = bpl / (kern_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode-attn KV tokens/s + HBM GB/s at 1,048,576 ctx; prefill attn TFLOP/s",
+        "value": value, "unit": "KV token-layers/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode step, 16 full-attention layers x 1,048,576 cached "
+                               "tokens (bf16, 16-token pages, seeded page permutation, planted "
+                               "needle), 24 q / 4 KV heads x 256, YaRN x4 from 262,144, batch 1",
+                   "layers": w.layers, "context": w.n_ctx, "batch": 1},
+        "kv_gbs": tokens * KV_BYTES_PER_TOKEN_LAYER / (wall / args.steps) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_attention (split + merge), per layer",
+                     "bytes_per_launch": bpl, "avg_launch_ms": kern_ms},
+    }
+    del layers, step, ev
+    torch.cuda.empty_cache()
+    if not args.no_nvfp4:
+        wf = W.WORKLOADS["long_fp4"]
+        log("building the NVFP4 16-layer cache")
+        stepf, evf, lf = build_step(W, Y, wf, torch, dev)
+        wallf, kf = time_steps(stepf, evf, max(3, args.steps // 2), args.warmup, torch)
+        bplf = decode_bytes_per_launch(wf.n_ctx, NVFP4_BYTES_PER_TOKEN_LAYER)
+        result["nvfp4_decode"] = {
+            "value": wf.layers * wf.n_ctx / (wallf / max(3, args.steps // 2)),
+            "unit": "KV token-layers/s", "avg_launch_ms": kf,
+            "roofline": {"bound": "hbm", "achieved": bplf / (kf * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bplf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+        del lf, stepf, evf
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("prefill")
+        try:
+            result["prefill"] = bench_prefill(W, Y, torch, dev, reps=3)
+        except Y.YrkError as e:
+            result["prefill"] = {"error": str(e)}
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(W, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,266 @@
+/*
+ * yrk.h -- C ABI of libyrk: YaRN-roped, GQA, paged long-context attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One data-parallel hot path: rotate queries and keys with a YaRN-stretched
+ * rotary table, append keys and values to a paged bf16 or NVFP4 KV cache,
+ * and run split-K decode attention and chunked causal prefill attention over
+ * that cache.
+ *
+ * Pages the definitions come from (cited by title and section):
+ *   [P1] "A 1,048,576-token context on two RTX 5090s: forking a C++ inference
+ *        engine for tensor-parallel and YaRN" (portfolio-site-axx.pages.dev)
+ *   [P3] "NInfer -- Windows 11 TP2 fork" README (git.onestrm.cn mirror)
+ *   [P5] "262,144 Tokens on One RTX 5090: Qwen3.8-27B with an NVFP4 KV Cache
+ *        That Actually Works" (stondo.github.io)
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers; everything else is host.
+ *   - The caller owns every buffer.  The library allocates nothing and keeps
+ *     no mutable global state; calls are thread-safe.
+ *   - Work is enqueued on `stream` and is asynchronous; device faults surface
+ *     at the caller's next synchronisation.
+ *   - Return value: YRK_OK (0) or a negative status.  Every error that the
+ *     host can detect is returned before anything is enqueued, so a failed
+ *     call writes nothing.  Errors only the device can see (a block id
+ *     outside the pool, a position beyond the block table) set bits in the
+ *     optional device word *dev_error_word (bitwise OR of YRK_DEVERR_*); the
+ *     offending write or read is skipped (a skipped key is masked out).
+ *   - bf16 is the bit pattern of IEEE binary32's upper 16 bits.
+ */
+#ifndef YRK_H
+#define YRK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define YRK_OK 0
+#define YRK_EINVAL (-1)  /* null pointer, bad shape, parameter outside its domain */
+#define YRK_ERANGE (-2)  /* a length or position beyond what the buffers / table can hold */
+#define YRK_ENOTSUP (-3) /* a shape or dtype this build has no kernel for */
+#define YRK_ENOSPC (-4)  /* workspace smaller than the size query returned */
+#define YRK_EDEVICE (-5) /* the HIP runtime refused a launch */
+
+#define YRK_DEVERR_BLOCK_ID 1u  /* a block-table entry outside [0, num_blocks) */
+#define YRK_DEVERR_POSITION 2u  /* a position < 0 or beyond the table / capacity */
+
+#define YRK_KV_BF16 0
+#define YRK_KV_NVFP4 1
+
+#define YRK_OUT_BF16 0
+#define YRK_OUT_F32 1
+
+/*
+ * YaRN parameters ([P1] "YaRN, and matching what vLLM actually does";
+ * [P3] "YaRN reference and drift guard" and "Usage").
+ *   rope_theta               rotary base (1e7 for the workload)
+ *   head_dim                 elements per head (256)
+ *   rotary_dim               leading dimensions that rotate (64); even, <= head_dim
+ *   factor                   YaRN scale s; finite, in [1, 64]; 1 = plain RoPE
+ *   original_max_position    trained window (262,144)
+ *   correction_max_position  length used for the correction range; 0 = the
+ *                            original window (the paper's formula, range
+ *                            (14, 22)); 4 x original reproduces the deployed
+ *                            range (16, 24)
+ *   beta_fast, beta_slow     turn counts bounding the correction range (32, 1)
+ *   mscale                   attention temperature on cos/sin; <= 0 derives
+ *                            0.1 ln s + 1 (1 when s == 1)
+ * Positions beyond original x factor are allowed: the window limit is a
+ * serving rule, not a limit of the arithmetic.
+ */
+typedef struct yrk_yarn_params {
+  double rope_theta;
+  int32_t head_dim;
+  int32_t rotary_dim;
+  double factor;
+  int64_t original_max_position;
+  int64_t correction_max_position;
+  double beta_fast;
+  double beta_slow;
+  double mscale;
+} yrk_yarn_params;
+
+/*
+ * One layer's KV cache, in caller-owned device memory.
+ *
+ * paged = 1 (the HND page layout of [P5] "Validation before vibes"; pages
+ * of [P1] "Things that bit me"; one shared pool, [P3] "Current limits"):
+ *   bf16:  k, v          [num_blocks][num_kv_heads][block_size][head_dim]       bf16
+ *   NVFP4: k, v          [num_blocks][num_kv_heads][block_size][head_dim / 2]   packed e2m1
+ *          k_scale, v_scale [num_blocks][num_kv_heads][block_size][head_dim / 16] e4m3
+ *   Logical token n of a sequence is block table[n / block_size], slot
+ *   n % block_size.
+ * paged = 0 (contiguous): the same rows as [capacity][num_kv_heads][row];
+ *   capacity = num_blocks * block_size; token n is row n; no block table.
+ *
+ * NVFP4 element codes: sign bit | 3-bit e2m1 magnitude; element 2j in the
+ * low nibble of byte j of a row.  One OCP E4M3FN scale per 16 consecutive
+ * head-dim elements.  k_tensor_scale_dev / v_tensor_scale_dev point to the
+ * fp32 tensor scale S of each tensor (device memory, one float).  The
+ * dequantised value is e2m1(code) * e4m3(scale) * S.
+ *
+ * This build supports head_dim 256 and block_size 16.
+ */
+typedef struct yrk_kv_layer {
+  int32_t dtype;          /* YRK_KV_BF16 or YRK_KV_NVFP4 */
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+  int32_t paged;
+  int32_t reserved;       /* must be 0 */
+  void* k;
+  void* v;
+  void* k_scale;
+  void* v_scale;
+  const float* k_tensor_scale_dev;
+  const float* v_tensor_scale_dev;
+} yrk_kv_layer;
+
+/*
+ * yrk_yarn_table -- host only.  The rotary inverse-frequency table of [P1]
+ * "YaRN, and matching what vLLM actually does": theta_i = rope_theta^(-2i/d)
+ * blended by a linear ramp over the correction range [low, high] between
+ * theta_i (below low) and theta_i / s (from high up), with
+ * corr(r) = d ln(L / (2 pi r)) / (2 ln rope_theta), low = floor(corr(beta_fast)),
+ * high = ceil(corr(beta_slow)), clamped to [0, d-1].
+ *   inv_freq_out   rotary_dim / 2 doubles (nullable)
+ *   mscale_out, corr_low_out, corr_high_out   (each nullable)
+ * Errors: YRK_EINVAL for null params or a parameter outside its domain.
+ */
+int yrk_yarn_table(const yrk_yarn_params* params, double* inv_freq_out, double* mscale_out,
+                   int32_t* corr_low_out, int32_t* corr_high_out);
+
+/*
+ * yrk_yarn_rope_apply -- rotate in place the first rotary_dim elements of
+ * each head of x: pair (i, i + rotary_dim/2) turns by position * inv_freq_i,
+ * cos and sin scaled by mscale ([P1] "YaRN, and matching what vLLM actually
+ * does": mscale sits inside the rope on the rotary dimensions only; [P3]
+ * "YaRN reference and drift guard": 64 of 256 dimensions).  The angle and
+ * the rotation are computed in fp64 and rounded once to bf16 (RNE);
+ * elements from rotary_dim on are not touched.
+ *   x_dev          bf16, token t head h at x + t*token_stride + h*head_dim
+ *   num_tokens     >= 0 (0 is a no-op)
+ *   num_heads      > 0, num_heads*head_dim <= token_stride
+ *   positions_dev  int32 [num_tokens], each >= 0 (negative positions are
+ *                  reported through nothing: they rotate the other way)
+ * Errors: YRK_EINVAL (null, bad params/shape), YRK_ENOTSUP (rotary_dim > 256).
+ */
+int yrk_yarn_rope_apply(const yrk_yarn_params* params, void* x_dev, int64_t num_tokens,
+                        int32_t num_heads, int64_t token_stride, const int32_t* positions_dev,
+                        hipStream_t stream);
+
+/*
+ * yrk_nvfp4_tensor_scale -- S = fl32(amax / (6 * 448)) of n bf16 values,
+ * amax = max |x|; amax == 0 gives S = 1.  Written to *scale_out_dev (one
+ * float, device).  This is the per-tensor scale of the NVFP4 format ([P5]
+ * "Why NVFP4 KV changes the math"; the tensor scale chosen as amax / (6*448)).
+ * Errors: YRK_EINVAL (null, n < 0).
+ */
+int yrk_nvfp4_tensor_scale(const void* x_dev, int64_t n, float* scale_out_dev,
+                           hipStream_t stream);
+
+/*
+ * yrk_kv_append_quantize -- write num_tokens new keys and values of one
+ * sequence into the cache.  Token t (k/v rows [num_tokens][num_kv_heads]
+ * [head_dim] bf16, contiguous) goes to logical position positions_dev[t].
+ *   bf16 cache:  an exact copy.
+ *   NVFP4 cache: per 16-element block, scale = RNE_e4m3(max|x| / (6 S)),
+ *                saturating at 448; codes = sign | RNE_e2m1(|x| / (e4m3(scale) S)),
+ *                ties to the even code, saturating at 6 ([P5] "Why NVFP4 KV
+ *                changes the math").  The decisions are exact: they equal
+ *                rounding the exact real quotients.
+ *   block_table_dev   int32 [block_table_len] (paged); NULL for contiguous
+ *   dev_error_word    nullable device uint32; positions outside the table or
+ *                     capacity, or table entries outside the pool, set a bit
+ *                     and that token is skipped.
+ * Errors: YRK_EINVAL, YRK_ENOTSUP (layout other than head_dim 256 / block 16).
+ */
+int yrk_kv_append_quantize(const yrk_kv_layer* layer, const void* k_dev, const void* v_dev,
+                           int64_t num_tokens, const int32_t* block_table_dev,
+                           int64_t block_table_len, const int32_t* positions_dev,
+                           uint32_t* dev_error_word, hipStream_t stream);
+
+/*
+ * yrk_decode_workspace_size -- bytes of device workspace that
+ * yrk_decode_attention needs for these sizes (the split partials: per
+ * sequence, query head and split, head_dim fp32 plus one fp32 log-sum-exp).
+ * Returns 0 for invalid sizes.
+ */
+size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int64_t max_seq_len);
+
+/*
+ * yrk_decode_attention -- one query per sequence attends to that sequence's
+ * seq_lens[s] cached tokens (logical positions 0 .. seq_lens[s]-1; the
+ * query's own key is not among them).  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).  Logits are softmax_scale * <q, k>
+ * (0 selects 1/sqrt(head_dim); YaRN adds no attention-level factor, [P1]
+ * "YaRN, and matching what vLLM actually does").  The cache is split into
+ * token ranges processed in parallel across compute units and merged by
+ * log-sum-exp ([P3] "Limitations": the decode split policy).
+ * seq_lens[s] == 0 gives a zero output row.
+ *   q_dev            bf16 [num_seqs][num_q_heads][head_dim] (already roped)
+ *   block_tables_dev int32 [num_seqs][block_table_stride] (paged); NULL for
+ *                    contiguous (num_seqs must then be 1)
+ *   seq_lens_dev     int32 [num_seqs], each in [0, max_seq_len]; larger values
+ *                    are clamped to max_seq_len and flagged
+ *   out_dev          [num_seqs][num_q_heads][head_dim], bf16 or fp32 (out_dtype)
+ *   workspace_dev    >= yrk_decode_workspace_size(...) bytes, 16-byte aligned
+ *   dev_error_word   nullable; see the conventions above
+ * Errors: YRK_EINVAL, YRK_ERANGE (max_seq_len beyond table or capacity),
+ * YRK_ENOTSUP (head_dim != 256, group size not in {1,2,3,4,6}),
+ * YRK_ENOSPC.
+ */
+int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                         int32_t num_q_heads, const int32_t* block_tables_dev,
+                         int64_t block_table_stride, const int32_t* seq_lens_dev,
+                         int64_t max_seq_len, float softmax_scale, void* out_dev,
+                         int32_t out_dtype, void* workspace_dev, size_t workspace_bytes,
+                         uint32_t* dev_error_word, hipStream_t stream);
+
+/*
+ * yrk_prefill_workspace_size -- bytes of device workspace that
+ * yrk_prefill_attention needs (0 in this build; kept so callers size it).
+ */
+size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t head_dim);
+
+/*
+ * yrk_prefill_attention -- causal attention of one chunk of num_q_tokens
+ * queries of one sequence at positions q_start_position .. +num_q_tokens-1
+ * over that sequence's cache, whose tokens 0 .. q_start_position +
+ * num_q_tokens - 1 must already be appended (the chunk's own keys
+ * included).  Query i attends to keys 0 .. q_start_position + i
+ * ([P1] "Against vLLM: prefill loses, decode wins": prompts are prefilled in
+ * chunks; the chunk attends causally).  QK^T and PV run on bf16 matrix cores
+ * with fp32 accumulation.
+ *   q_dev        bf16 [num_q_tokens][num_q_heads][head_dim] (already roped)
+ *   block_table_dev  int32 [block_table_len]; NULL for contiguous
+ *   out_dev      bf16 [num_q_tokens][num_q_heads][head_dim]
+ * Errors: YRK_EINVAL, YRK_ERANGE (positions beyond table or capacity),
+ * YRK_ENOTSUP (dtype other than bf16, head_dim != 256, group size other
+ * than 6), YRK_ENOSPC.
+ */
+int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t num_q_tokens,
+                          int32_t num_q_heads, int64_t q_start_position,
+                          const int32_t* block_table_dev, int64_t block_table_len,
+                          float softmax_scale, void* out_dev, void* workspace_dev,
+                          size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* yrk_status_string(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int yrk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YRK_H */

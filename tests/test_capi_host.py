@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, computes the host-only YaRN table like the oracle, and rejects bad
+arguments before enqueueing anything (no GPU needed: none of these calls
+reaches a launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import yarn_rope_kv_amd as Y
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "yrk.h")
+
+
+def test_every_declared_symbol_is_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^(?:int|size_t|const char\*)\s+(yrk_\w+)\(", text, re.M))
+    assert len(declared) >= 10
+    assert declared == set(Y.exported_symbols())
+    for name in declared:
+        assert hasattr(Y._lib, name)
+    assert Y._lib.yrk_abi_version() == 1
+
+
+@pytest.mark.parametrize("orig,corr,factor", [(262144, 0, 4.0), (262144, 1048576, 4.0),
+                                              (1024, 0, 4.0), (4096, 0, 1.0), (32768, 0, 16.0)])
+def test_library_table_matches_oracle(orig, corr, factor):
+    p = Y.YarnParams(original_max_position=orig, correction_max_position=corr, factor=factor)
+    inv, ms, lo, hi = Y.yarn_table(p)
+    t = O.yarn_table(original_max_position=orig, correction_max_position=corr, factor=factor)
+    assert (lo, hi) == (t.low, t.high)
+    assert ms == pytest.approx(t.mscale, rel=1e-15)
+    assert np.allclose(inv, t.inv_freq, rtol=4e-16, atol=0)
+
+
+def _rope(p, x=0x1000, T=1, H=24, stride=24 * 256, pos=0x2000):
+    cp = p.c()
+    return Y._lib.yrk_yarn_rope_apply(ctypes.byref(cp), x, T, H, stride, pos, None)
+
+
+@pytest.mark.parametrize("kw", [dict(factor=0.5), dict(factor=65.0), dict(factor=float("nan")),
+                                dict(rotary_dim=63), dict(rotary_dim=258), dict(rope_theta=1.0),
+                                dict(original_max_position=0), dict(beta_fast=0.5),
+                                dict(mscale=float("inf"))])
+def test_rope_rejects_bad_params(kw):
+    assert _rope(Y.YarnParams(**kw)) == Y.EINVAL
+
+
+def test_rope_rejects_bad_shapes_and_nulls():
+    p = Y.YarnParams()
+    assert _rope(p, stride=24 * 256 - 1) == Y.EINVAL
+    assert _rope(p, x=None) == Y.EINVAL
+    assert _rope(p, pos=None) == Y.EINVAL
+    assert _rope(p, T=-1) == Y.EINVAL
+    assert _rope(p, x=None, T=0) == Y.OK   # nothing to do, nothing touched
+
+
+def _layer(**kw):
+    base = dict(dtype=Y.KV_BF16, num_kv_heads=4, head_dim=256, block_size=16, num_blocks=64,
+                paged=1, reserved=0, k=0x10000, v=0x20000, k_scale=None, v_scale=None,
+                k_tensor_scale_dev=None, v_tensor_scale_dev=None)
+    base.update(kw)
+    return Y._KvLayerC(**base)
+
+
+def _decode(layer, S=1, Hq=24, bt=0x3000, stride=64, lens=0x4000, max_len=1024, out=0x5000,
+            out_dtype=Y.OUT_BF16, ws=0x6000, ws_bytes=1 << 30, q=0x7000, scale=0.0):
+    return Y._lib.yrk_decode_attention(ctypes.byref(layer), q, S, Hq, bt, stride, lens, max_len,
+                                       scale, out, out_dtype, ws, ws_bytes, None, None)
+
+
+def test_decode_validation():
+    L = _layer()
+    assert _decode(_layer(head_dim=128)) == Y.ENOTSUP
+    assert _decode(_layer(block_size=32)) == Y.ENOTSUP
+    assert _decode(_layer(dtype=7)) == Y.EINVAL
+    assert _decode(_layer(reserved=1)) == Y.EINVAL
+    assert _decode(_layer(dtype=Y.KV_NVFP4)) == Y.EINVAL     # scale planes missing
+    assert _decode(L, Hq=22) == Y.EINVAL                     # not a multiple of KV heads
+    assert _decode(L, Hq=40) == Y.ENOTSUP                    # group of 10
+    assert _decode(L, max_len=64 * 16 + 1) == Y.ERANGE       # beyond the block table
+    assert _decode(L, q=0x7001) == Y.EINVAL                  # misaligned
+    assert _decode(L, out_dtype=5) == Y.EINVAL
+    assert _decode(L, scale=-1.0) == Y.EINVAL
+    assert _decode(L, bt=None) == Y.EINVAL
+    assert _decode(L, ws_bytes=16) == Y.ENOSPC
+    assert _decode(_layer(paged=0), S=2, bt=None) == Y.EINVAL   # contiguous needs one sequence
+    assert _decode(_layer(paged=0), bt=None, max_len=64 * 16 + 1) == Y.ERANGE
+
+
+def test_decode_workspace_size_is_stable():
+    a = Y.decode_workspace_size(1, 24, 4, 1048576)
+    assert a == Y.decode_workspace_size(1, 24, 4, 1048576) > 0
+    assert Y.decode_workspace_size(0, 24, 4, 1048576) == 0
+    assert Y.decode_workspace_size(1, 24, 4, 1048576, head_dim=128) == 0
+    # partial outputs grow with the number of sequences, never below one split each
+    assert Y.decode_workspace_size(15, 24, 4, 131072) >= 15 * 24 * 257 * 4
+
+
+def test_append_validation():
+    L = _layer()
+    f = Y._lib.yrk_kv_append_quantize
+    assert f(ctypes.byref(L), 0x100, 0x200, 4, None, 0, 0x300, None, None) == Y.EINVAL
+    assert f(ctypes.byref(L), 0x100, 0x200, -1, 0x400, 4, 0x300, None, None) == Y.EINVAL
+    assert f(ctypes.byref(L), 0x101, 0x200, 4, 0x400, 4, 0x300, None, None) == Y.EINVAL
+    assert f(ctypes.byref(L), None, None, 0, 0x400, 4, None, None, None) == Y.OK
+    assert f(ctypes.byref(_layer(head_dim=64)), 0x100, 0x200, 4, 0x400, 4, 0x300, None,
+             None) == Y.ENOTSUP
+
+
+def test_prefill_validation():
+    L = _layer()
+    f = Y._lib.yrk_prefill_attention
+    args = lambda **kw: dict(dict(q=0x100, T=64, Hq=24, start=0, bt=0x400, bt_len=64, out=0x800),
+                             **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(ctypes.byref(kw.get("layer", L)), a["q"], a["T"], a["Hq"], a["start"], a["bt"],
+                 a["bt_len"], 0.0, a["out"], None, 0, None, None)
+
+    assert call(start=64 * 16 - 63) == Y.ERANGE
+    assert call(bt=None) == Y.EINVAL
+    assert call(Hq=8) == Y.ENOTSUP
+    assert call(T=-1) == Y.EINVAL
+    assert call(layer=_layer(dtype=Y.KV_NVFP4, k_scale=0x1, v_scale=0x1,
+                             k_tensor_scale_dev=0x10, v_tensor_scale_dev=0x10)) == Y.ENOTSUP
+    assert call(T=0, q=None, out=None) == Y.OK
+
+
+def test_tensor_scale_validation():
+    f = Y._lib.yrk_nvfp4_tensor_scale
+    assert f(0x100, -1, 0x200, None) == Y.EINVAL
+    assert f(0x100, 10, None, None) == Y.EINVAL
+    assert f(0x100, 10, 0x201, None) == Y.EINVAL
+
+
+def test_status_strings():
+    for s in (Y.OK, Y.EINVAL, Y.ERANGE, Y.ENOTSUP, Y.ENOSPC, Y.EDEVICE):
+        assert Y._lib.yrk_status_string(s)

@@ -1,0 +1,429 @@
+"""GPU parity: every kernel behind the C ABI against the fp64 oracle on the
+same seeded inputs.  Bit-exact for indexing, paging and NVFP4 codes/scales;
+attention within max |err| <= 1e-2 (bf16 output, fp32 accumulation)."""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ATOL = 1e-2
+STATS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                     "parity_stats.jsonl")
+
+
+def _say(msg):
+    print(f"[parity] {msg}", file=sys.stderr, flush=True)
+
+
+def _record(case, **kw):
+    if os.path.isdir(os.path.dirname(STATS)):
+        with open(STATS, "a") as f:
+            f.write(json.dumps(dict(case=case, **kw)) + "\n")
+
+
+@pytest.fixture(scope="module")
+def Y():
+    import yarn_rope_kv_amd
+    return yarn_rope_kv_amd
+
+
+@pytest.fixture(scope="module")
+def W():
+    import workloads
+    return workloads
+
+
+DEV = "cuda:0"
+
+
+def _bits(t):
+    """A bf16 CUDA tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _f64(t):
+    if t.dtype == torch.bfloat16:
+        return O.bf16_to_f64(_bits(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def _oracle_table(w):
+    return O.yarn_table(rope_theta=1e7, rotary_dim=64, factor=4.0, original_max_position=w.orig)
+
+
+def _compare_attention(case, gpu, ref, atol=ATOL):
+    err = np.abs(gpu - ref)
+    ref_b = O.bf16_to_f64(O.round_bf16(ref))
+    spacing = np.maximum(np.abs(ref_b) * 2.0 ** -7, 2.0 ** -133)
+    stats = dict(max_abs_err=float(err.max()), rel_l2=float(np.linalg.norm(gpu - ref) /
+                                                           max(np.linalg.norm(ref), 1e-300)),
+                 rel_l2_bf16_oracle=float(np.linalg.norm(ref_b - ref) /
+                                          max(np.linalg.norm(ref), 1e-300)),
+                 max_err_in_bf16_spacings=float((np.abs(gpu - ref_b) / spacing).max()),
+                 ref_rms=float(np.sqrt(np.mean(ref ** 2))))
+    _say(f"{case}: {stats}")
+    _record(case, **stats)
+    assert stats["max_abs_err"] <= atol, stats
+    return stats
+
+
+# -- generator ------------------------------------------------------------------
+
+def test_device_generator_matches_host():
+    w_tensor = torch.empty((300, 4, 256), dtype=torch.bfloat16, device=DEV)
+    mul = synth.outlier_channels(1002, 0, synth.K, 4, 256, 4, 8.0)
+    synth.dev_fill(w_tensor, 1002, 7, 1000, 300, 4, 256, chan_mul=mul, outlier_stream=9,
+                   outlier_p=0.01, outlier_mul=20.0)
+    host = synth.host_fill(1002, 7, 1000, 300, 4, 256, chan_mul=mul, outlier_stream=9,
+                           outlier_p=0.01, outlier_mul=20.0)
+    assert np.array_equal(_bits(w_tensor), host)
+
+
+# -- rope -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("orig,corr,factor", [(262144, 0, 4.0), (1024, 0, 4.0),
+                                              (262144, 1048576, 4.0), (4096, 0, 1.0)])
+def test_rope_matches_oracle(Y, orig, corr, factor):
+    _say(f"rope orig={orig} corr={corr} factor={factor}")
+    rng = np.random.default_rng(orig + corr)
+    pos = np.concatenate([[0, 1, 4095, 4096, 262143, 262144, 1048575, 1048576],
+                          rng.integers(0, 1 << 20, 56)]).astype(np.int64)
+    T = len(pos)
+    for H, stream in ((24, synth.Q), (4, synth.K)):
+        raw = synth.host_fill(77, stream, 0, T, H, 256)
+        x = torch.from_numpy(raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+        p = Y.YarnParams(original_max_position=orig, correction_max_position=corr, factor=factor)
+        Y.yarn_rope_apply(p, x, torch.from_numpy(pos.astype(np.int32)).to(DEV))
+        got = _bits(x)
+        t = O.yarn_table(original_max_position=orig, correction_max_position=corr, factor=factor)
+        ref = O.rope(raw, pos, t, bf16_out=True)
+        diff = got != ref
+        _record("rope", orig=orig, corr=corr, factor=factor, heads=H, mismatches=int(diff.sum()),
+                elements=int(diff.size))
+        # the only allowed difference is one bf16 step from fp64 noise at a rounding tie
+        assert np.all(np.abs(got.astype(np.int32) - ref.astype(np.int32))[diff] <= 1)
+        assert diff.sum() <= max(1, diff.size // 100000)
+        assert np.array_equal(got[..., 64:], raw[..., 64:])
+
+
+def test_rope_on_strided_rows(Y):
+    """q heads inside a wider per-token row (a fused projection output)."""
+    T, H = 9, 24
+    buf = torch.zeros((T, 40 * 256), dtype=torch.bfloat16, device=DEV)
+    raw = synth.host_fill(78, synth.Q, 0, T, H, 256)
+    buf[:, 256 * 8: 256 * 32] = torch.from_numpy(raw.view(np.int16)).to(DEV).view(
+        torch.bfloat16).reshape(T, -1)
+    view = buf[:, 256 * 8: 256 * 32].view(T, H, 256)
+    pos = np.arange(1040000, 1040000 + T)
+    Y.yarn_rope_apply(Y.YarnParams(), view, torch.from_numpy(pos.astype(np.int32)).to(DEV))
+    ref = O.rope(raw, pos, O.yarn_table(), bf16_out=True)
+    got = _bits(buf)
+    assert np.sum(_bits(view) != ref) <= 1
+    assert np.all(got[:, : 256 * 8] == 0) and np.all(got[:, 256 * 32:] == 0)
+
+
+# -- append -----------------------------------------------------------------------
+
+def test_append_bf16_paged_and_contiguous_bit_exact(Y):
+    T, pages = 200, 32
+    k_raw = synth.host_fill(90, 1, 0, T, 4, 256)
+    v_raw = synth.host_fill(90, 2, 0, T, 4, 256)
+    k = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    v = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    table = synth.block_permutation(90, pages)
+    pos = np.arange(T, dtype=np.int32)
+    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=True, device=DEV)
+    L.k.zero_(), L.v.zero_()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.kv_append_quantize(L, k, v, torch.from_numpy(table).to(DEV), torch.from_numpy(pos).to(DEV),
+                         err=err)
+    for pool, raw in ((L.k, k_raw), (L.v, v_raw)):
+        got = O.gather_paged(_bits(pool).view(np.uint8), pages, 4, 16, 512, table, T)
+        assert np.array_equal(got.view(np.uint16).reshape(T, 4, 256), raw)
+    assert int(err.item()) == 0
+    C = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=False, device=DEV)
+    perm = np.random.default_rng(1).permutation(T).astype(np.int32)   # out-of-order positions
+    Y.kv_append_quantize(C, k[perm], v[perm], None, torch.from_numpy(perm).to(DEV))
+    assert np.array_equal(_bits(C.k)[:T], k_raw) and np.array_equal(_bits(C.v)[:T], v_raw)
+
+
+def test_append_flags_bad_positions_and_pages(Y):
+    pages = 4
+    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=True, device=DEV)
+    L.k.zero_(), L.v.zero_()
+    table = torch.tensor([0, 1, 7, 3], dtype=torch.int32, device=DEV)   # page 2 -> 7: outside
+    k = torch.ones((3, 4, 256), dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pos = torch.tensor([5, 40, 70], dtype=torch.int32, device=DEV)      # 70 is beyond the table
+    Y.kv_append_quantize(L, k, k, table, pos, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == Y.DEVERR_BLOCK_ID | Y.DEVERR_POSITION
+    assert float(L.k.float().sum()) == 4 * 256                          # only position 5 written
+
+
+def test_tensor_scale_bit_exact(Y):
+    out = torch.empty(1, dtype=torch.float32, device=DEV)
+    for seed, rows, cut in ((3, 1 << 17, 0), (4, 1543, 3), (5, 1, 7)):
+        raw = synth.host_fill(seed, 1, 0, rows, 1, 8, outlier_stream=3, outlier_p=0.01,
+                              outlier_mul=20.0).reshape(-1)
+        raw = raw[: raw.size - cut]           # odd lengths exercise the tail loop
+        x = torch.from_numpy(raw.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+        Y.nvfp4_tensor_scale(x, out)
+        assert out.item() == float(O.nvfp4_tensor_scale(raw))
+    z = torch.zeros(100, dtype=torch.bfloat16, device=DEV)
+    Y.nvfp4_tensor_scale(z, out)
+    assert out.item() == 1.0
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_append_nvfp4_bit_exact(Y, paged):
+    T, pages = 300, 32
+    k_raw = synth.host_fill(91, 1, 0, T, 4, 256, outlier_stream=3, outlier_p=0.01,
+                            outlier_mul=20.0)
+    v_raw = synth.host_fill(91, 2, 0, T, 4, 256, outlier_stream=4, outlier_p=0.01,
+                            outlier_mul=20.0)
+    v_raw[5, 1, :16] = 0            # an all-zero block
+    v_raw[6, 2, 3] = 0x8000         # -0
+    k = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    v = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    L = Y.KVLayer.allocate(Y.KV_NVFP4, 4, pages, paged=paged, device=DEV)
+    Y.nvfp4_tensor_scale(k, L.k_tensor_scale)
+    Y.nvfp4_tensor_scale(v, L.v_tensor_scale)
+    table = synth.block_permutation(91, pages)
+    pos = np.arange(T, dtype=np.int32)
+    Y.kv_append_quantize(L, k, v, torch.from_numpy(table).to(DEV) if paged else None,
+                         torch.from_numpy(pos).to(DEV))
+    for raw, codes_t, scales_t, S_t in ((k_raw, L.k, L.k_scale, L.k_tensor_scale),
+                                        (v_raw, L.v, L.v_scale, L.v_tensor_scale)):
+        S = O.nvfp4_tensor_scale(raw)
+        assert S_t.item() == float(S)
+        c_ref, s_ref = O.nvfp4_quantize(raw, S)
+        packed_ref = O.nvfp4_pack(c_ref)
+        cb = codes_t.cpu().numpy()
+        sb = scales_t.cpu().numpy()
+        if paged:
+            got_c = O.gather_paged(cb.reshape(-1), pages, 4, 16, 128, table, T)
+            got_s = O.gather_paged(sb.reshape(-1), pages, 4, 16, 16, table, T)
+        else:
+            got_c, got_s = cb[:T], sb[:T]
+        assert np.array_equal(got_s.reshape(s_ref.shape), s_ref)
+        assert np.array_equal(got_c.reshape(packed_ref.shape), packed_ref)
+
+
+# -- decode -----------------------------------------------------------------------
+
+def _host_case(W, w, u, N=None):
+    """The oracle side of one layer / session: roped q (bits), roped K, V."""
+    N = w.n_ctx if N is None else N
+    t = _oracle_table(w)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, 24, 256)
+    q = O.rope(q_raw, [N], t, bf16_out=True)[0]
+    kw = {}
+    if w.elem_outlier_p:
+        kw = dict(outlier_p=w.elem_outlier_p, outlier_mul=20.0)
+    k_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.K), 0, N, 4, 256,
+                            chan_mul=W.chan_mul(w, u, synth.K),
+                            outlier_stream=synth.stream_id(u, synth.K_OUTLIER), **kw)
+    k = O.rope(k_raw, np.arange(N), t, bf16_out=True)
+    del k_raw
+    v = synth.host_fill(w.seed, synth.stream_id(u, synth.V), 0, N, 4, 256,
+                        chan_mul=W.chan_mul(w, u, synth.V),
+                        outlier_stream=synth.stream_id(u, synth.V_OUTLIER), **kw)
+    p_star = -1
+    if w.needle:
+        p_star = synth.needle_position(w.seed, u, N)
+        for g in range(4):
+            k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[6 * g]))
+    return q, k, v, p_star
+
+
+def _decode_gpu(W, dl, w):
+    out, ws = W.decode_outputs(w, dl, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    W.run_decode(dl, out, ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return out
+
+
+def test_decode_tiny_contiguous_f32(Y, W):
+    w = W.WORKLOADS["tiny"]
+    _say("decode tiny")
+    dl = W.build_decode_layer(w, 0, device=DEV, keep_raw=True)
+    out = _decode_gpu(W, dl, w)
+    q, k, v, _ = _host_case(W, w, 0)
+    assert np.array_equal(_bits(dl.q)[0], q)
+    assert np.array_equal(_bits(dl.k_roped), k)
+    ref = O.decode_attention(O.bf16_to_f64(q), k, v)
+    _compare_attention("tiny", _f64(out)[0], ref, atol=1e-4)
+
+
+@pytest.mark.parametrize("name,units", [("native", [0]), ("long", [0]), ("long", [11])])
+def test_decode_bf16_paged(Y, W, name, units):
+    w = W.WORKLOADS[name]
+    for u in units:
+        _say(f"decode {name} layer {u}")
+        dl = W.build_decode_layer(w, u, device=DEV)
+        out = _decode_gpu(W, dl, w)
+        gq = _bits(dl.q)[0]
+        del dl
+        torch.cuda.empty_cache()
+        q, k, v, p_star = _host_case(W, w, u)
+        assert np.array_equal(gq, q)
+        ref = O.decode_attention(O.bf16_to_f64(q), k, v)
+        got = _f64(out)[0]
+        _compare_attention(f"{name}/layer{u}", got, ref)
+        if p_star >= 0:
+            vf = O.bf16_to_f64(v[p_star])
+            for g in range(4):
+                assert np.abs(got[6 * g] - vf[g]).max() < 0.05
+
+
+def test_decode_sessions_batched(Y, W):
+    w = W.WORKLOADS["sessions"]
+    _say("decode sessions")
+    dl = W.build_decode_layer(w, 0, device=DEV)
+    out = _f64(_decode_gpu(W, dl, w))
+    del dl
+    torch.cuda.empty_cache()
+    for s in (0, 7, 14):
+        q, k, v, _ = _host_case(W, w, s)
+        ref = O.decode_attention(O.bf16_to_f64(q), k, v)
+        _compare_attention(f"sessions/{s}", out[s], ref)
+
+
+def test_decode_long_nvfp4_sampled_layer(Y, W):
+    w = W.WORKLOADS["long_fp4"]
+    u = 5
+    _say("decode long_fp4 layer 5")
+    dl = W.build_decode_layer(w, u, device=DEV, keep_raw=True)
+    out = _f64(_decode_gpu(W, dl, w))
+    kg = _bits(dl.k_roped)
+    L = dl.layer
+    kS, vS = L.k_tensor_scale.item(), L.v_tensor_scale.item()
+    table = dl.block_tables[0].cpu().numpy()
+    pages = L.num_blocks
+    kc = O.gather_paged(L.k.cpu().numpy().reshape(-1), pages, 4, 16, 128, table, w.n_ctx)
+    ks = O.gather_paged(L.k_scale.cpu().numpy().reshape(-1), pages, 4, 16, 16, table, w.n_ctx)
+    vc = O.gather_paged(L.v.cpu().numpy().reshape(-1), pages, 4, 16, 128, table, w.n_ctx)
+    vs = O.gather_paged(L.v_scale.cpu().numpy().reshape(-1), pages, 4, 16, 16, table, w.n_ctx)
+    del dl, L
+    torch.cuda.empty_cache()
+    q, k, v, _ = _host_case(W, w, u)
+    same = kg == k
+    _record("long_fp4/rope_k", mismatches=int((~same).sum()))
+    assert (~same).sum() <= k.size // 100000
+    del kg
+    assert kS == float(O.nvfp4_tensor_scale(k)) and vS == float(O.nvfp4_tensor_scale(v))
+    k_codes, k_scales = O.nvfp4_quantize(k, np.float32(kS))
+    v_codes, v_scales = O.nvfp4_quantize(v, np.float32(vS))
+    rows_ok = same.all(axis=-1)                  # rows whose roped input agrees bit for bit
+    assert np.array_equal(vs.reshape(v_scales.shape), v_scales)
+    assert np.array_equal(vc.reshape(-1, 4, 128), O.nvfp4_pack(v_codes))
+    assert np.array_equal(ks.reshape(k_scales.shape)[rows_ok], k_scales[rows_ok])
+    assert np.array_equal(kc.reshape(-1, 4, 128)[rows_ok], O.nvfp4_pack(k_codes)[rows_ok])
+    ref = O.decode_attention(O.bf16_to_f64(q), k_codes, v_codes,
+                             nvfp4=(k_scales, v_scales, kS, vS))
+    _compare_attention("long_fp4/layer5", out[0], ref)
+
+
+def test_decode_ragged_batch_and_empty(Y, W):
+    """One batched call over sequences of lengths 0, 1, 15, 16, 17, 1000 and
+    4097 (partial pages, a page-aligned end, an empty sequence)."""
+    lens = [0, 1, 15, 16, 17, 1000, 4097]
+    S, max_len = len(lens), 5000
+    pages_per = -(-max_len // 16)
+    pool = S * pages_per
+    perm = synth.block_permutation(123, pool).reshape(S, pages_per)
+    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pool, paged=True, device=DEV)
+    yp = Y.YarnParams()
+    qs, refs = [], []
+    for s, n in enumerate(lens):
+        q_raw = synth.host_fill(124, synth.stream_id(s, synth.Q), 0, 1, 24, 256)
+        k_raw = synth.host_fill(124, synth.stream_id(s, synth.K), 0, max(n, 1), 4, 256)
+        v_raw = synth.host_fill(124, synth.stream_id(s, synth.V), 0, max(n, 1), 4, 256)
+        qt = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+        Y.yarn_rope_apply(yp, qt, torch.tensor([n], dtype=torch.int32, device=DEV))
+        qs.append(qt)
+        if n:
+            kt = torch.from_numpy(k_raw[:n].view(np.int16)).to(DEV).view(torch.bfloat16)
+            vt = torch.from_numpy(v_raw[:n].view(np.int16)).to(DEV).view(torch.bfloat16)
+            pos = torch.arange(n, dtype=torch.int32, device=DEV)
+            Y.yarn_rope_apply(yp, kt, pos)
+            Y.kv_append_quantize(L, kt, vt, torch.from_numpy(perm[s]).to(DEV), pos)
+        t = O.yarn_table()
+        q = O.rope(q_raw, [n], t, bf16_out=True)[0]
+        k = O.rope(k_raw[:n], np.arange(n), t, bf16_out=True)
+        refs.append(O.decode_attention(O.bf16_to_f64(q), k, v_raw[:n]))
+    q = torch.cat(qs)
+    out = torch.empty((S, 24, 256), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(Y.decode_workspace_size(S, 24, 4, max_len), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.decode_attention(L, q, torch.from_numpy(perm).to(DEV),
+                       torch.tensor(lens, dtype=torch.int32, device=DEV), max_len, out, ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = _f64(out)
+    assert np.all(got[0] == 0)
+    for s in range(1, S):
+        _compare_attention(f"ragged/len{lens[s]}", got[s], refs[s])
+
+
+def test_decode_masks_and_flags_a_bad_page(Y, W):
+    n, pages = 300, 19
+    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=True, device=DEV)
+    table = synth.block_permutation(55, pages)
+    yp = Y.YarnParams()
+    q_raw = synth.host_fill(56, 0, 0, 1, 24, 256)
+    k_raw = synth.host_fill(56, 1, 0, n, 4, 256)
+    v_raw = synth.host_fill(56, 2, 0, n, 4, 256)
+    qt = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    kt = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    vt = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    pos = torch.arange(n, dtype=torch.int32, device=DEV)
+    Y.yarn_rope_apply(yp, qt, torch.tensor([n], dtype=torch.int32, device=DEV))
+    Y.yarn_rope_apply(yp, kt, pos)
+    bt = torch.from_numpy(table).to(DEV)
+    Y.kv_append_quantize(L, kt, vt, bt, pos)
+    bad = bt.clone()
+    bad[5] = pages + 3
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device=DEV)
+    ws = torch.empty(Y.decode_workspace_size(1, 24, 4, n), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.decode_attention(L, qt, bad.view(1, -1), torch.tensor([n], dtype=torch.int32, device=DEV),
+                       n, out, ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == Y.DEVERR_BLOCK_ID
+    t = O.yarn_table()
+    q = O.rope(q_raw, [n], t, bf16_out=True)[0]
+    k = O.rope(k_raw, np.arange(n), t, bf16_out=True)
+    keep = np.r_[0:80, 96:n]
+    ref = O.decode_attention(O.bf16_to_f64(q), k[keep], v_raw[keep])
+    _compare_attention("bad_page_masked", _f64(out)[0], ref, atol=1e-4)
+
+
+def test_decode_paged_equals_contiguous_and_repeats_bitwise(Y, W):
+    w = W.WORKLOADS["tiny"]
+    dl = W.build_decode_layer(w, 0, device=DEV, keep_raw=True)
+    out1, ws = W.decode_outputs(w, dl, device=DEV)
+    out2 = torch.empty_like(out1)
+    W.run_decode(dl, out1, ws)
+    W.run_decode(dl, out2, ws)
+    pages = w.pages_per_seq
+    P = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=True, device=DEV)
+    table = torch.from_numpy(synth.block_permutation(5, pages)).to(DEV)
+    Y.kv_append_quantize(P, dl.k_roped, dl.v, table,
+                         torch.arange(w.n_ctx, dtype=torch.int32, device=DEV))
+    out3 = torch.empty_like(out1)
+    Y.decode_attention(P, dl.q, table.view(1, -1), dl.seq_lens, dl.max_seq_len, out3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(out1, out3)

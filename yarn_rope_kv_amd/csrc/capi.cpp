@@ -1,0 +1,289 @@
+// The C ABI of libyrk (include/yrk.h): host-side validation, the YaRN table
+// and planning; kernels are enqueued only after every check has passed, so a
+// failed call writes nothing.
+#include "yrk.h"
+
+#include <cmath>
+#include <string.h>
+
+#include "yrk_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool is_finite(double x) { return __builtin_isfinite(x); }
+
+// Host-only YaRN table ([P1] "YaRN, and matching what vLLM actually does";
+// [P3] "YaRN reference and drift guard").  Pair i of the rotary dims has the
+// trained frequency theta_i = base^(-2i/d).  The correction range [low,
+// high] holds the pairs whose number of full turns over the correction
+// length L lies between beta_slow and beta_fast; below it frequencies are
+// kept, from `high` up they are divided by the factor, in between a linear
+// ramp blends the two.
+int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32_t* lo_out,
+               int32_t* hi_out) {
+  if (!p) return YRK_EINVAL;
+  const double base = p->rope_theta, s = p->factor;
+  const int d = p->rotary_dim;
+  if (!is_finite(base) || base <= 1.0) return YRK_EINVAL;
+  if (d <= 0 || (d & 1) || d > p->head_dim || p->head_dim <= 0) return YRK_EINVAL;
+  if (!is_finite(s) || s < 1.0 || s > 64.0) return YRK_EINVAL;
+  if (p->original_max_position <= 0 || p->correction_max_position < 0) return YRK_EINVAL;
+  if (!is_finite(p->beta_fast) || !is_finite(p->beta_slow) || p->beta_fast <= 0.0 ||
+      p->beta_slow <= 0.0 || p->beta_slow > p->beta_fast)
+    return YRK_EINVAL;
+  if (!is_finite(p->mscale)) return YRK_EINVAL;
+
+  const double L = (double)(p->correction_max_position > 0 ? p->correction_max_position
+                                                           : p->original_max_position);
+  const double ln_base = log(base);
+  // pair index at which a pair makes exactly `turns` full rotations over L
+  auto pair_at_turns = [&](double turns) {
+    return (double)d * log(L / (turns * 2.0 * M_PI)) / (2.0 * ln_base);
+  };
+  int32_t lo = (int32_t)floor(pair_at_turns(p->beta_fast));
+  int32_t hi = (int32_t)ceil(pair_at_turns(p->beta_slow));
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > d - 1 ? d - 1 : hi;
+  const double span = hi == lo ? 0.001 : (double)(hi - lo);
+  if (inv_freq) {
+    for (int i = 0; i < d / 2; ++i) {
+      const double theta = pow(base, -2.0 * (double)i / (double)d);
+      double w = ((double)i - (double)lo) / span;   // weight of the interpolated frequency
+      w = w < 0.0 ? 0.0 : (w > 1.0 ? 1.0 : w);
+      inv_freq[i] = theta * (1.0 - w) + (theta / s) * w;
+    }
+  }
+  if (mscale) *mscale = p->mscale > 0.0 ? p->mscale : (s > 1.0 ? 1.0 + 0.1 * log(s) : 1.0);
+  if (lo_out) *lo_out = lo;
+  if (hi_out) *hi_out = hi;
+  return YRK_OK;
+}
+
+int check_layer(const yrk_kv_layer* L) {
+  if (!L) return YRK_EINVAL;
+  if (L->dtype != YRK_KV_BF16 && L->dtype != YRK_KV_NVFP4) return YRK_EINVAL;
+  if (L->num_kv_heads <= 0 || L->head_dim <= 0 || L->block_size <= 0 || L->num_blocks <= 0)
+    return YRK_EINVAL;
+  if (L->paged != 0 && L->paged != 1) return YRK_EINVAL;
+  if (L->reserved != 0) return YRK_EINVAL;
+  if (!L->k || !L->v) return YRK_EINVAL;
+  if (L->dtype == YRK_KV_NVFP4 &&
+      (!L->k_scale || !L->v_scale || !L->k_tensor_scale_dev || !L->v_tensor_scale_dev))
+    return YRK_EINVAL;
+  if (L->head_dim != yrk::kHeadDim || L->block_size != yrk::kBlockSize) return YRK_ENOTSUP;
+  return YRK_OK;
+}
+
+yrk::KvGeometry geometry(const yrk_kv_layer* L) {
+  yrk::KvGeometry g;
+  g.num_kv_heads = L->num_kv_heads;
+  g.paged = L->paged;
+  g.num_blocks = L->num_blocks;
+  return g;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? YRK_OK : YRK_EDEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int yrk_abi_version(void) { return kAbiVersion; }
+
+const char* yrk_status_string(int status) {
+  switch (status) {
+    case YRK_OK: return "ok";
+    case YRK_EINVAL: return "invalid argument";
+    case YRK_ERANGE: return "length or position out of range";
+    case YRK_ENOTSUP: return "shape or dtype not supported by this build";
+    case YRK_ENOSPC: return "workspace too small";
+    case YRK_EDEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int yrk_yarn_table(const yrk_yarn_params* params, double* inv_freq_out, double* mscale_out,
+                   int32_t* corr_low_out, int32_t* corr_high_out) {
+  return yarn_table(params, inv_freq_out, mscale_out, corr_low_out, corr_high_out);
+}
+
+int yrk_yarn_rope_apply(const yrk_yarn_params* params, void* x_dev, int64_t num_tokens,
+                        int32_t num_heads, int64_t token_stride, const int32_t* positions_dev,
+                        hipStream_t stream) {
+  yrk::RopeArgs a;
+  int rc = yarn_table(params, a.inv_freq, &a.mscale, nullptr, nullptr);
+  if (rc) return rc;
+  if (params->rotary_dim / 2 > yrk::kMaxRotaryHalf) return YRK_ENOTSUP;
+  if (num_tokens < 0 || num_heads <= 0) return YRK_EINVAL;
+  if (token_stride < (int64_t)num_heads * params->head_dim) return YRK_EINVAL;
+  if (num_tokens == 0) return YRK_OK;
+  if (!x_dev || !positions_dev) return YRK_EINVAL;
+  a.x = static_cast<uint16_t*>(x_dev);
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.head_dim = params->head_dim;
+  a.token_stride = token_stride;
+  a.half = params->rotary_dim / 2;
+  a.positions = positions_dev;
+  return launch_status(yrk::launch_rope(a, stream));
+}
+
+int yrk_nvfp4_tensor_scale(const void* x_dev, int64_t n, float* scale_out_dev,
+                           hipStream_t stream) {
+  if (n < 0 || !scale_out_dev || (n > 0 && !x_dev)) return YRK_EINVAL;
+  if (((uintptr_t)scale_out_dev & 3u) != 0) return YRK_EINVAL;
+  return launch_status(
+      yrk::launch_tensor_scale(static_cast<const uint16_t*>(x_dev), n, scale_out_dev, stream));
+}
+
+int yrk_kv_append_quantize(const yrk_kv_layer* layer, const void* k_dev, const void* v_dev,
+                           int64_t num_tokens, const int32_t* block_table_dev,
+                           int64_t block_table_len, const int32_t* positions_dev,
+                           uint32_t* dev_error_word, hipStream_t stream) {
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  if (num_tokens < 0) return YRK_EINVAL;
+  if (layer->paged && (!block_table_dev || block_table_len <= 0)) return YRK_EINVAL;
+  if (num_tokens == 0) return YRK_OK;
+  if (!k_dev || !v_dev || !positions_dev) return YRK_EINVAL;
+  if (!aligned16(k_dev) || !aligned16(v_dev) || !aligned16(layer->k) || !aligned16(layer->v))
+    return YRK_EINVAL;
+  yrk::AppendArgs a;
+  a.geo = geometry(layer);
+  a.dtype = layer->dtype;
+  a.k_src = static_cast<const uint16_t*>(k_dev);
+  a.v_src = static_cast<const uint16_t*>(v_dev);
+  a.num_tokens = num_tokens;
+  a.block_table = layer->paged ? block_table_dev : nullptr;
+  a.block_table_len = layer->paged ? block_table_len : 0;
+  a.positions = positions_dev;
+  a.err = dev_error_word;
+  a.k_dst = layer->k;
+  a.v_dst = layer->v;
+  a.k_scale_dst = static_cast<uint8_t*>(layer->k_scale);
+  a.v_scale_dst = static_cast<uint8_t*>(layer->v_scale);
+  a.k_tensor_scale = layer->k_tensor_scale_dev;
+  a.v_tensor_scale = layer->v_tensor_scale_dev;
+  return launch_status(yrk::launch_append(a, stream));
+}
+
+size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int64_t max_seq_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != yrk::kHeadDim ||
+      max_seq_len < 0)
+    return 0;
+  const yrk::DecodePlan p = yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len);
+  return yrk::decode_workspace_bytes(num_seqs, num_q_heads, p);
+}
+
+int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                         int32_t num_q_heads, const int32_t* block_tables_dev,
+                         int64_t block_table_stride, const int32_t* seq_lens_dev,
+                         int64_t max_seq_len, float softmax_scale, void* out_dev,
+                         int32_t out_dtype, void* workspace_dev, size_t workspace_bytes,
+                         uint32_t* dev_error_word, hipStream_t stream) {
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len < 0) return YRK_EINVAL;
+  if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
+  if (!q_dev || !seq_lens_dev || !out_dev || !workspace_dev) return YRK_EINVAL;
+  if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
+  if (!aligned16(q_dev) || !aligned16(workspace_dev)) return YRK_EINVAL;
+  const int group = num_q_heads / layer->num_kv_heads;
+  if (group != 1 && group != 2 && group != 3 && group != 4 && group != 6)
+    return YRK_ENOTSUP;
+  if (layer->paged) {
+    if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
+    if (max_seq_len > block_table_stride * yrk::kBlockSize) return YRK_ERANGE;
+  } else {
+    if (num_seqs != 1) return YRK_EINVAL;
+    if (max_seq_len > layer->num_blocks * yrk::kBlockSize) return YRK_ERANGE;
+  }
+  if (max_seq_len > INT32_MAX) return YRK_ERANGE;
+  yrk::DecodeArgs a;
+  a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len);
+  const size_t need = yrk::decode_workspace_bytes(num_seqs, num_q_heads, a.plan);
+  if (workspace_bytes < need) return YRK_ENOSPC;
+  if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
+  a.geo = geometry(layer);
+  a.dtype = layer->dtype;
+  a.group = group;
+  a.num_q_heads = num_q_heads;
+  a.num_seqs = num_seqs;
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.k = layer->k;
+  a.v = layer->v;
+  a.k_scale = static_cast<const uint8_t*>(layer->k_scale);
+  a.v_scale = static_cast<const uint8_t*>(layer->v_scale);
+  a.k_tensor_scale = layer->k_tensor_scale_dev;
+  a.v_tensor_scale = layer->v_tensor_scale_dev;
+  a.block_tables = layer->paged ? block_tables_dev : nullptr;
+  a.block_table_stride = layer->paged ? block_table_stride : 0;
+  a.seq_lens = seq_lens_dev;
+  a.max_seq_len = max_seq_len;
+  a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
+  a.out = out_dev;
+  a.out_f32 = out_dtype == YRK_OUT_F32;
+  const size_t slots = (size_t)num_seqs * num_q_heads * a.plan.num_splits;
+  a.ws_o = static_cast<float*>(workspace_dev);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace_dev) +
+                                      ((slots * yrk::kHeadDim * sizeof(float) + 255) / 256) * 256);
+  a.err = dev_error_word;
+  return launch_status(yrk::launch_decode(a, stream));
+}
+
+size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t head_dim) {
+  (void)num_q_tokens;
+  (void)num_q_heads;
+  (void)head_dim;
+  return 0;
+}
+
+int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t num_q_tokens,
+                          int32_t num_q_heads, int64_t q_start_position,
+                          const int32_t* block_table_dev, int64_t block_table_len,
+                          float softmax_scale, void* out_dev, void* workspace_dev,
+                          size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream) {
+  (void)workspace_dev;
+  (void)workspace_bytes;
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  if (num_q_tokens < 0 || num_q_heads <= 0 || q_start_position < 0) return YRK_EINVAL;
+  if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
+  if (layer->paged && (!block_table_dev || block_table_len <= 0)) return YRK_EINVAL;
+  const int64_t end = q_start_position + num_q_tokens;
+  if (end > INT32_MAX) return YRK_ERANGE;
+  if (layer->paged ? end > block_table_len * yrk::kBlockSize
+                   : end > layer->num_blocks * yrk::kBlockSize)
+    return YRK_ERANGE;
+  if (num_q_tokens == 0) return YRK_OK;
+  if (!q_dev || !out_dev) return YRK_EINVAL;
+  if (!aligned16(q_dev) || !aligned16(out_dev)) return YRK_EINVAL;
+  if (layer->dtype != YRK_KV_BF16) return YRK_ENOTSUP;
+  const int group = num_q_heads / layer->num_kv_heads;
+  if (group != 6) return YRK_ENOTSUP;
+  if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
+  yrk::PrefillArgs a;
+  a.geo = geometry(layer);
+  a.group = group;
+  a.num_q_heads = num_q_heads;
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.k = static_cast<const uint16_t*>(layer->k);
+  a.v = static_cast<const uint16_t*>(layer->v);
+  a.num_q_tokens = num_q_tokens;
+  a.q_start = q_start_position;
+  a.block_table = layer->paged ? block_table_dev : nullptr;
+  a.block_table_len = layer->paged ? block_table_len : 0;
+  a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
+  a.out = static_cast<uint16_t*>(out_dev);
+  a.err = dev_error_word;
+  return launch_status(yrk::launch_prefill(a, stream));
+}
+
+}  // extern "C"

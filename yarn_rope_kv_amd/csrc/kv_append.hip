@@ -1,0 +1,235 @@
+// KV append into the paged cache: an exact bf16 copy, or NVFP4 quantisation
+// on the way in; plus the per-tensor NVFP4 scale.
+//
+// Paging follows [P1] "Things that bit me" (per-sequence page lists), [P3]
+// "Current limits" (one shared pool fixed at start-up) and the HND page
+// layout of [P5] "Validation before vibes": a page holds, per KV head, 16
+// consecutive token rows.  The NVFP4 format is the one of [P5] "Why NVFP4 KV
+// changes the math": e2m1 element codes, one e4m3 scale per 16 contiguous
+// head-dim elements, one fp32 tensor scale S = amax / (6 * 448).
+#include "device_common.h"
+#include "yrk_internal.h"
+
+namespace yrk {
+namespace {
+
+constexpr int kChunksPerRow = kHeadDim * 2 / 16;  // 16-byte chunks of a bf16 row
+constexpr int kQBlocks = kHeadDim / 16;           // NVFP4 scale blocks per row
+
+// Row index (in units of one head row) of logical position `pos` for KV head
+// h, or -1 after flagging the error.
+__device__ __forceinline__ int64_t cache_row(const KvGeometry& g, const int32_t* table,
+                                             int64_t table_len, int32_t pos, int h,
+                                             uint32_t* err, bool report) {
+  if (g.paged) {
+    const int64_t b = pos / kBlockSize;
+    if (pos < 0 || b >= table_len) {
+      if (report) set_error(err, kErrPosition);
+      return -1;
+    }
+    const int64_t blk = table[b];
+    if (blk < 0 || blk >= g.num_blocks) {
+      if (report) set_error(err, kErrBlockId);
+      return -1;
+    }
+    return (blk * g.num_kv_heads + h) * kBlockSize + pos % kBlockSize;
+  }
+  if (pos < 0 || (int64_t)pos >= g.num_blocks * kBlockSize) {
+    if (report) set_error(err, kErrPosition);
+    return -1;
+  }
+  return (int64_t)pos * g.num_kv_heads + h;
+}
+
+// One thread copies one 16-byte chunk of K and the matching chunk of V.
+__global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
+  const int H = a.geo.num_kv_heads;
+  const int64_t total = a.num_tokens * H * kChunksPerRow;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total; gid += stride) {
+    const int64_t t = gid / (H * kChunksPerRow);
+    const int rem = (int)(gid - t * H * kChunksPerRow);
+    const int h = rem / kChunksPerRow;
+    const int c = rem % kChunksPerRow;
+    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
+                                  a.err, c == 0);
+    if (row < 0) continue;
+    const int64_t src = (t * H + h) * kChunksPerRow + c;
+    const int64_t dst = row * kChunksPerRow + c;
+    reinterpret_cast<uint4*>(a.k_dst)[dst] = reinterpret_cast<const uint4*>(a.k_src)[src];
+    reinterpret_cast<uint4*>(a.v_dst)[dst] = reinterpret_cast<const uint4*>(a.v_src)[src];
+  }
+}
+
+// ---- NVFP4 -----------------------------------------------------------------
+
+// e4m3 (OCP E4M3FN) value of a non-negative code 0x00..0x7E, exact.
+__device__ __forceinline__ double e4m3_value(int code) {
+  const int e = code >> 3, m = code & 7;
+  return e == 0 ? (double)m * 0x1p-9 : ldexp((double)(8 + m), e - 10);
+}
+
+// Nearest e4m3 code to q >= 0, ties to even mantissa, saturating at 448.
+// Works on the IEEE-754 binary64 fields of q: keep 3 fraction bits (or the
+// subnormal multiple of 2^-9) and round the dropped bits half-to-even.
+__device__ __forceinline__ int e4m3_encode(double q) {
+  if (!(q < 448.0)) return 0x7E;
+  if (q == 0.0) return 0;
+  const uint64_t u = (uint64_t)__double_as_longlong(q);
+  const int E = (int)(u >> 52) - 1023;           // q is a normal fp64 here
+  const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  if (E >= -6) {
+    // keep the leading 1 + 3 bits: drop 49 bits
+    uint64_t keep = sig >> 49;
+    const uint64_t rest = sig & ((1ull << 49) - 1);
+    const uint64_t half = 1ull << 48;
+    if (rest > half || (rest == half && (keep & 1))) ++keep;   // may carry to 16
+    int code = ((E + 7) << 3) + (int)(keep - 8);               // carry bumps the exponent
+    return code > 0x7E ? 0x7E : code;
+  }
+  // subnormal target: k = RNE(q * 2^9) = RNE(sig * 2^(E - 43))
+  const int shift = 43 - E;  // >= 50
+  if (shift >= 64) return 0;
+  uint64_t keep = sig >> shift;
+  const uint64_t rest = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rest > half || (rest == half && (keep & 1))) ++keep;
+  return (int)keep;  // 0..8; 8 is the smallest normal, code 0x08
+}
+
+// Quantise 16 bf16 values: returns the scale code and writes 8 packed bytes
+// (element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, double S,
+                                               uint2* packed) {
+  uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bmax = max(bmax, w[i] & 0x7fffu);
+    bmax = max(bmax, (w[i] >> 16) & 0x7fffu);
+  }
+  const double b = (double)bf16_to_f32((uint16_t)bmax);   // |x| ordering == bit ordering
+  const int qs = e4m3_encode(b / (6.0 * S));
+  const double eff = e4m3_value(qs) * S;                  // exact in fp64
+  // Decision points between neighbouring e2m1 magnitudes, scaled by eff.  At
+  // a point exactly between two codes the even code wins: >= where the upper
+  // code is even, > where the lower one is.
+  const double t0 = 0.25 * eff, t1 = 0.75 * eff, t2 = 1.25 * eff, t3 = 1.75 * eff;
+  const double t4 = 2.5 * eff, t5 = 3.5 * eff, t6 = 5.0 * eff;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
+    const double a = (double)bf16_to_f32((uint16_t)(bits & 0x7fffu));
+    uint32_t mag = 0;
+    if (eff > 0.0)
+      mag = (uint32_t)(a > t0) + (uint32_t)(a >= t1) + (uint32_t)(a > t2) + (uint32_t)(a >= t3) +
+            (uint32_t)(a > t4) + (uint32_t)(a >= t5) + (uint32_t)(a > t6);
+    const uint32_t code = ((bits >> 15) << 3) | mag;
+    out[i >> 3] |= code << (4 * (i & 7));
+  }
+  packed->x = out[0];
+  packed->y = out[1];
+  return (uint32_t)qs;
+}
+
+// One thread quantises one 16-element block of K and the matching block of V.
+__global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
+  const int H = a.geo.num_kv_heads;
+  const int64_t total = a.num_tokens * H * kQBlocks;
+  const double kS = (double)*a.k_tensor_scale;
+  const double vS = (double)*a.v_tensor_scale;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total; gid += stride) {
+    const int64_t t = gid / (H * kQBlocks);
+    const int rem = (int)(gid - t * H * kQBlocks);
+    const int h = rem / kQBlocks;
+    const int qb = rem % kQBlocks;
+    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
+                                  a.err, qb == 0);
+    if (row < 0) continue;
+    const int64_t src = ((t * H + h) * kHeadDim + qb * 16) / 8;  // in uint4 units
+    const uint4* ks = reinterpret_cast<const uint4*>(a.k_src) + src;
+    const uint4* vs = reinterpret_cast<const uint4*>(a.v_src) + src;
+    uint2 kp, vp;
+    const uint32_t kq = quantize16(ks[0], ks[1], kS, &kp);
+    const uint32_t vq = quantize16(vs[0], vs[1], vS, &vp);
+    reinterpret_cast<uint2*>(a.k_dst)[row * kQBlocks + qb] = kp;
+    reinterpret_cast<uint2*>(a.v_dst)[row * kQBlocks + qb] = vp;
+    a.k_scale_dst[row * kQBlocks + qb] = (uint8_t)kq;
+    a.v_scale_dst[row * kQBlocks + qb] = (uint8_t)vq;
+  }
+}
+
+// ---- tensor scale ----------------------------------------------------------
+
+__global__ void store_word_kernel(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
+}
+
+// Largest |x| as bf16 magnitude bits (for finite bf16, |x| orders like the
+// low 15 bits); NaN patterns are ignored.
+__global__ __launch_bounds__(256) void amax_bits_kernel(const uint16_t* x, int64_t n,
+                                                        uint32_t* out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto take = [&m](uint32_t bits) {
+    const uint32_t a = bits & 0x7fffu;
+    if (a <= 0x7f80u) m = max(m, a);
+  };
+  if (((uintptr_t)x & 15u) == 0) {
+    const int64_t n8 = n / 8;
+    const uint4* x8 = reinterpret_cast<const uint4*>(x);
+    for (int64_t i = tid; i < n8; i += stride) {
+      const uint4 w = x8[i];
+      take(w.x); take(w.x >> 16); take(w.y); take(w.y >> 16);
+      take(w.z); take(w.z >> 16); take(w.w); take(w.w >> 16);
+    }
+    for (int64_t i = n8 * 8 + tid; i < n; i += stride) take(x[i]);
+  } else {
+    for (int64_t i = tid; i < n; i += stride) take(x[i]);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+}
+
+__global__ void finalize_scale_kernel(float* out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const uint32_t bits = *reinterpret_cast<uint32_t*>(out);
+    const float amax = bf16_to_f32((uint16_t)bits);
+    *out = amax == 0.0f ? 1.0f : amax / 2688.0f;
+  }
+}
+
+unsigned grid_for(int64_t work, int64_t cap) {
+  int64_t b = (work + 255) / 256;
+  if (b < 1) b = 1;
+  return (unsigned)(b > cap ? cap : b);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    const int64_t work = a.num_tokens * a.geo.num_kv_heads * kChunksPerRow;
+    hipLaunchKernelGGL(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+  } else {
+    const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
+    hipLaunchKernelGGL(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s) {
+  uint32_t* word = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(store_word_kernel, dim3(1), dim3(64), 0, s, word, 0u);
+  if (n > 0)
+    hipLaunchKernelGGL(amax_bits_kernel, dim3(grid_for(n / 8 + 1, 8192)), dim3(256), 0, s, x, n,
+                       word);
+  hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(64), 0, s, out);
+  return hipGetLastError();
+}
+
+}  // namespace yrk

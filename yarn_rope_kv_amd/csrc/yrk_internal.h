@@ -1,0 +1,111 @@
+// Internal launch interface between the C-ABI layer (capi.cpp, host
+// validation) and the gfx950 kernels (*.hip).  Every launcher assumes its
+// arguments were validated by the caller and only enqueues work.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace yrk {
+
+constexpr int kHeadDim = 256;   // elements per head this build supports
+constexpr int kBlockSize = 16;  // tokens per KV page
+constexpr int kMaxRotaryHalf = 128;
+constexpr uint32_t kErrBlockId = 1u;   // same bits as YRK_DEVERR_BLOCK_ID
+constexpr uint32_t kErrPosition = 2u;  // same bits as YRK_DEVERR_POSITION
+
+struct RopeArgs {
+  uint16_t* x;
+  int64_t num_tokens;
+  int32_t num_heads;
+  int32_t head_dim;
+  int64_t token_stride;
+  int32_t half;                    // rotary_dim / 2
+  const int32_t* positions;
+  double mscale;
+  double inv_freq[kMaxRotaryHalf];
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+
+// Where one token row of one KV head lives.
+struct KvGeometry {
+  int32_t num_kv_heads;
+  int32_t paged;
+  int64_t num_blocks;
+};
+
+struct AppendArgs {
+  KvGeometry geo;
+  int32_t dtype;
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t num_tokens;
+  const int32_t* block_table;
+  int64_t block_table_len;
+  const int32_t* positions;
+  uint32_t* err;
+  void* k_dst;
+  void* v_dst;
+  uint8_t* k_scale_dst;
+  uint8_t* v_scale_dst;
+  const float* k_tensor_scale;
+  const float* v_tensor_scale;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s);
+
+struct DecodePlan {
+  int32_t num_splits;
+  int64_t tokens_per_split;  // multiple of 4 * kBlockSize
+};
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const DecodePlan& p);
+
+struct DecodeArgs {
+  KvGeometry geo;
+  int32_t dtype;
+  int32_t group;        // q heads per kv head
+  int32_t num_q_heads;
+  int32_t num_seqs;
+  const uint16_t* q;
+  const void* k;
+  const void* v;
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
+  const float* k_tensor_scale;
+  const float* v_tensor_scale;
+  const int32_t* block_tables;
+  int64_t block_table_stride;
+  const int32_t* seq_lens;
+  int64_t max_seq_len;
+  float scale_log2;     // softmax scale * log2(e)
+  void* out;
+  int32_t out_f32;
+  float* ws_o;          // [S][Hq][splits][256]
+  float* ws_lse;        // [S][Hq][splits]   (log2 domain)
+  uint32_t* err;
+  DecodePlan plan;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+  KvGeometry geo;
+  int32_t group;
+  int32_t num_q_heads;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t num_q_tokens;
+  int64_t q_start;
+  const int32_t* block_table;
+  int64_t block_table_len;
+  float scale_log2;
+  uint16_t* out;
+  uint32_t* err;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace yrk
