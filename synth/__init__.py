@@ -69,6 +69,7 @@ def _host():
 def _dev():
     if not os.path.exists(DEV_LIB):
         raise ImportError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
+    import torch  # noqa: F401  (bind to the HIP runtime torch already loaded)
     lib = ctypes.CDLL(DEV_LIB)
     lib.synth_dev_fill_bf16.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -122,7 +123,7 @@ def dev_fill(out, seed, stream, token0, ntok, nheads, dim, chan_mul=None, outlie
                                     outlier_threshold(outlier_p), outlier_mul, out.data_ptr(),
                                     torch.cuda.current_stream(dev).cuda_stream)
     if rc != 0:
-        raise RuntimeError("synth_dev_fill_bf16 failed")
+        raise RuntimeError(f"synth_dev_fill_bf16 failed (status {rc})")
     return out
 
 

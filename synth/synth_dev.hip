@@ -75,9 +75,13 @@ extern "C" int synth_dev_fill_bf16(uint64_t seed, uint64_t stream, int64_t token
   int64_t n8 = ntok * row / 8;
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(fill_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream_h,
-                     stream_key(seed, stream), stream_key(seed, outlier_stream),
-                     (uint64_t)token0 * (uint64_t)row, n8, (int32_t)row, table, chan_mul,
-                     outlier_thresh, outlier_mul, out);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  // The launch's own status (not the sticky last-error state).
+  uint64_t key = stream_key(seed, stream), okey = stream_key(seed, outlier_stream);
+  uint64_t first = (uint64_t)token0 * (uint64_t)row;
+  int32_t row32 = (int32_t)row;
+  void* args[] = {&key, &okey, &first, &n8, &row32, &table, &chan_mul, &outlier_thresh,
+                  &outlier_mul, &out};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fill_bf16_kernel),
+                                       dim3((unsigned)blocks), dim3(256), args, 0, stream_h);
+  return e == hipSuccess ? 0 : -(int)e;
 }

@@ -26,6 +26,11 @@ HEAD_DIM, BLOCK_SIZE = 256, 16
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
                       "there is no fallback path")
+# torch brings its own HIP runtime.  Load it before libyrk so that libyrk's
+# libamdhip64 dependency resolves to that same, already-loaded runtime: two
+# HIP runtimes in one process do not share devices, memory or streams.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 

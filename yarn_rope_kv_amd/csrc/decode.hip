@@ -249,6 +249,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
         }
       }
       softmax_update<G>(sc, m, l, acc);
+      // Rows past the end of the sequence (or of a masked page) hold whatever
+      // the pool holds; their weight is 0, but 0 * NaN is not, so clear them.
+      if (!ok || (page + 1) * kBlockSize > tok1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (!(ok && page * kBlockSize + 4 * j + r < tok1))
+            vr[j][0] = vr[j][1] = make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float vf[16];
@@ -388,6 +396,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
         }
       }
       softmax_update<G>(sc, m, l, acc);
+      // Stale codes and scales decode to finite values, so p = 0 already
+      // cancels them; clearing keeps masked rows exactly out of the sum.
+      if (!ok || (page + 1) * kBlockSize > tok1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (!(ok && page * kBlockSize + 4 * j + r < tok1)) {
+            vc[j] = make_uint2(0, 0);
+            vsc[j] = 0;
+          }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float vf[16];
@@ -464,11 +482,8 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge(DecodeArgs a) {
 template <int G>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.plan.num_splits, a.geo.num_kv_heads, a.num_seqs);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL(decode_split_bf16<G>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_split_nvfp4<G>, grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  if (a.dtype == 0) return launch(decode_split_bf16<G>, grid, dim3(kThreads), 0, st, a);
+  return launch(decode_split_nvfp4<G>, grid, dim3(kThreads), 0, st, a);
 }
 
 }  // namespace
@@ -509,8 +524,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge, dim3(a.num_q_heads, a.num_seqs), dim3(kHeadDim), 0, st, a);
-  return hipGetLastError();
+  return launch(decode_merge, dim3(a.num_q_heads, a.num_seqs), dim3(kHeadDim), 0, st, a);
 }
 
 }  // namespace yrk

@@ -6,6 +6,19 @@
 
 namespace yrk {
 
+template <typename T>
+struct same_type { using type = T; };
+
+// Enqueue a kernel and return the launch's own status.  (Reading the sticky
+// hipGetLastError() state instead would also report an error some earlier,
+// unrelated call left behind.)
+template <typename... KArgs>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, typename same_type<KArgs>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -214,22 +214,19 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   if (a.dtype == 0) {
     const int64_t work = a.num_tokens * a.geo.num_kv_heads * kChunksPerRow;
-    hipLaunchKernelGGL(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
-  } else {
-    const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
-    hipLaunchKernelGGL(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+    return launch(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
   }
-  return hipGetLastError();
+  const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
+  return launch(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
 }
 
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s) {
   uint32_t* word = reinterpret_cast<uint32_t*>(out);
-  hipLaunchKernelGGL(store_word_kernel, dim3(1), dim3(64), 0, s, word, 0u);
-  if (n > 0)
-    hipLaunchKernelGGL(amax_bits_kernel, dim3(grid_for(n / 8 + 1, 8192)), dim3(256), 0, s, x, n,
-                       word);
-  hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(64), 0, s, out);
-  return hipGetLastError();
+  hipError_t e = launch(store_word_kernel, dim3(1), dim3(64), 0, s, word, 0u);
+  if (e == hipSuccess && n > 0)
+    e = launch(amax_bits_kernel, dim3(grid_for(n / 8 + 1, 8192)), dim3(256), 0, s, x, n, word);
+  if (e == hipSuccess) e = launch(finalize_scale_kernel, dim3(1), dim3(64), 0, s, out);
+  return e;
 }
 
 }  // namespace yrk

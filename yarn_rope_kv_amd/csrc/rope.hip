@@ -73,8 +73,7 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   if (k.total == 0) return hipSuccess;
   int64_t blocks = (k.total + 255) / 256;
   if (blocks > 1 << 20) blocks = 1 << 20;
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)blocks), dim3(256), 0, s, k);
-  return hipGetLastError();
+  return launch(rope_kernel, dim3((unsigned)blocks), dim3(256), 0, s, k);
 }
 
 }  // namespace yrk
