@@ -444,3 +444,92 @@ def test_decode_paged_equals_contiguous_and_repeats_bitwise(Y, W):
     Y.decode_attention(P, dl.q, table.view(1, -1), dl.seq_lens, dl.max_seq_len, out3, ws)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(out1, out3)
+
+
+# -- prefill ----------------------------------------------------------------------
+
+def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None):
+    total = n_prior + T
+    pages = -(-total // 16) + 1
+    t = O.yarn_table()
+    k_raw = synth.host_fill(seed, 1, 0, total, 4, 256)
+    v_raw = synth.host_fill(seed, 2, 0, total, 4, 256)
+    q_raw = synth.host_fill(seed, 0, 0, T, 24, 256)
+    yp = Y.YarnParams()
+    kt = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    vt = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    qt = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    pos_all = torch.arange(total, dtype=torch.int32, device=DEV)
+    Y.yarn_rope_apply(yp, kt, pos_all)
+    Y.yarn_rope_apply(yp, qt, pos_all[n_prior:])
+    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=paged, device=DEV)
+    table = synth.block_permutation(seed, pages) if paged else None
+    bt = torch.from_numpy(table).to(DEV) if paged else None
+    Y.kv_append_quantize(L, kt, vt, bt, pos_all)
+    if bad_page is not None:
+        bt = bt.clone()
+        bt[bad_page] = pages + 5
+    out = torch.empty_like(qt)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.prefill_attention(L, qt, n_prior, bt, out, err=err)
+    torch.cuda.synchronize()
+    k = O.rope(k_raw, np.arange(total), t, bf16_out=True)
+    q = O.rope(q_raw, np.arange(n_prior, total), t, bf16_out=True)
+    return _f64(out), O.bf16_to_f64(q), k, v_raw, int(err.item())
+
+
+@pytest.mark.parametrize("n_prior,T,paged", [(1000, 77, True), (0, 200, False),
+                                             (4093, 130, True), (31, 1, True)])
+def test_prefill_small_matches_oracle(Y, n_prior, T, paged):
+    _say(f"prefill n_prior={n_prior} T={T} paged={paged}")
+    got, q, k, v, err = _prefill_small(Y, n_prior, T, paged, seed=300 + T)
+    assert err == 0
+    ref = O.prefill_attention(q, np.arange(n_prior, n_prior + T), k, v)
+    _compare_attention(f"prefill/{n_prior}+{T}", got, ref)
+    if n_prior == 0:
+        vf = O.bf16_to_f64(v)
+        for h in range(24):      # the first row sees only key 0
+            assert np.abs(got[0, h] - vf[0, h // 6]).max() <= np.abs(vf[0]).max() * 2 ** -8
+
+
+def test_prefill_flags_and_masks_a_bad_page(Y):
+    n_prior, T = 500, 40
+    got, q, k, v, err = _prefill_small(Y, n_prior, T, True, seed=77, bad_page=3)
+    assert err == Y.DEVERR_BLOCK_ID
+    keep = np.r_[0:48, 64:n_prior + T]
+    refs = []
+    for i in range(T):
+        p = n_prior + i
+        kk = keep[keep <= p]
+        refs.append(O.decode_attention(q[i], k[kk], v[kk]))
+    _compare_attention("prefill/bad_page", got, np.stack(refs))
+
+
+def test_prefill_workload_sampled_rows(Y, W):
+    """The full chunk (8,192 queries at 1,040,384..1,048,575 over a
+    1,048,576-token paged cache) in the bench's launch configuration; rows
+    checked one by one against the oracle."""
+    w = W.WORKLOADS["prefill"]
+    _say("prefill workload")
+    case = W.build_prefill(w, device=DEV)
+    out = torch.empty_like(case.q)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rows = [0, 1, 31, 4097, 8190, 8191]
+    got = _f64(out[rows])
+    qg = _bits(case.q[rows])
+    del case, out
+    torch.cuda.empty_cache()
+    N, q0 = w.n_ctx, w.n_ctx - w.prefill_chunk
+    t = _oracle_table(w)
+    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, 4, 256), np.arange(N),
+               t, bf16_out=True)
+    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, 4, 256)
+    for j, r in enumerate(rows):
+        q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0 + r, 1, 24, 256)
+        q = O.rope(q_raw, [q0 + r], t, bf16_out=True)[0]
+        assert np.array_equal(q, qg[j])
+        ref = O.decode_attention(O.bf16_to_f64(q), k[: q0 + r + 1], v[: q0 + r + 1])
+        _compare_attention(f"prefill_workload/row{r}", got[j], ref)

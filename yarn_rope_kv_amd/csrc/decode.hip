@@ -437,27 +437,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 
 // ---- merge ------------------------------------------------------------------
 
-// One workgroup per (query head, sequence), one thread per head dimension:
+// Grid (4 x q_head, seq), 256 threads: a workgroup owns 64 head dims of one
+// (sequence, query head); its 4 waves each walk every 4th split, and the 4
+// partial (max, sum, weighted output) triples are combined through LDS:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // Splits that saw no token carry lse = -inf and weigh nothing.
-__global__ __launch_bounds__(kHeadDim) void decode_merge(DecodeArgs a) {
-  const int qh = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+constexpr int kMergeGroups = 4;
+constexpr int kMergeDims = kHeadDim / 4;
+
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  __shared__ float sm_m[kMergeGroups], sm_l[kMergeGroups];
+  __shared__ float sm_o[kMergeGroups][kMergeDims];
+  const int qh = blockIdx.x >> 2, chunk = blockIdx.x & 3, s = blockIdx.y;
+  const int grp = threadIdx.x >> 6, dl = threadIdx.x & 63;
+  const int d = chunk * kMergeDims + dl;
   const int nsp = a.plan.num_splits;
   const int64_t slot0 = ((int64_t)s * a.num_q_heads + qh) * nsp;
   const float* lse = a.ws_lse + slot0;
   const float* o = a.ws_o + slot0 * kHeadDim + d;
   float M = -INFINITY;
-  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, lse[sp]);
-  float res = 0.f;
+  for (int sp = grp; sp < nsp; sp += kMergeGroups) M = fmaxf(M, lse[sp]);
+  float L = 0.f, O = 0.f;
   if (M != -INFINITY) {
-    float L = 0.f, O = 0.f;
-    int sp = 0;
-    for (; sp + 4 <= nsp; sp += 4) {
+    int sp = grp;
+    for (; sp + 3 * kMergeGroups < nsp; sp += 4 * kMergeGroups) {
       float w[4], v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        w[u] = fast_exp2(lse[sp + u] - M);
-        v[u] = o[(int64_t)(sp + u) * kHeadDim];
+        w[u] = fast_exp2(lse[sp + u * kMergeGroups] - M);
+        v[u] = o[(int64_t)(sp + u * kMergeGroups) * kHeadDim];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -465,18 +473,39 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge(DecodeArgs a) {
         O = fmaf(w[u], v[u], O);
       }
     }
-    for (; sp < nsp; ++sp) {
+    for (; sp < nsp; sp += kMergeGroups) {
       const float w = fast_exp2(lse[sp] - M);
       L += w;
       O = fmaf(w, o[(int64_t)sp * kHeadDim], O);
     }
-    res = O / L;
   }
-  const int64_t oi = ((int64_t)s * a.num_q_heads + qh) * kHeadDim + d;
-  if (a.out_f32)
-    static_cast<float*>(a.out)[oi] = res;
-  else
-    static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(res);
+  if (dl == 0) {
+    sm_m[grp] = M;
+    sm_l[grp] = L;
+  }
+  sm_o[grp][dl] = O;
+  __syncthreads();
+  if (grp == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int g2 = 0; g2 < kMergeGroups; ++g2) Mt = fmaxf(Mt, sm_m[g2]);
+    float res = 0.f;
+    if (Mt != -INFINITY) {
+      float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < kMergeGroups; ++g2) {
+        const float sc = sm_m[g2] == -INFINITY ? 0.f : fast_exp2(sm_m[g2] - Mt);
+        Lt += sm_l[g2] * sc;
+        Ot += sm_o[g2][dl] * sc;
+      }
+      res = Ot / Lt;
+    }
+    const int64_t oi = ((int64_t)s * a.num_q_heads + qh) * kHeadDim + d;
+    if (a.out_f32)
+      static_cast<float*>(a.out)[oi] = res;
+    else
+      static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(res);
+  }
 }
 
 template <int G>
@@ -524,7 +553,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  return launch(decode_merge, dim3(a.num_q_heads, a.num_seqs), dim3(kHeadDim), 0, st, a);
+  return launch(decode_merge, dim3(4 * a.num_q_heads, a.num_seqs), dim3(256), 0, st, a);
 }
 
 }  // namespace yrk
