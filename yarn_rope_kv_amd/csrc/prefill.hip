@@ -46,7 +46,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 6;                 // query heads per KV head
-constexpr int kKeys = 32;                 // keys per tile
 constexpr int kWavesP = 4;
 constexpr int kPThreads = 64 * kWavesP;   // 256
 constexpr int kRowsPerWave = 32;
@@ -55,11 +54,15 @@ constexpr int kRB = kRowsPerWave / 16;    // 2 row blocks per wave
 constexpr int kKStride = kHeadDim + 8;    // LDS row stride of K (elements), 16 B pad
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
+#ifndef YRK_PREFILL_KEYS
+#define YRK_PREFILL_KEYS 32
+#endif
+constexpr int kPrefillKeys = YRK_PREFILL_KEYS;   // keys per tile (32 or 64)
 
+template <int NK>
 struct Smem {
-  uint16_t k[kKeys][kKStride];            // K tile, one row per key
-  uint2 vt[kKeys / 4][kHeadDim];          // V tile as [key/4][dim][4 keys]
-  int32_t page_ok[kKeys / kBlockSize];
+  uint16_t k[NK][kKStride];               // K tile, one row per key
+  uint2 vt[NK / 4][kHeadDim];             // V tile as [key/4][dim][4 keys]
 };
 
 __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
@@ -71,83 +74,119 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// Element offset of key `key`'s row (KV head g), or -1 for a page outside the
-// pool or beyond the table.
-__device__ __forceinline__ int64_t key_row(const PrefillArgs& a, int g, int64_t key) {
-  if (a.geo.paged) {
-    const int64_t p = key / kBlockSize;
-    if (p >= a.block_table_len) return -1;
-    const int64_t blk = a.block_table[p];
-    if (blk < 0 || blk >= a.geo.num_blocks) return -1;
-    return ((blk * a.geo.num_kv_heads + g) * kBlockSize + key % kBlockSize) * kHeadDim;
-  }
-  if (key >= a.geo.num_blocks * kBlockSize) return -1;
-  return (key * a.geo.num_kv_heads + g) * kHeadDim;
-}
-
-struct Stage {
-  uint4 v[4];   // keys 4kg .. 4kg+3, dims 8c .. 8c+7
-  uint4 k[4];   // K chunks t + 256 i
+// The pages of one key tile, resolved once per workgroup (uniform values):
+// element offset of each page's first row for KV head g, or -1 when the page
+// holds no visible key (past kend) or is not a valid pool page.
+template <int NK>
+struct TilePages {
+  int64_t base[NK / kBlockSize];
+  bool bad;   // a page with visible keys is missing from the pool
 };
 
-// Keys at or past kend are never attended; their rows load as zeros (a masked
-// key has weight 0, but 0 * NaN from an unwritten row would not be 0).
-__device__ __forceinline__ void stage_load(const PrefillArgs& a, int g, int64_t k0, int64_t kend,
-                                           Stage& st) {
-  const int t = threadIdx.x;
-  const int kg = t >> 5, c = t & 31;
+template <int NK>
+__device__ __forceinline__ TilePages<NK> tile_pages(const PrefillArgs& a, int g, int64_t k0,
+                                                    int64_t kend) {
+  TilePages<NK> tp;
+  tp.bad = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t key = k0 + 4 * kg + j;
-    const int64_t row = key < kend ? key_row(a, g, key) : -1;
-    st.v[j] = row >= 0 ? *reinterpret_cast<const uint4*>(a.v + row + 8 * c)
-                       : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NK / kBlockSize; ++j) {
+    const int64_t key = k0 + j * kBlockSize;
+    int64_t base = -1;
+    if (key < kend) {
+      if (a.geo.paged) {
+        const int64_t p = key / kBlockSize;
+        const int64_t blk = p < a.block_table_len ? (int64_t)a.block_table[p] : -1;
+        if (blk >= 0 && blk < a.geo.num_blocks)
+          base = (blk * a.geo.num_kv_heads + g) * kBlockSize * kHeadDim;
+      } else if (key < a.geo.num_blocks * kBlockSize) {
+        base = (key * a.geo.num_kv_heads + g) * kHeadDim;
+      }
+      if (base < 0) tp.bad = true;
+    }
+    tp.base[j] = base;
+  }
+  return tp;
+}
+
+// Element offset of key k0 + kk (0 <= kk < NK), or -1 for a key not to load.
+template <int NK>
+__device__ __forceinline__ int64_t tile_row(const PrefillArgs& a, const TilePages<NK>& tp,
+                                            int64_t k0, int kk, int64_t kend) {
+  const int64_t base = tp.base[kk / kBlockSize];
+  if (base < 0 || k0 + kk >= kend) return -1;
+  const int slot = kk % kBlockSize;
+  return base + (int64_t)slot * (a.geo.paged ? kHeadDim : (int64_t)a.geo.num_kv_heads * kHeadDim);
+}
+
+template <int NK>
+struct Stage {
+  uint4 v[NK / 8];   // (NK/32) groups of 4 keys x 8 dims
+  uint4 k[NK / 8];   // K chunks t + 256 i
+};
+
+// Rows of keys that are never attended (at or past kend) load as zeros: a
+// masked key has weight 0, but 0 * NaN from an unwritten row would not be 0.
+template <int NK>
+__device__ __forceinline__ void stage_load(const PrefillArgs& a, const TilePages<NK>& tp,
+                                           int64_t k0, int64_t kend, Stage<NK>& st) {
+  const int t = threadIdx.x;
+  const int c = t & 31;
+#pragma unroll
+  for (int u = 0; u < NK / 32; ++u) {
+    const int kg = (t >> 5) + 8 * u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = tile_row<NK>(a, tp, k0, 4 * kg + j, kend);
+      st.v[4 * u + j] = row >= 0 ? *reinterpret_cast<const uint4*>(a.v + row + 8 * c)
+                                 : make_uint4(0, 0, 0, 0);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NK / 8; ++i) {
     const int chunk = t + kPThreads * i;
-    const int64_t key = k0 + (chunk >> 5);
-    const int64_t row = key < kend ? key_row(a, g, key) : -1;
+    const int64_t row = tile_row<NK>(a, tp, k0, chunk >> 5, kend);
     st.k[i] = row >= 0 ? *reinterpret_cast<const uint4*>(a.k + row + 8 * (chunk & 31))
                        : make_uint4(0, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void stage_store(const PrefillArgs& a, int g, int64_t k0,
-                                            const Stage& st, Smem& sm) {
+template <int NK>
+__device__ __forceinline__ void stage_store(const Stage<NK>& st, Smem<NK>& sm) {
   const int t = threadIdx.x;
-  const int kg = t >> 5, c = t & 31;
-  const uint32_t w0[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
-  const uint32_t w1[4] = {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w};
-  const uint32_t w2[4] = {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w};
-  const uint32_t w3[4] = {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w};
+  const int c = t & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // word i of a row holds dims 8c + 2i (low half) and 8c + 2i + 1 (high half)
-    uint2 lo, hi;
-    lo.x = (w0[i] & 0xffffu) | (w1[i] << 16);
-    lo.y = (w2[i] & 0xffffu) | (w3[i] << 16);
-    hi.x = (w0[i] >> 16) | (w1[i] & 0xffff0000u);
-    hi.y = (w2[i] >> 16) | (w3[i] & 0xffff0000u);
-    sm.vt[kg][8 * c + 2 * i] = lo;
-    sm.vt[kg][8 * c + 2 * i + 1] = hi;
+  for (int u = 0; u < NK / 32; ++u) {
+    const int kg = (t >> 5) + 8 * u;
+    const uint4* r = &st.v[4 * u];
+    const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+    const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
+    const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
+    const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // word i of a row holds dims 8c + 2i (low half) and 8c + 2i + 1 (high half)
+      uint2 lo, hi;
+      lo.x = (w0[i] & 0xffffu) | (w1[i] << 16);
+      lo.y = (w2[i] & 0xffffu) | (w3[i] << 16);
+      hi.x = (w0[i] >> 16) | (w1[i] & 0xffff0000u);
+      hi.y = (w2[i] >> 16) | (w3[i] & 0xffff0000u);
+      sm.vt[kg][8 * c + 2 * i] = lo;
+      sm.vt[kg][8 * c + 2 * i + 1] = hi;
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NK / 8; ++i) {
     const int chunk = t + kPThreads * i;
     *reinterpret_cast<uint4*>(&sm.k[chunk >> 5][8 * (chunk & 31)]) = st.k[i];
   }
-  if (t < kKeys / kBlockSize) {
-    const bool ok = key_row(a, g, k0 + t * kBlockSize) >= 0;
-    sm.page_ok[t] = ok;
-    if (!ok) set_error(a.err, kErrBlockId);
-  }
 }
 
+template <int NK>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, int32_t tiles,
                                                                int32_t xcd_share) {
-  __shared__ Smem sm;
-  // block id -> (KV head, token tile): XCD x = b % 8 serves head x / xcd_share
+  constexpr int KB = NK / 16;             // 16-key blocks per tile
+  __shared__ Smem<NK> sm;
+  // block id -> (KV head, row tile): XCD x = b % 8 serves head x / xcd_share
   const int b = blockIdx.x;
   int g, tile;
   if (xcd_share > 0) {
@@ -204,49 +243,60 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   const int64_t first_tok = row0 / kGroup;
   const int64_t last_tok = min((row0 + kRowsPerWG - 1) / kGroup, a.num_q_tokens - 1);
   const int64_t kend = a.q_start + last_tok + 1;    // keys [0, kend) are ever visible
-  const int64_t ntiles = (kend + kKeys - 1) / kKeys;
+  const int64_t ntiles = (kend + NK - 1) / NK;
   const int64_t diag_from = a.q_start + first_tok;   // smallest row position here
 
-  Stage st;
-  stage_load(a, g, 0, kend, st);
+  // pages are resolved two tiles ahead, the tile's rows one tile ahead
+  TilePages<NK> tp_st = tile_pages<NK>(a, g, 0, kend);   // pages of the rows held in st
+  Stage<NK> st;
+  stage_load<NK>(a, tp_st, 0, kend, st);
+  TilePages<NK> tp_next = tile_pages<NK>(a, g, NK, kend);
   for (int64_t it = 0; it < ntiles; ++it) {
-    const int64_t k0 = it * kKeys;
+    const int64_t k0 = it * NK;
+    const TilePages<NK> tp = tp_st;   // pages of the tile computed in this iteration
+    const bool bad = tp.bad;
     __syncthreads();                  // the previous tile is no longer read
-    stage_store(a, g, k0, st, sm);
+    stage_store<NK>(st, sm);
     __syncthreads();
-    if (it + 1 < ntiles) stage_load(a, g, k0 + kKeys, kend, st);
+    if (it + 1 < ntiles) {
+      stage_load<NK>(a, tp_next, k0 + NK, kend, st);
+      tp_st = tp_next;
+      tp_next = tile_pages<NK>(a, g, k0 + 2 * NK, kend);
+    }
+    if (bad && threadIdx.x == 0) set_error(a.err, kErrBlockId);
 
     // S^T = K Q^T
-    floatx4_t sacc[2][kRB];
+    floatx4_t sacc[KB][kRB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = floatx4_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const uint4 kop = *reinterpret_cast<const uint4*>(&sm.k[16 * kb + r16][32 * ks + 8 * q4]);
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = mfma16(kop, qreg[rb][ks], sacc[kb][rb]);
       }
     }
 
-    const bool pages_ok = sm.page_ok[0] && sm.page_ok[1];
-    const bool need_mask = k0 + kKeys - 1 > diag_from || k0 + kKeys > kend || !pages_ok;
-    uint4 pop[kRB];
+    // A key is masked if it lies past the row's position, or (rare) in a page
+    // that is missing from the pool.
+    const bool need_mask = k0 + NK - 1 > diag_from || k0 + NK > kend || bad;
+    uint4 pop[NK / 32][kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      float sv[8];
+      float sv[4 * KB];
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sacc[kb][rb][i] * a.scale_log2;
           if (need_mask) {
             const int kk = 16 * kb + 4 * q4 + i;
-            if (k0 + kk > pos[rb] || !sm.page_ok[kk / kBlockSize]) v = -INFINITY;
+            if (k0 + kk > pos[rb] || (bad && tile_row<NK>(a, tp, k0, kk, kend) < 0)) v = -INFINITY;
           }
           sv[4 * kb + i] = v;
           mx = fmaxf(mx, v);
@@ -261,26 +311,34 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 #pragma unroll
         for (int d = 0; d < 16; ++d) o[d][rb] *= alpha;
       }
-      uint32_t pb[4];
       float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        pb[i >> 1] = pack_bf16x2(fast_exp2(sv[i] - m_run[rb]), fast_exp2(sv[i + 1] - m_run[rb]));
-        lsum += bf16_lo(pb[i >> 1]) + bf16_hi(pb[i >> 1]);
+      for (int s2 = 0; s2 < NK / 32; ++s2) {
+        uint32_t pb[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const int e = 8 * s2 + i;
+          pb[i >> 1] = pack_bf16x2(fast_exp2(sv[e] - m_run[rb]), fast_exp2(sv[e + 1] - m_run[rb]));
+          lsum += bf16_lo(pb[i >> 1]) + bf16_hi(pb[i >> 1]);
+        }
+        pop[s2][rb] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
       }
       l_run[rb] += lsum;
-      pop[rb] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
     }
 
-    // O^T += V^T P^T, 16 tiles of 16 dims; operand keys {4q4..+3} and {16+4q4..+3}
+    // O^T += V^T P^T: per 32-key step s2, operand keys {32s2 + 4q4..+3} and
+    // {32s2 + 16 + 4q4..+3}; 16 tiles of 16 dims
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      const int dim = 16 * d + r16;
-      const uint2 a0 = sm.vt[q4][dim];
-      const uint2 a1 = sm.vt[4 + q4][dim];
-      const uint4 vop = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    for (int s2 = 0; s2 < NK / 32; ++s2) {
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) o[d][rb] = mfma16(vop, pop[rb], o[d][rb]);
+      for (int d = 0; d < 16; ++d) {
+        const int dim = 16 * d + r16;
+        const uint2 a0 = sm.vt[8 * s2 + q4][dim];
+        const uint2 a1 = sm.vt[8 * s2 + 4 + q4][dim];
+        const uint4 vop = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) o[d][rb] = mfma16(vop, pop[s2][rb], o[d][rb]);
+      }
     }
   }
 
@@ -317,7 +375,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     share = 8 / H;   // XCDs per KV head
     blocks = 8 * (((int64_t)tiles + share - 1) / share);
   }
-  return launch(prefill_kernel, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a, tiles, share);
+  return launch(prefill_kernel<kPrefillKeys>, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
+                tiles, share);
 }
 
 }  // namespace yrk
