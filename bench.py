@@ -31,6 +31,22 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic(record):
+    """HBM bytes per launch from a committed rocprofv3 counter record, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", record)
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
+        return None
+    return 1024.0 * (rec["fetch_kib_per_call"] * rec["fetch_scale"] +
+                     rec["write_kib_per_call"] * rec["write_scale"])
+
+
 def decode_bytes_per_launch(n_ctx, per_token):
     # KV stream + q and out (24 heads x 256 x 2 B each) + the page table (4 B / 16 tokens)
     return per_token * n_ctx + 2 * 24 * 256 * 2 + 4 * (n_ctx // 16)
@@ -200,7 +216,8 @@ def main():
                    "layers": w.layers, "context": w.n_ctx, "batch": 1},
         "kv_gbs": tokens * KV_BYTES_PER_TOKEN_LAYER / (wall / args.steps) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_split_bf16_long_1m.json"),
                      "kernel": "decode_attention (split + merge), per layer",
                      "bytes_per_launch": bpl, "avg_launch_ms": kern_ms},
     }
