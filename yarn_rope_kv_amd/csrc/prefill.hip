@@ -9,33 +9,46 @@
 //   rows       a (token, query head) pair is one row, R = 6 x token + head
 //              within the GQA group of KV head g.  A workgroup owns 128
 //              consecutive rows (about 21 tokens x the 6 heads that share g),
-//              so every K/V tile staged in LDS serves the whole group.
-//   workgroup  4 waves, one per SIMD, so a wave may hold 512 registers (Q and
-//              O for 32 rows of head dim 256 take 192 of them).
-//   wave       32 rows as 2 blocks of 16.  Per 32-key tile, with
+//              so every K/V tile in LDS serves the whole group.
+//   workgroup  4 waves, one per SIMD (a wave may hold 512 registers; Q and O
+//              for 32 rows of head dim 256 take 192).
+//   wave       32 rows as 2 blocks of 16.  Per 32 keys, with
 //              v_mfma_f32_16x16x32_bf16:
 //                S^T[32 keys x 32 rows]  = K . Q^T        32 MFMA
 //                O^T[256 x 32 rows]     += V^T . P^T      32 MFMA
-//              Each K or V operand read from LDS feeds both row blocks.  The
-//              S^T accumulator gives lane l (row l%16 of a block, quad q =
-//              l/16) keys 16kb + 4q + i (kb < 2, i < 4).  The P^T operand of
-//              the 32-key PV step needs, in lane l, operand slots 8q .. 8q+7;
-//              mapping slot 8q + m to key 16(m/4) + 4q + m%4 makes them
-//              exactly the lane's own scores, so P goes from the softmax into
-//              the PV MFMA without a shuffle.  V^T follows the same key
-//              order: LDS holds V as [key/4][dim][4 keys], one 8-byte read
-//              per operand half.
+//              The S^T accumulator gives lane l (row l%16 of a block, quad q =
+//              l/16) keys 16kb + 4q + i (i < 4).  The P^T operand of a 32-key
+//              PV step needs, in lane l, operand slots 8q .. 8q+7; mapping
+//              slot 8q + m to key 16(m/4) + 4q + m%4 makes them exactly the
+//              lane's own scores, so P goes from the softmax into the PV MFMA
+//              without a shuffle.
+//   LDS ring   K and V tiles arrive by direct global-to-LDS loads (16 bytes
+//              per lane, no registers), NST tiles deep, so NST-1 tiles are in
+//              flight while one is computed.  Rows keep the cache's natural
+//              [key][256] layout with 16-byte chunk c of row r stored at
+//              position c ^ (r % 16); the loads fetch the chunks in that
+//              permuted order, and both operand reads below touch 16
+//              different chunk positions per 16 lanes.
+//                K^T operand: one 16-byte read per lane.
+//                V^T operand: two ds_read_b64_tr_b16 per lane.  In each
+//              16-lane group that instruction hands lane j element j%4 of the
+//              8 bytes lane 4r + j/4 addressed, as its slot r; pointing lane
+//              L at key 4q + L/4, dims 16d + 4(L%4) .. +3 gives lane j the
+//              values of dim 16d + j at keys 4q .. 4q+3 -- the V^T operand
+//              in the key order of P^T.
 //   softmax    online, per row, log2 domain.  The running maximum is raised
 //              (and O rescaled) only when a tile's maximum exceeds it by more
 //              than 8, so p <= 2^8 and O is rarely touched.  P is rounded to
 //              bf16 for the MFMA and the row sum adds the same rounded values.
 //   masking    a row at position p sees keys <= p; only tiles that reach past
 //              the smallest row position of the workgroup test it per key.
-//   staging    every thread loads 4 V rows x 8 dims (transposed in registers
-//              into the 4-key groups) and 4 K chunks; the next tile's global
-//              loads are in flight while the current tile is computed.
+//              Rows that are never attended (past the chunk, or in a page
+//              missing from the pool) are loaded from the query buffer
+//              instead, so the masked products are 0 x finite.
 //   order      workgroups are numbered so that each XCD (block id mod 8) runs
 //              one KV head: the tiles of that head stream through one L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "yrk_internal.h"
 
@@ -44,6 +57,9 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 constexpr int kGroup = 6;                 // query heads per KV head
 constexpr int kWavesP = 4;
@@ -51,18 +67,21 @@ constexpr int kPThreads = 64 * kWavesP;   // 256
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;   // 128 (token, head) rows
 constexpr int kRB = kRowsPerWave / 16;    // 2 row blocks per wave
-constexpr int kKStride = kHeadDim + 8;    // LDS row stride of K (elements), 16 B pad
+constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per row
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
 #ifndef YRK_PREFILL_KEYS
 #define YRK_PREFILL_KEYS 32
 #endif
-constexpr int kPrefillKeys = YRK_PREFILL_KEYS;   // keys per tile (32 or 64)
+#ifndef YRK_PREFILL_STAGES
+#define YRK_PREFILL_STAGES 2
+#endif
+constexpr int kNK = YRK_PREFILL_KEYS;     // keys per tile
+constexpr int kNST = YRK_PREFILL_STAGES;  // tiles in the LDS ring
 
 template <int NK>
-struct Smem {
-  uint16_t k[NK][kKStride];               // K tile, one row per key
-  uint2 vt[NK / 4][kHeadDim];             // V tile as [key/4][dim][4 keys]
+struct Tile {
+  uint4 kv[2][NK][kChunks];               // [K or V][key][chunk position]
 };
 
 __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
@@ -74,118 +93,196 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// The pages of one key tile, resolved once per workgroup (uniform values):
-// element offset of each page's first row for KV head g, or -1 when the page
-// holds no visible key (past kend) or is not a valid pool page.
+// Two floats to packed bf16 with the hardware conversion (round to nearest
+// even, as f32_to_bf16 above for finite values).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
+}
+
+// Maximum over the four lanes l, l^16, l^32, l^48 (one row's 4 quads) with
+// cross-row lane swaps: each swap leaves a lane holding its own value and
+// its partner's, in one order or the other.
+__device__ __forceinline__ float quad_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// acc *= alpha (per lane) for an MFMA accumulator that lives in AGPRs.  The
+// product goes through VGPR temporaries inside the asm, so the compiler keeps
+// no VGPR copy of the accumulators alive around the (rarely taken) rescale.
+// Callers put acc_hazard_fence() before the first and after the last call:
+// the compiler does not count wait states across inline asm.
+__device__ __forceinline__ void scale_acc(floatx4_t& x, float alpha) {
+  float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+  float t0, t1, t2, t3;
+  asm volatile(
+      "v_accvgpr_read_b32 %4, %0\n\t"
+      "v_accvgpr_read_b32 %5, %1\n\t"
+      "v_accvgpr_read_b32 %6, %2\n\t"
+      "v_accvgpr_read_b32 %7, %3\n\t"
+      "v_mul_f32 %4, %4, %8\n\t"
+      "v_mul_f32 %5, %5, %8\n\t"
+      "v_mul_f32 %6, %6, %8\n\t"
+      "v_mul_f32 %7, %7, %8\n\t"
+      "v_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_write_b32 %1, %5\n\t"
+      "v_accvgpr_write_b32 %2, %6\n\t"
+      "v_accvgpr_write_b32 %3, %7"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(alpha));
+  x = floatx4_t{x0, x1, x2, x3};
+}
+
+// Wait states between MFMA writes and VALU reads of the same registers (and
+// VALU writes before MFMA reads), covering the longest 16x16 MFMA case.
+__device__ __forceinline__ void acc_hazard_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
+
+// Compiler-level fence plus the hardware workgroup barrier, without the
+// memory-counter drain a full __syncthreads() implies (loads of later tiles
+// must stay in flight across it).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// base + voff_l and its bytes land at lds_base + 16 l.  Written as inline
+// assembly so that the compiler does not treat the ring as one aliasing LDS
+// store stream (it would drain every tile in flight before the first LDS
+// read); the ring's own vmcnt waits and barriers order the accesses.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t ub = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(ub)
+               : "memory", "m0");
+}
+
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// Pages of one key tile, resolved by every wave (uniform values).  Key and
+// page indices fit in 32 bits (the host rejects chunks that end past 2^31-1),
+// so the bounds tests stay on the scalar unit; the page table is read through
+// the constant address space, which the compiler loads with scalar loads.
 template <int NK>
-struct TilePages {
-  int64_t base[NK / kBlockSize];
-  bool bad;   // a page with visible keys is missing from the pool
+struct Pages {
+  int64_t base[NK / kBlockSize];   // element offset of the page's first row, or -1
+  uint32_t missing;                // bit j: page j holds visible keys but is not in the pool
 };
 
 template <int NK>
-__device__ __forceinline__ TilePages<NK> tile_pages(const PrefillArgs& a, int g, int64_t k0,
-                                                    int64_t kend) {
-  TilePages<NK> tp;
-  tp.bad = false;
+__device__ __forceinline__ Pages<NK> resolve_pages(const PrefillArgs& a, int g, int32_t k0,
+                                                   int32_t kend) {
+  Pages<NK> pg;
+  pg.missing = 0;
+  const_i32_t* bt = (const_i32_t*)a.block_table;
+  const int32_t bt_len = (int32_t)min(a.block_table_len, (int64_t)INT32_MAX);
+  const int32_t nb = (int32_t)min(a.geo.num_blocks, (int64_t)INT32_MAX);
 #pragma unroll
   for (int j = 0; j < NK / kBlockSize; ++j) {
-    const int64_t key = k0 + j * kBlockSize;
+    const int32_t key = k0 + j * kBlockSize;
     int64_t base = -1;
     if (key < kend) {
       if (a.geo.paged) {
-        const int64_t p = key / kBlockSize;
-        const int64_t blk = p < a.block_table_len ? (int64_t)a.block_table[p] : -1;
-        if (blk >= 0 && blk < a.geo.num_blocks)
-          base = (blk * a.geo.num_kv_heads + g) * kBlockSize * kHeadDim;
-      } else if (key < a.geo.num_blocks * kBlockSize) {
-        base = (key * a.geo.num_kv_heads + g) * kHeadDim;
+        const int32_t p = key / kBlockSize;
+        const int32_t blk = p < bt_len ? bt[p] : -1;
+        if (blk >= 0 && blk < nb)
+          base = ((int64_t)blk * a.geo.num_kv_heads + g) * (kBlockSize * kHeadDim);
+      } else if (key < nb * (int64_t)kBlockSize) {
+        base = ((int64_t)key * a.geo.num_kv_heads + g) * kHeadDim;
       }
-      if (base < 0) tp.bad = true;
+      if (base < 0) pg.missing |= 1u << j;
     }
-    tp.base[j] = base;
+    pg.base[j] = base;
   }
-  return tp;
+  return pg;
 }
 
-// Element offset of key k0 + kk (0 <= kk < NK), or -1 for a key not to load.
+// Start the direct loads of tile j (keys j*NK ..) into `t`.  Wave w moves
+// tensor w/2 (K, then V) of pages (w%2)*NK/32 .. of the tile, 8 instructions
+// per 16-row page (1 KiB each: rows 2i and 2i+1, lane l taking the chunk
+// that belongs at position l % 32 of row 2i + l / 32).  `voff` holds those
+// per-lane byte offsets within a page, the same for every page.  In a page
+// that is only partly visible, rows past kend are clamped to the last
+// visible one; a page with no visible row (or missing from the pool) is
+// replaced by query rows: every loaded value is finite and never attended.
+// Returns the tile's missing-page mask (the same in every wave).
 template <int NK>
-__device__ __forceinline__ int64_t tile_row(const PrefillArgs& a, const TilePages<NK>& tp,
-                                            int64_t k0, int kk, int64_t kend) {
-  const int64_t base = tp.base[kk / kBlockSize];
-  if (base < 0 || k0 + kk >= kend) return -1;
-  const int slot = kk % kBlockSize;
-  return base + (int64_t)slot * (a.geo.paged ? kHeadDim : (int64_t)a.geo.num_kv_heads * kHeadDim);
-}
-
-template <int NK>
-struct Stage {
-  uint4 v[NK / 8];   // (NK/32) groups of 4 keys x 8 dims
-  uint4 k[NK / 8];   // K chunks t + 256 i
-};
-
-// Rows of keys that are never attended (at or past kend) load as zeros: a
-// masked key has weight 0, but 0 * NaN from an unwritten row would not be 0.
-template <int NK>
-__device__ __forceinline__ void stage_load(const PrefillArgs& a, const TilePages<NK>& tp,
-                                           int64_t k0, int64_t kend, Stage<NK>& st) {
-  const int t = threadIdx.x;
-  const int c = t & 31;
+__device__ __forceinline__ uint32_t issue_tile(const PrefillArgs& a, int g, int wave, int32_t j,
+                                               int32_t kend, Tile<NK>& t,
+                                               const uint32_t (&voff)[8], uint32_t stride_b) {
+  constexpr int NP = NK / kBlockSize, PPW = NK / 32;
+  const int32_t k0 = j * NK;
+  const Pages<NK> pg = resolve_pages<NK>(a, g, k0, kend);
+  const int lane = threadIdx.x & 63;
+  const int tensor = wave >> 1;
+  const uint16_t* src_t = tensor ? a.v : a.k;
 #pragma unroll
-  for (int u = 0; u < NK / 32; ++u) {
-    const int kg = (t >> 5) + 8 * u;
+  for (int pp = 0; pp < PPW; ++pp) {
+    const int p = (wave & 1) * PPW + pp;
+    int64_t base = pg.base[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = tile_row<NK>(a, tp, k0, 4 * kg + j, kend);
-      st.v[4 * u + j] = row >= 0 ? *reinterpret_cast<const uint4*>(a.v + row + 8 * c)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-  }
+    for (int q = 1; q < NP; ++q)
+      if (p == q) base = pg.base[q];
+    const int32_t key0 = k0 + kBlockSize * p;
+    const uint32_t lds0 =
+        (uint32_t)(uintptr_t)(lds_void_t*)(void*)(&t.kv[tensor][kBlockSize * p][0]);
+    if (base >= 0 && key0 + kBlockSize <= kend) {
+      const uint16_t* src = src_t + base;
 #pragma unroll
-  for (int i = 0; i < NK / 8; ++i) {
-    const int chunk = t + kPThreads * i;
-    const int64_t row = tile_row<NK>(a, tp, k0, chunk >> 5, kend);
-    st.k[i] = row >= 0 ? *reinterpret_cast<const uint4*>(a.k + row + 8 * (chunk & 31))
-                       : make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <int NK>
-__device__ __forceinline__ void stage_store(const Stage<NK>& st, Smem<NK>& sm) {
-  const int t = threadIdx.x;
-  const int c = t & 31;
+      for (int i = 0; i < 8; ++i) dma16(src, voff[i], lds0 + 1024u * i);
+    } else {
+      const int last = kend - 1 - key0;            // < 15 here, or base < 0
 #pragma unroll
-  for (int u = 0; u < NK / 32; ++u) {
-    const int kg = (t >> 5) + 8 * u;
-    const uint4* r = &st.v[4 * u];
-    const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-    const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
-    const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
-    const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // word i of a row holds dims 8c + 2i (low half) and 8c + 2i + 1 (high half)
-      uint2 lo, hi;
-      lo.x = (w0[i] & 0xffffu) | (w1[i] << 16);
-      lo.y = (w2[i] & 0xffffu) | (w3[i] << 16);
-      hi.x = (w0[i] >> 16) | (w1[i] & 0xffff0000u);
-      hi.y = (w2[i] >> 16) | (w3[i] & 0xffff0000u);
-      sm.vt[kg][8 * c + 2 * i] = lo;
-      sm.vt[kg][8 * c + 2 * i + 1] = hi;
+      for (int i = 0; i < 8; ++i) {
+        int row = 2 * i + (lane >> 5);
+        if (base >= 0) {
+          if (row > last) row = last;
+          dma16(src_t + base, (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row),
+                lds0 + 1024u * i);
+        } else {
+          dma16(a.q, 16u * (uint32_t)(lane & 31), lds0 + 1024u * i);
+        }
+      }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NK / 8; ++i) {
-    const int chunk = t + kPThreads * i;
-    *reinterpret_cast<uint4*>(&sm.k[chunk >> 5][8 * (chunk & 31)]) = st.k[i];
-  }
+  return pg.missing;
 }
 
-template <int NK>
+template <int NK, int NST>
+__device__ __forceinline__ void wait_tile(int32_t tiles_after) {
+  // my loads of the tile to compute are done once at most tiles_after later
+  // tiles' loads (NK/4 instructions each) are still outstanding
+  constexpr int P = NK / 4;
+  if (tiles_after >= 3 && NST > 3) wait_vm<3 * P>();
+  else if (tiles_after >= 2 && NST > 2) wait_vm<2 * P>();
+  else if (tiles_after >= 1) wait_vm<P>();
+  else wait_vm<0>();
+}
+
+template <int NK, int NST>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, int32_t tiles,
                                                                int32_t xcd_share) {
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
   constexpr int KB = NK / 16;             // 16-key blocks per tile
-  __shared__ Smem<NK> sm;
+  __shared__ Tile<NK> ring[NST];
   // block id -> (KV head, row tile): XCD x = b % 8 serves head x / xcd_share
   const int b = blockIdx.x;
   int g, tile;
@@ -200,12 +297,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   if (g >= a.geo.num_kv_heads || tile >= tiles) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int64_t row0 = (int64_t)tile * kRowsPerWG;   // first (token, head) row
 
   // rows of this lane: row block rb -> R = row0 + 32 wave + 16 rb + r16 = 6 token + head
-  int64_t tok[kRB], pos[kRB];
+  int64_t tok[kRB];
+  int32_t pos[kRB];                                   // positions fit in 32 bits
   int head[kRB];
   bool valid[kRB];
 #pragma unroll
@@ -214,7 +312,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     tok[rb] = R / kGroup;
     head[rb] = (int)(R % kGroup);
     valid[rb] = tok[rb] < a.num_q_tokens;
-    pos[rb] = a.q_start + (valid[rb] ? tok[rb] : a.num_q_tokens - 1);
+    pos[rb] = (int32_t)(a.q_start + (valid[rb] ? tok[rb] : a.num_q_tokens - 1));
   }
 
   // Q^T operands: lane holds, per 32-dim step ks, dims 32ks + 8q4 .. +8 of its row
@@ -228,44 +326,89 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
                                : make_uint4(0, 0, 0, 0);
   }
 
+  // Q is in registers before the ring starts: a wait the compiler sees here
+  // keeps it from waiting on Q (and so on every tile in flight) inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
+
   floatx4_t o[16][kRB];
 #pragma unroll
   for (int d = 0; d < 16; ++d)
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) o[d][rb] = floatx4_t{};
-  float m_run[kRB], l_run[kRB];
+  // running maximum (log2 units) and row sums; lsum[rb] = ones . P^T, so
+  // every element holds the lane's row sum of the rounded P values
+  float m_run[kRB];
+  floatx4_t lsum[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     m_run[rb] = kNegBig;
-    l_run[rb] = 0.f;
+    lsum[rb] = floatx4_t{};
   }
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  const float c2 = a.scale_log2;
 
   const int64_t first_tok = row0 / kGroup;
   const int64_t last_tok = min((row0 + kRowsPerWG - 1) / kGroup, a.num_q_tokens - 1);
-  const int64_t kend = a.q_start + last_tok + 1;    // keys [0, kend) are ever visible
-  const int64_t ntiles = (kend + NK - 1) / NK;
-  const int64_t diag_from = a.q_start + first_tok;   // smallest row position here
+  const int32_t kend = (int32_t)(a.q_start + last_tok + 1);   // keys [0, kend) are ever visible
+  const int32_t ntiles = (kend + NK - 1) / NK;
+  const int32_t diag_from = (int32_t)(a.q_start + first_tok);  // smallest row position here
 
-  // pages are resolved two tiles ahead, the tile's rows one tile ahead
-  TilePages<NK> tp_st = tile_pages<NK>(a, g, 0, kend);   // pages of the rows held in st
-  Stage<NK> st;
-  stage_load<NK>(a, tp_st, 0, kend, st);
-  TilePages<NK> tp_next = tile_pages<NK>(a, g, NK, kend);
-  for (int64_t it = 0; it < ntiles; ++it) {
-    const int64_t k0 = it * NK;
-    const TilePages<NK> tp = tp_st;   // pages of the tile computed in this iteration
-    const bool bad = tp.bad;
-    __syncthreads();                  // the previous tile is no longer read
-    stage_store<NK>(st, sm);
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      stage_load<NK>(a, tp_next, k0 + NK, kend, st);
-      tp_st = tp_next;
-      tp_next = tile_pages<NK>(a, g, k0 + 2 * NK, kend);
-    }
-    if (bad && threadIdx.x == 0) set_error(a.err, kErrBlockId);
+  // per-lane byte offsets of the direct loads within a page (see issue_tile)
+  const uint32_t stride_b =
+      2u * (uint32_t)(a.geo.paged ? kHeadDim : a.geo.num_kv_heads * kHeadDim);
+  uint32_t voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 2 * i + (lane >> 5);
+    voff[i] = (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row);
+  }
 
-    // S^T = K Q^T
+  uint32_t missing[NST];   // indexed by compile-time-unrolled ring slot only
+#pragma unroll
+  for (int s = 0; s < NST; ++s) missing[s] = 0;
+  uint32_t any_missing = 0;
+
+  // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < ntiles) missing[s] = issue_tile<NK>(a, g, wave, s, kend, ring[s], voff, stride_b);
+
+  // V^T operand j of a tile (j = 16 s2 + d): keys 32 s2 .. +31, dims 16d ..
+  // +15.  Lane (r16, q4) points its two transposing reads at keys
+  // 32s2 + 4q4 + r16/4 (+16) and dims 16d + 4(r16%4) .. +3.
+  const int kq = 4 * q4 + (r16 >> 2);            // key within the 16-key half, 0..15
+  const int coff = (r16 & 3) >> 1;               // chunk within the 32-byte dim span
+  const int boff = (r16 & 1) * 8;                // byte within the chunk
+  auto read_v = [&](const Tile<NK>& t, int j) {
+    const int s2 = j / 16, c = 2 * (j % 16) + coff;
+    const char* p0 = reinterpret_cast<const char*>(&t.kv[1][32 * s2 + kq][c ^ kq]) + boff;
+    const char* p1 = reinterpret_cast<const char*>(&t.kv[1][32 * s2 + 16 + kq][c ^ kq]) + boff;
+    const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p0));
+    const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p1));
+    const uint2 w0 = __builtin_bit_cast(uint2, v0);
+    const uint2 w1 = __builtin_bit_cast(uint2, v1);
+    return make_uint4(w0.x, w0.y, w1.x, w1.y);
+  };
+  constexpr int kVOps = NK / 32 * 16;            // V^T operands per tile
+  constexpr int kVAhead = 8;                     // operands read ahead of their MFMAs
+
+  // Scores of the tile in `t` (keys k0 ..): S^T = K Q^T, masked, kept raw
+  // (the scale, > 0, is applied inside the exponent), with each row's
+  // maximum in log2 units.  All K operands are read before the first MFMA,
+  // and the first V operands are started behind them, so that LDS latency
+  // overlaps the products and the softmax (the compiler would otherwise
+  // wait for each read just before its use).
+  float sv[kRB][4 * KB];
+  float mxs[kRB];
+  uint4 vpre[kVAhead];
+  auto scores = [&](const Tile<NK>& t, int32_t k0, uint32_t miss) {
+    constexpr int kKAhead = 4;                   // 32-dim steps of K read ahead
+    uint4 kop[8][KB];
+#pragma unroll
+    for (int ks = 0; ks < kKAhead; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kop[ks][kb] = t.kv[0][16 * kb + r16][(4 * ks + q4) ^ r16];
+    __builtin_amdgcn_sched_barrier(0);
     floatx4_t sacc[KB][kRB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -273,81 +416,144 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
       for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = floatx4_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      if (ks + kKAhead < 8) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(&sm.k[16 * kb + r16][32 * ks + 8 * q4]);
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = mfma16(kop, qreg[rb][ks], sacc[kb][rb]);
+        for (int kb = 0; kb < KB; ++kb)
+          kop[ks + kKAhead][kb] = t.kv[0][16 * kb + r16][(4 * (ks + kKAhead) + q4) ^ r16];
       }
-    }
-
-    // A key is masked if it lies past the row's position, or (rare) in a page
-    // that is missing from the pool.
-    const bool need_mask = k0 + NK - 1 > diag_from || k0 + NK > kend || bad;
-    uint4 pop[NK / 32][kRB];
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      float sv[4 * KB];
-      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[kb][rb][i] * a.scale_log2;
-          if (need_mask) {
-            const int kk = 16 * kb + 4 * q4 + i;
-            if (k0 + kk > pos[rb] || (bad && tile_row<NK>(a, tp, k0, kk, kend) < 0)) v = -INFINITY;
-          }
-          sv[4 * kb + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool raise = mx > m_run[rb] + kRescale;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? fast_exp2(m_run[rb] - mx) : 1.0f;
-        if (raise) m_run[rb] = mx;
-        l_run[rb] *= alpha;
+        for (int rb = 0; rb < kRB; ++rb)
+          sacc[kb][rb] = mfma16(kop[ks][kb], qreg[rb][ks], sacc[kb][rb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-        for (int d = 0; d < 16; ++d) o[d][rb] *= alpha;
+    for (int j = 0; j < kVAhead; ++j) vpre[j] = read_v(t, j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[rb][4 * kb + i] = sacc[kb][rb][i];
+    // Masking, only on tiles that reach past the smallest row position or
+    // the visible range, or hold a missing page: key 16kb + 4q4 + i is kept
+    // when it is at most the row's position and its page is present.
+    if (k0 + NK - 1 > diag_from || k0 + NK > kend || miss != 0) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int lim = pos[rb] - k0 - 4 * q4;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int limk = ((miss >> (16 * kb / kBlockSize)) & 1u) ? -1 : lim - 16 * kb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sv[rb][4 * kb + i] = i <= limk ? sv[rb][4 * kb + i] : -INFINITY;
+        }
       }
-      float lsum = 0.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      float mx = sv[rb][0];
+#pragma unroll
+      for (int e = 1; e < 4 * KB; ++e) mx = fmaxf(mx, sv[rb][e]);
+      mxs[rb] = quad_max(mx) * c2;
+    }
+  };
+
+  // P = exp2(scale S - m) in bf16, its row sums, and O^T += V^T P^T, with
+  // the V^T reads kVAhead operands ahead of their MFMAs.
+  auto accumulate = [&](const Tile<NK>& t) {
+    uint4 pop[NK / 32][kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const float negm = -m_run[rb];
 #pragma unroll
       for (int s2 = 0; s2 < NK / 32; ++s2) {
         uint32_t pb[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           const int e = 8 * s2 + i;
-          pb[i >> 1] = pack_bf16x2(fast_exp2(sv[e] - m_run[rb]), fast_exp2(sv[e + 1] - m_run[rb]));
-          lsum += bf16_lo(pb[i >> 1]) + bf16_hi(pb[i >> 1]);
+          pb[i >> 1] = cvt_pk_bf16(fast_exp2(fmaf(sv[rb][e], c2, negm)),
+                                   fast_exp2(fmaf(sv[rb][e + 1], c2, negm)));
         }
         pop[s2][rb] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
+        lsum[rb] = mfma16(ones, pop[s2][rb], lsum[rb]);
       }
-      l_run[rb] += lsum;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 vring[kVAhead];
+#pragma unroll
+    for (int j = 0; j < kVAhead; ++j) vring[j] = vpre[j];
+#pragma unroll
+    for (int j = 0; j < kVOps; ++j) {
+      const uint4 vop = vring[j % kVAhead];
+      if (j + kVAhead < kVOps) vring[j % kVAhead] = read_v(t, j + kVAhead);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        o[j % 16][rb] = mfma16(vop, pop[j / 16][rb], o[j % 16][rb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-    // O^T += V^T P^T: per 32-key step s2, operand keys {32s2 + 4q4..+3} and
-    // {32s2 + 16 + 4q4..+3}; 16 tiles of 16 dims
+  // The main loop never touches O outside the MFMAs.  When a tile's maximum
+  // exceeds a row's running maximum by more than the threshold, it leaves,
+  // raises the maximum and rescales O and the row sums, finishes that tile
+  // and resumes; this happens on the first tile and rarely after it.
+  // Scalar loads still pending here (kernel arguments the compiler fetches
+  // late) would make every LDS wait in the loop a full one: wait for them
+  // (lgkmcnt(0) only; the tiles in flight stay in flight).
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  int32_t it = 0;
+  for (;;) {
+    bool raised = false;
+    for (; it < ntiles; ++it) {
+      const int slot = (int)(it % NST);
+      const int nslot = (int)((it + NST - 1) % NST);   // the slot tile it-1 used
+      wg_barrier();                                   // all waves are done with tile it-1
+      uint32_t miss = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < NK / 32; ++s2) {
+      for (int s = 0; s < NST; ++s) if (s == slot) miss = missing[s];
+      if (it + NST - 1 < ntiles) {
+        const uint32_t m =
+            issue_tile<NK>(a, g, wave, it + NST - 1, kend, ring[nslot], voff, stride_b);
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const int dim = 16 * d + r16;
-        const uint2 a0 = sm.vt[8 * s2 + q4][dim];
-        const uint2 a1 = sm.vt[8 * s2 + 4 + q4][dim];
-        const uint4 vop = make_uint4(a0.x, a0.y, a1.x, a1.y);
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) o[d][rb] = mfma16(vop, pop[s2][rb], o[d][rb]);
+        for (int s = 0; s < NST; ++s) if (s == nslot) missing[s] = m;
       }
+      wait_tile<NK, NST>(min(NST - 1, ntiles - 1 - it));
+      wg_barrier();                                   // every wave's loads of tile it landed
+      any_missing |= miss;
+      scores(ring[slot], it * NK, miss);
+      bool r = false;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) r |= mxs[rb] > m_run[rb] + kRescale;
+      if (__builtin_amdgcn_ballot_w64(r)) {
+        raised = true;
+        break;
+      }
+      accumulate(ring[slot]);
     }
+    if (!raised) break;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const bool raise = mxs[rb] > m_run[rb] + kRescale;
+      const float alpha = raise ? fast_exp2(m_run[rb] - mxs[rb]) : 1.0f;
+      if (raise) m_run[rb] = mxs[rb];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[d][rb] *= alpha;
+      lsum[rb] *= alpha;
+    }
+    accumulate(ring[it % NST]);
+    ++it;
   }
 
-  // row sums over the 4 quads, normalise, store dims 16d + 4q4 .. +3
+  if (any_missing && threadIdx.x == 0) set_error(a.err, kErrBlockId);
+
+  // normalise by the row sum and store dims 16d + 4q4 .. +3
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    float lt = l_run[rb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lsum[rb][0];
     if (valid[rb]) {
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       uint16_t* orow = a.out + (tok[rb] * a.num_q_heads + g * kGroup + head[rb]) * kHeadDim;
@@ -375,7 +581,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     share = 8 / H;   // XCDs per KV head
     blocks = 8 * (((int64_t)tiles + share - 1) / share);
   }
-  return launch(prefill_kernel<kPrefillKeys>, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
+  return launch(prefill_kernel<kNK, kNST>, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
                 tiles, share);
 }
 
