@@ -70,14 +70,8 @@ constexpr int kRB = kRowsPerWave / 16;    // 2 row blocks per wave
 constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per row
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
-#ifndef YRK_PREFILL_KEYS
-#define YRK_PREFILL_KEYS 32
-#endif
-#ifndef YRK_PREFILL_STAGES
-#define YRK_PREFILL_STAGES 2
-#endif
-constexpr int kNK = YRK_PREFILL_KEYS;     // keys per tile
-constexpr int kNST = YRK_PREFILL_STAGES;  // tiles in the LDS ring
+constexpr int kNK = 32;                   // keys per tile
+constexpr int kNST = 4;                   // tiles in the LDS ring
 
 template <int NK>
 struct Tile {
@@ -177,93 +171,87 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
-// Pages of one key tile, resolved by every wave (uniform values).  Key and
-// page indices fit in 32 bits (the host rejects chunks that end past 2^31-1),
-// so the bounds tests stay on the scalar unit; the page table is read through
-// the constant address space, which the compiler loads with scalar loads.
-template <int NK>
-struct Pages {
-  int64_t base[NK / kBlockSize];   // element offset of the page's first row, or -1
-  uint32_t missing;                // bit j: page j holds visible keys but is not in the pool
+// Block ids of the two 16-key pages of a 32-key tile, read ahead of use
+// through the constant address space (the compiler loads them with scalar
+// loads).  Page indices past the table are clamped into it; such pages hold
+// no visible key (the host checks that the table covers the chunk), so
+// their ids are never used.
+struct PageIds {
+  int32_t id[2];
 };
 
-template <int NK>
-__device__ __forceinline__ Pages<NK> resolve_pages(const PrefillArgs& a, int g, int32_t k0,
-                                                   int32_t kend) {
-  Pages<NK> pg;
-  pg.missing = 0;
-  const_i32_t* bt = (const_i32_t*)a.block_table;
-  const int32_t bt_len = (int32_t)min(a.block_table_len, (int64_t)INT32_MAX);
-  const int32_t nb = (int32_t)min(a.geo.num_blocks, (int64_t)INT32_MAX);
-#pragma unroll
-  for (int j = 0; j < NK / kBlockSize; ++j) {
-    const int32_t key = k0 + j * kBlockSize;
-    int64_t base = -1;
-    if (key < kend) {
-      if (a.geo.paged) {
-        const int32_t p = key / kBlockSize;
-        const int32_t blk = p < bt_len ? bt[p] : -1;
-        if (blk >= 0 && blk < nb)
-          base = ((int64_t)blk * a.geo.num_kv_heads + g) * (kBlockSize * kHeadDim);
-      } else if (key < nb * (int64_t)kBlockSize) {
-        base = ((int64_t)key * a.geo.num_kv_heads + g) * kHeadDim;
-      }
-      if (base < 0) pg.missing |= 1u << j;
-    }
-    pg.base[j] = base;
+template <bool PAGED>
+__device__ __forceinline__ PageIds load_page_ids(const PrefillArgs& a, int32_t j) {
+  PageIds r{{0, 0}};
+  if constexpr (PAGED) {
+    const_i32_t* bt = (const_i32_t*)a.block_table;
+    const int32_t last = (int32_t)min(a.block_table_len, (int64_t)INT32_MAX) - 1;
+    r.id[0] = bt[min(2 * j, last)];
+    r.id[1] = bt[min(2 * j + 1, last)];
   }
-  return pg;
+  return r;
 }
 
-// Start the direct loads of tile j (keys j*NK ..) into `t`.  Wave w moves
-// tensor w/2 (K, then V) of pages (w%2)*NK/32 .. of the tile, 8 instructions
-// per 16-row page (1 KiB each: rows 2i and 2i+1, lane l taking the chunk
-// that belongs at position l % 32 of row 2i + l / 32).  `voff` holds those
-// per-lane byte offsets within a page, the same for every page.  In a page
-// that is only partly visible, rows past kend are clamped to the last
-// visible one; a page with no visible row (or missing from the pool) is
-// replaced by query rows: every loaded value is finite and never attended.
-// Returns the tile's missing-page mask (the same in every wave).
-template <int NK>
+// Start the direct loads of tile j (keys 32j ..) into `t`.  Wave w moves
+// tensor w/2 (K, then V) of page w%2 of the tile, 8 instructions per page
+// (1 KiB each: rows 2i and 2i+1, lane l taking the chunk that belongs at
+// position l % 32 of row 2i + l / 32).  `voff` holds those per-lane byte
+// offsets within a page, the same for every page.  In a page that is only
+// partly visible, rows past kend are clamped to the last visible one; a page
+// with no visible row (or missing from the pool) is replaced by query rows:
+// every loaded value is finite and never attended.  Key and page indices fit
+// in 32 bits (the host rejects chunks that end past 2^31-1), so all of this
+// stays on the scalar unit.  Returns the tile's missing-page mask (bit p:
+// page p holds visible keys but is not in the pool; the same in every wave).
+template <bool PAGED>
 __device__ __forceinline__ uint32_t issue_tile(const PrefillArgs& a, int g, int wave, int32_t j,
-                                               int32_t kend, Tile<NK>& t,
+                                               int32_t kend, PageIds ids, Tile<32>& t,
                                                const uint32_t (&voff)[8], uint32_t stride_b) {
-  constexpr int NP = NK / kBlockSize, PPW = NK / 32;
-  const int32_t k0 = j * NK;
-  const Pages<NK> pg = resolve_pages<NK>(a, g, k0, kend);
+  const int32_t nb = (int32_t)min(a.geo.num_blocks, (int64_t)INT32_MAX);
+  const int64_t nkeys = a.geo.num_blocks * kBlockSize;
+  uint32_t missing = 0;
+  int64_t base[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int32_t key = 32 * j + kBlockSize * p;
+    bool ok;
+    if constexpr (PAGED) {
+      ok = ids.id[p] >= 0 && ids.id[p] < nb;
+      base[p] = ((int64_t)ids.id[p] * a.geo.num_kv_heads + g) * (kBlockSize * kHeadDim);
+    } else {
+      ok = key < nkeys;
+      base[p] = ((int64_t)key * a.geo.num_kv_heads + g) * kHeadDim;
+    }
+    const bool visible = key < kend;
+    if (visible && !ok) missing |= 1u << p;
+    if (!visible || !ok) base[p] = -1;
+  }
   const int lane = threadIdx.x & 63;
   const int tensor = wave >> 1;
+  const int p = wave & 1;
+  const int64_t b = p ? base[1] : base[0];
   const uint16_t* src_t = tensor ? a.v : a.k;
+  const int32_t key0 = 32 * j + kBlockSize * p;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)(void*)(&t.kv[tensor][kBlockSize * p][0]);
+  if (b >= 0 && key0 + kBlockSize <= kend) {
+    const uint16_t* src = src_t + b;
 #pragma unroll
-  for (int pp = 0; pp < PPW; ++pp) {
-    const int p = (wave & 1) * PPW + pp;
-    int64_t base = pg.base[0];
+    for (int i = 0; i < 8; ++i) dma16(src, voff[i], lds0 + 1024u * i);
+  } else {
+    const int last = kend - 1 - key0;            // < 15 here, or b < 0
 #pragma unroll
-    for (int q = 1; q < NP; ++q)
-      if (p == q) base = pg.base[q];
-    const int32_t key0 = k0 + kBlockSize * p;
-    const uint32_t lds0 =
-        (uint32_t)(uintptr_t)(lds_void_t*)(void*)(&t.kv[tensor][kBlockSize * p][0]);
-    if (base >= 0 && key0 + kBlockSize <= kend) {
-      const uint16_t* src = src_t + base;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(src, voff[i], lds0 + 1024u * i);
-    } else {
-      const int last = kend - 1 - key0;            // < 15 here, or base < 0
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int row = 2 * i + (lane >> 5);
-        if (base >= 0) {
-          if (row > last) row = last;
-          dma16(src_t + base, (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row),
-                lds0 + 1024u * i);
-        } else {
-          dma16(a.q, 16u * (uint32_t)(lane & 31), lds0 + 1024u * i);
-        }
+    for (int i = 0; i < 8; ++i) {
+      int row = 2 * i + (lane >> 5);
+      if (b >= 0) {
+        if (row > last) row = last;
+        dma16(src_t + b, (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row),
+              lds0 + 1024u * i);
+      } else {
+        dma16(a.q, 16u * (uint32_t)(lane & 31), lds0 + 1024u * i);
       }
     }
   }
-  return pg.missing;
+  return missing;
 }
 
 template <int NK, int NST>
@@ -277,10 +265,11 @@ __device__ __forceinline__ void wait_tile(int32_t tiles_after) {
   else wait_vm<0>();
 }
 
-template <int NK, int NST>
+template <int NK, int NST, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, int32_t tiles,
                                                                int32_t xcd_share) {
-  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  static_assert(NST == 4, "ring depth (slot arithmetic assumes a power of two)");
+  static_assert(NK == 32, "tile keys");
   constexpr int KB = NK / 16;             // 16-key blocks per tile
   __shared__ Tile<NK> ring[NST];
   // block id -> (KV head, row tile): XCD x = b % 8 serves head x / xcd_share
@@ -363,46 +352,50 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     voff[i] = (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row);
   }
 
-  uint32_t missing[NST];   // indexed by compile-time-unrolled ring slot only
-#pragma unroll
-  for (int s = 0; s < NST; ++s) missing[s] = 0;
+  // missing-page masks of the tiles in the ring, 2 bits per slot
+  uint32_t missing = 0;
   uint32_t any_missing = 0;
 
-  // prologue: tiles 0 .. NST-2 in flight
+  // prologue: tiles 0 .. NST-2 in flight, and the page ids of tile NST-1
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < ntiles) missing[s] = issue_tile<NK>(a, g, wave, s, kend, ring[s], voff, stride_b);
+    if (s < ntiles)
+      missing |= issue_tile<PAGED>(a, g, wave, s, kend, load_page_ids<PAGED>(a, s), ring[s],
+                                   voff, stride_b) << (2 * s);
+  PageIds ids_next = load_page_ids<PAGED>(a, NST - 1);
 
-  // V^T operand j of a tile (j = 16 s2 + d): keys 32 s2 .. +31, dims 16d ..
-  // +15.  Lane (r16, q4) points its two transposing reads at keys
-  // 32s2 + 4q4 + r16/4 (+16) and dims 16d + 4(r16%4) .. +3.
+  // V^T operand d of a tile: keys 0 .. 31, dims 16d .. +15.  Lane (r16, q4)
+  // points its two transposing reads at keys 4q4 + r16/4 (+16) and dims
+  // 16d + 4(r16%4) .. +3.
   const int kq = 4 * q4 + (r16 >> 2);            // key within the 16-key half, 0..15
   const int coff = (r16 & 3) >> 1;               // chunk within the 32-byte dim span
   const int boff = (r16 & 1) * 8;                // byte within the chunk
-  auto read_v = [&](const Tile<NK>& t, int j) {
-    const int s2 = j / 16, c = 2 * (j % 16) + coff;
-    const char* p0 = reinterpret_cast<const char*>(&t.kv[1][32 * s2 + kq][c ^ kq]) + boff;
-    const char* p1 = reinterpret_cast<const char*>(&t.kv[1][32 * s2 + 16 + kq][c ^ kq]) + boff;
+  auto read_v = [&](const Tile<NK>& t, int d) {
+    const int c = 2 * d + coff;
+    const char* p0 = reinterpret_cast<const char*>(&t.kv[1][kq][c ^ kq]) + boff;
+    const char* p1 = reinterpret_cast<const char*>(&t.kv[1][16 + kq][c ^ kq]) + boff;
     const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p0));
     const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p1));
     const uint2 w0 = __builtin_bit_cast(uint2, v0);
     const uint2 w1 = __builtin_bit_cast(uint2, v1);
     return make_uint4(w0.x, w0.y, w1.x, w1.y);
   };
-  constexpr int kVOps = NK / 32 * 16;            // V^T operands per tile
-  constexpr int kVAhead = 8;                     // operands read ahead of their MFMAs
+  constexpr int kVAhead = 8;                     // V^T operands read ahead of their MFMAs
+  uint4 vpre[kVAhead];
+  auto read_v_first = [&](const Tile<NK>& t) {
+#pragma unroll
+    for (int d = 0; d < kVAhead; ++d) vpre[d] = read_v(t, d);
+  };
 
-  // Scores of the tile in `t` (keys k0 ..): S^T = K Q^T, masked, kept raw
-  // (the scale, > 0, is applied inside the exponent), with each row's
-  // maximum in log2 units.  All K operands are read before the first MFMA,
-  // and the first V operands are started behind them, so that LDS latency
-  // overlaps the products and the softmax (the compiler would otherwise
-  // wait for each read just before its use).
+  // Scores of the tile in `t` (keys k0 ..): S^T = K Q^T, kept raw (the
+  // scale, > 0, is applied inside the exponent) and masked.  K operands are
+  // read four 32-dim steps ahead of their MFMAs, so that LDS latency overlaps
+  // the products (the compiler would otherwise wait for each read just
+  // before its use).
   float sv[kRB][4 * KB];
   float mxs[kRB];
-  uint4 vpre[kVAhead];
   auto scores = [&](const Tile<NK>& t, int32_t k0, uint32_t miss) {
-    constexpr int kKAhead = 4;                   // 32-dim steps of K read ahead
+    constexpr int kKAhead = 4;
     uint4 kop[8][KB];
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks)
@@ -429,9 +422,6 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = 0; j < kVAhead; ++j) vpre[j] = read_v(t, j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -446,13 +436,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
         const int lim = pos[rb] - k0 - 4 * q4;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int limk = ((miss >> (16 * kb / kBlockSize)) & 1u) ? -1 : lim - 16 * kb;
+          const int limk = ((miss >> kb) & 1u) ? -1 : lim - 16 * kb;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sv[rb][4 * kb + i] = i <= limk ? sv[rb][4 * kb + i] : -INFINITY;
         }
       }
     }
+  };
+
+  // Row maxima of sv (log2 units) and P = exp2(scale S - m) in bf16, for
+  // the (re)start of the pipeline below.
+  auto tile_max = [&]() {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       float mx = sv[rb][0];
@@ -461,80 +456,89 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
       mxs[rb] = quad_max(mx) * c2;
     }
   };
-
-  // P = exp2(scale S - m) in bf16, its row sums, and O^T += V^T P^T, with
-  // the V^T reads kVAhead operands ahead of their MFMAs.
-  auto accumulate = [&](const Tile<NK>& t) {
-    uint4 pop[NK / 32][kRB];
+  auto make_p = [&](uint4 (&p)[kRB]) {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const float negm = -m_run[rb];
+      uint32_t w[4];
 #pragma unroll
-      for (int s2 = 0; s2 < NK / 32; ++s2) {
-        uint32_t pb[4];
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const int e = 8 * s2 + i;
-          pb[i >> 1] = cvt_pk_bf16(fast_exp2(fmaf(sv[rb][e], c2, negm)),
-                                   fast_exp2(fmaf(sv[rb][e + 1], c2, negm)));
-        }
-        pop[s2][rb] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
-        lsum[rb] = mfma16(ones, pop[s2][rb], lsum[rb]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    uint4 vring[kVAhead];
-#pragma unroll
-    for (int j = 0; j < kVAhead; ++j) vring[j] = vpre[j];
-#pragma unroll
-    for (int j = 0; j < kVOps; ++j) {
-      const uint4 vop = vring[j % kVAhead];
-      if (j + kVAhead < kVOps) vring[j % kVAhead] = read_v(t, j + kVAhead);
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        o[j % 16][rb] = mfma16(vop, pop[j / 16][rb], o[j % 16][rb]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 8; e += 2)
+        w[e >> 1] = cvt_pk_bf16(fast_exp2(fmaf(sv[rb][e], c2, negm)),
+                                fast_exp2(fmaf(sv[rb][e + 1], c2, negm)));
+      p[rb] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
 
-  // The main loop never touches O outside the MFMAs.  When a tile's maximum
-  // exceeds a row's running maximum by more than the threshold, it leaves,
-  // raises the maximum and rescales O and the row sums, finishes that tile
-  // and resumes; this happens on the first tile and rarely after it.
-  // Scalar loads still pending here (kernel arguments the compiler fetches
-  // late) would make every LDS wait in the loop a full one: wait for them
-  // (lgkmcnt(0) only; the tiles in flight stay in flight).
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  // O^T += V^T P^T and the row sums (ones . P^T) for the tile in `t`, whose
+  // first V operands are in vpre.  With SM, the softmax of the next tile
+  // (scores in sv) runs between the products: one exponential per MFMA pair,
+  // filling the cycles the matrix core is busy; pn receives its P and mxs
+  // its row maxima.
+  auto pv = [&]<bool SM>(const Tile<NK>& t, const uint4(&pc)[kRB], uint4(&pn)[kRB]) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) lsum[rb] = mfma16(ones, pc[rb], lsum[rb]);
+    uint4 vr[kVAhead];
+#pragma unroll
+    for (int d = 0; d < kVAhead; ++d) vr[d] = vpre[d];
+    float negm[kRB], mx[kRB], xe = 0.f;
+    uint32_t w[kRB][4];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) negm[rb] = -m_run[rb];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const uint4 vop = vr[d % kVAhead];
+      if (d + kVAhead < 16) vr[d % kVAhead] = read_v(t, d + kVAhead);
+      o[d][0] = mfma16(vop, pc[0], o[d][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SM) {
+        const int rb = d / 8, e = d % 8;         // score e of row block rb
+        float x = fast_exp2(fmaf(sv[rb][e], c2, negm[rb]));
+        // instruction selection orders pure arithmetic freely; the empty asm
+        // pins this exponential to its slot between the two products
+        asm volatile("" : "+v"(x));
+        if (e & 1) w[rb][e >> 1] = cvt_pk_bf16(xe, x);
+        else xe = x;
+        mx[rb] = e ? fmaxf(mx[rb], sv[rb][e]) : sv[rb][e];
+        if (d == 8) mxs[0] = quad_max(mx[0]) * c2;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      o[d][1] = mfma16(vop, pc[1], o[d][1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SM) {
+      mxs[1] = quad_max(mx[1]) * c2;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        pn[rb] = make_uint4(w[rb][0], w[rb][1], w[rb][2], w[rb][3]);
+        // P is dead on the (rare) rescale path, so the compiler would sink
+        // its exponentials below the branch, out of the gaps between the
+        // products; this empty use keeps them here.
+        asm volatile("" ::"v"(pn[rb].x), "v"(pn[rb].y), "v"(pn[rb].z), "v"(pn[rb].w));
+      }
+    }
+  };
+
+  // Software pipeline over key tiles, NST deep ring, one barrier per tile.
+  // Iteration it: wait for this wave's loads of tile it+1, barrier (every
+  // wave's loads of tile it+1 landed, and every wave is done with tile it-1,
+  // whose slot the next load reuses), start tile it+NST-1, then S(it+1) on
+  // the matrix cores, then PV(it) with the softmax of tile it+1 between its
+  // products.  A tile whose maximum rises past a row's running maximum by
+  // more than the threshold leaves the loop after PV(it): the maximum is
+  // raised, O and the row sums are rescaled and its P is recomputed; this
+  // happens on the first tile and rarely after it, so O is only ever touched
+  // by the MFMAs inside the loop.
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // pending scalar loads only (see below)
+  wait_tile<NK, NST>(min(NST - 2, ntiles - 1));
+  wg_barrier();
+  any_missing |= missing & 3u;
+  read_v_first(ring[0]);
+  scores(ring[0], 0, missing & 3u);
+  tile_max();
+  uint4 pcur[kRB], pnext[kRB];
   int32_t it = 0;
   for (;;) {
-    bool raised = false;
-    for (; it < ntiles; ++it) {
-      const int slot = (int)(it % NST);
-      const int nslot = (int)((it + NST - 1) % NST);   // the slot tile it-1 used
-      wg_barrier();                                   // all waves are done with tile it-1
-      uint32_t miss = 0;
-#pragma unroll
-      for (int s = 0; s < NST; ++s) if (s == slot) miss = missing[s];
-      if (it + NST - 1 < ntiles) {
-        const uint32_t m =
-            issue_tile<NK>(a, g, wave, it + NST - 1, kend, ring[nslot], voff, stride_b);
-#pragma unroll
-        for (int s = 0; s < NST; ++s) if (s == nslot) missing[s] = m;
-      }
-      wait_tile<NK, NST>(min(NST - 1, ntiles - 1 - it));
-      wg_barrier();                                   // every wave's loads of tile it landed
-      any_missing |= miss;
-      scores(ring[slot], it * NK, miss);
-      bool r = false;
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) r |= mxs[rb] > m_run[rb] + kRescale;
-      if (__builtin_amdgcn_ballot_w64(r)) {
-        raised = true;
-        break;
-      }
-      accumulate(ring[slot]);
-    }
-    if (!raised) break;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const bool raise = mxs[rb] > m_run[rb] + kRescale;
@@ -544,9 +548,41 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
       for (int d = 0; d < 16; ++d) o[d][rb] *= alpha;
       lsum[rb] *= alpha;
     }
-    accumulate(ring[it % NST]);
-    ++it;
+    make_p(pcur);
+    // Pending scalar loads on entry would make every LDS wait in the loop a
+    // full one: wait for them here (lgkmcnt only; tiles stay in flight).
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    bool raised = false;
+    for (; it + 1 < ntiles; ++it) {
+      const uint32_t cslot = (uint32_t)it & (NST - 1), nslot = (uint32_t)(it + 1) & (NST - 1),
+                     islot = (uint32_t)(it + NST - 1) & (NST - 1);
+      wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
+      wg_barrier();
+      if (it + NST - 1 < ntiles) {
+        const uint32_t m = issue_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
+                                             ring[islot], voff, stride_b);
+        missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
+      }
+      const uint32_t miss = (missing >> (2 * nslot)) & 3u;
+      any_missing |= miss;
+      scores(ring[nslot], (it + 1) * NK, miss);
+      pv.template operator()<true>(ring[cslot], pcur, pnext);
+      read_v_first(ring[nslot]);
+      ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
+      bool r = false;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) r |= mxs[rb] > m_run[rb] + kRescale;
+      if (__builtin_amdgcn_ballot_w64(r)) {
+        raised = true;
+        ++it;
+        break;
+      }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) pcur[rb] = pnext[rb];
+    }
+    if (!raised) break;
   }
+  pv.template operator()<false>(ring[(uint32_t)it & (NST - 1)], pcur, pnext);
 
   if (any_missing && threadIdx.x == 0) set_error(a.err, kErrBlockId);
 
@@ -581,7 +617,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     share = 8 / H;   // XCDs per KV head
     blocks = 8 * (((int64_t)tiles + share - 1) / share);
   }
-  return launch(prefill_kernel<kNK, kNST>, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
+  auto kernel = a.geo.paged ? prefill_kernel<kNK, kNST, true> : prefill_kernel<kNK, kNST, false>;
+  return launch(kernel, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
                 tiles, share);
 }
 
