@@ -64,9 +64,9 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 constexpr int kGroup = 6;                 // query heads per KV head
 constexpr int kWavesP = 4;
 constexpr int kPThreads = 64 * kWavesP;   // 256
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kRowsPerWave * kWavesP;   // 128 (token, head) rows
-constexpr int kRB = kRowsPerWave / 16;    // 2 row blocks per wave
+constexpr int kRowsPerWave = 48;
+constexpr int kRowsPerWG = kRowsPerWave * kWavesP;   // 192 (token, head) rows = 32 tokens
+constexpr int kRB = kRowsPerWave / 16;    // 3 row blocks per wave
 constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per row
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
@@ -86,6 +86,14 @@ __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floa
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+
+// LDS position of logical 16-byte chunk c of ring row r is c ^ swz(r).  swz
+// permutes the bits of r % 16 so that (a) 8 rows starting at a multiple of 8
+// get distinct values mod 8, and the K operand reads (8 lanes, one row each,
+// 16 bytes) cover all 32 banks; (b) 4 rows starting at a multiple of 4 differ
+// in bits 1-2, and the transposing V reads (4 rows x 32 bytes per 16 lanes)
+// land in 4 distinct 8-bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 // Two floats to packed bf16 with the hardware conversion (round to nearest
 // even, as f32_to_bf16 above for finite values).
@@ -169,6 +177,27 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory", "m0");
 }
 
+// Four 1 KiB direct loads behind one M0 write: load k (0..3) reads
+// base + v_k + 1024 k and lands at lds_base + 1024 k + 16 lane (the
+// instruction offset moves the global and the LDS address alike).  Each M0
+// write ahead of a direct load costs the wave about as much as a fifth load.
+__device__ __forceinline__ void dma16x4(const void* base, uint32_t v0, uint32_t v1, uint32_t v2,
+                                        uint32_t v3, uint32_t lds_base) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t ub = ((uint64_t)hi << 32) | lo;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(ub)
+      : "memory", "m0");
+}
+
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 // Block ids of the two 16-key pages of a 32-key tile, read ahead of use
@@ -192,21 +221,28 @@ __device__ __forceinline__ PageIds load_page_ids(const PrefillArgs& a, int32_t j
   return r;
 }
 
-// Start the direct loads of tile j (keys 32j ..) into `t`.  Wave w moves
-// tensor w/2 (K, then V) of page w%2 of the tile, 8 instructions per page
-// (1 KiB each: rows 2i and 2i+1, lane l taking the chunk that belongs at
-// position l % 32 of row 2i + l / 32).  `voff` holds those per-lane byte
-// offsets within a page, the same for every page.  In a page that is only
-// partly visible, rows past kend are clamped to the last visible one; a page
-// with no visible row (or missing from the pool) is replaced by query rows:
-// every loaded value is finite and never attended.  Key and page indices fit
-// in 32 bits (the host rejects chunks that end past 2^31-1), so all of this
-// stays on the scalar unit.  Returns the tile's missing-page mask (bit p:
-// page p holds visible keys but is not in the pool; the same in every wave).
+// One wave's share of a tile load: tensor w/2 (K, then V) of page w%2 of
+// tile j (keys 32j ..), moved by 8 direct loads of 1 KiB (rows 2i and 2i+1,
+// lane l taking the chunk that belongs at position l % 32 of row 2i + l/32;
+// the per-lane byte offsets within a page are the same for every page).  In a page that is only partly visible, rows past kend are clamped
+// to the last visible one; a page with no visible row (or missing from the
+// pool) is replaced by query rows: every loaded value is finite and never
+// attended.  Key and page indices fit in 32 bits (the host rejects chunks
+// that end past 2^31-1), so the planning stays on the scalar unit.
+struct PageLoad {
+  const uint16_t* src;   // first row of the page (valid when present)
+  uint32_t lds0;         // LDS byte address of the page's first row in the slot
+  int32_t last;          // last visible row of the page
+  bool present;          // in the pool and holding visible rows
+  bool full;             // present with all 16 rows visible
+};
+
+// Plans the load of tile j; returns the tile's missing-page mask (bit p: page
+// p holds visible keys but is not in the pool; the same in every wave).
 template <bool PAGED>
-__device__ __forceinline__ uint32_t issue_tile(const PrefillArgs& a, int g, int wave, int32_t j,
-                                               int32_t kend, PageIds ids, Tile<32>& t,
-                                               const uint32_t (&voff)[8], uint32_t stride_b) {
+__device__ __forceinline__ uint32_t plan_tile(const PrefillArgs& a, int g, int wave, int32_t j,
+                                              int32_t kend, PageIds ids, Tile<32>& t,
+                                              PageLoad& pl) {
   const int32_t nb = (int32_t)min(a.geo.num_blocks, (int64_t)INT32_MAX);
   const int64_t nkeys = a.geo.num_blocks * kBlockSize;
   uint32_t missing = 0;
@@ -226,32 +262,43 @@ __device__ __forceinline__ uint32_t issue_tile(const PrefillArgs& a, int g, int 
     if (visible && !ok) missing |= 1u << p;
     if (!visible || !ok) base[p] = -1;
   }
-  const int lane = threadIdx.x & 63;
   const int tensor = wave >> 1;
   const int p = wave & 1;
   const int64_t b = p ? base[1] : base[0];
-  const uint16_t* src_t = tensor ? a.v : a.k;
   const int32_t key0 = 32 * j + kBlockSize * p;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)(void*)(&t.kv[tensor][kBlockSize * p][0]);
-  if (b >= 0 && key0 + kBlockSize <= kend) {
-    const uint16_t* src = src_t + b;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(src, voff[i], lds0 + 1024u * i);
-  } else {
-    const int last = kend - 1 - key0;            // < 15 here, or b < 0
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int row = 2 * i + (lane >> 5);
-      if (b >= 0) {
-        if (row > last) row = last;
-        dma16(src_t + b, (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row),
-              lds0 + 1024u * i);
-      } else {
-        dma16(a.q, 16u * (uint32_t)(lane & 31), lds0 + 1024u * i);
-      }
-    }
-  }
+  pl.src = (tensor ? a.v : a.k) + (b >= 0 ? b : 0);
+  pl.lds0 = (uint32_t)(uintptr_t)(lds_void_t*)(void*)(&t.kv[tensor][kBlockSize * p][0]);
+  pl.last = kend - 1 - key0;
+  pl.present = b >= 0;
+  pl.full = b >= 0 && key0 + kBlockSize <= kend;
   return missing;
+}
+
+// Direct load i (0..7) of a page that is only partly visible or not present.
+__device__ __forceinline__ void load_rows(const PrefillArgs& a, const PageLoad& pl, int i,
+                                          uint32_t stride_b) {
+  const int lane = threadIdx.x & 63;
+  int row = 2 * i + (lane >> 5);
+  if (pl.present) {
+    if (row > pl.last) row = pl.last;
+    dma16(pl.src, (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ swz(row)),
+          pl.lds0 + 1024u * i);
+  } else {
+    dma16(a.q, 16u * (uint32_t)(lane & 31), pl.lds0 + 1024u * i);
+  }
+}
+
+// The 8 direct loads of a planned page.  `voffq` holds the per-lane offsets
+// of a full page less the instruction offset each load carries.
+__device__ __forceinline__ void load_page(const PrefillArgs& a, const PageLoad& pl,
+                                          const uint32_t (&voffq)[8], uint32_t stride_b) {
+  if (pl.full) {
+    dma16x4(pl.src, voffq[0], voffq[1], voffq[2], voffq[3], pl.lds0);
+    dma16x4(pl.src, voffq[4], voffq[5], voffq[6], voffq[7], pl.lds0 + 4096u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_rows(a, pl, i, stride_b);
+  }
 }
 
 template <int NK, int NST>
@@ -342,14 +389,16 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   const int32_t ntiles = (kend + NK - 1) / NK;
   const int32_t diag_from = (int32_t)(a.q_start + first_tok);  // smallest row position here
 
-  // per-lane byte offsets of the direct loads within a page (see issue_tile)
+  // per-lane byte offsets of the direct loads within a page, less the
+  // instruction offset of each (see load_page; never negative)
   const uint32_t stride_b =
       2u * (uint32_t)(a.geo.paged ? kHeadDim : a.geo.num_kv_heads * kHeadDim);
   uint32_t voff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 2 * i + (lane >> 5);
-    voff[i] = (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ row);
+    voff[i] = (uint32_t)row * stride_b + 16u * (uint32_t)((lane & 31) ^ swz(row)) -
+              1024u * (uint32_t)(i & 3);
   }
 
   // missing-page masks of the tiles in the ring, 2 bits per slot
@@ -359,9 +408,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   // prologue: tiles 0 .. NST-2 in flight, and the page ids of tile NST-1
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < ntiles)
-      missing |= issue_tile<PAGED>(a, g, wave, s, kend, load_page_ids<PAGED>(a, s), ring[s],
-                                   voff, stride_b) << (2 * s);
+    if (s < ntiles) {
+      PageLoad pl;
+      missing |= plan_tile<PAGED>(a, g, wave, s, kend, load_page_ids<PAGED>(a, s), ring[s], pl)
+                 << (2 * s);
+      load_page(a, pl, voff, stride_b);
+    }
   PageIds ids_next = load_page_ids<PAGED>(a, NST - 1);
 
   // V^T operand d of a tile: keys 0 .. 31, dims 16d .. +15.  Lane (r16, q4)
@@ -372,15 +424,15 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   const int boff = (r16 & 1) * 8;                // byte within the chunk
   auto read_v = [&](const Tile<NK>& t, int d) {
     const int c = 2 * d + coff;
-    const char* p0 = reinterpret_cast<const char*>(&t.kv[1][kq][c ^ kq]) + boff;
-    const char* p1 = reinterpret_cast<const char*>(&t.kv[1][16 + kq][c ^ kq]) + boff;
+    const char* p0 = reinterpret_cast<const char*>(&t.kv[1][kq][c ^ swz(kq)]) + boff;
+    const char* p1 = reinterpret_cast<const char*>(&t.kv[1][16 + kq][c ^ swz(kq)]) + boff;
     const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p0));
     const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(void*)(p1));
     const uint2 w0 = __builtin_bit_cast(uint2, v0);
     const uint2 w1 = __builtin_bit_cast(uint2, v1);
     return make_uint4(w0.x, w0.y, w1.x, w1.y);
   };
-  constexpr int kVAhead = 8;                     // V^T operands read ahead of their MFMAs
+  constexpr int kVAhead = 4;                     // V^T operands read ahead of their MFMAs
   uint4 vpre[kVAhead];
   auto read_v_first = [&](const Tile<NK>& t) {
 #pragma unroll
@@ -394,13 +446,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   // before its use).
   float sv[kRB][4 * KB];
   float mxs[kRB];
-  auto scores = [&](const Tile<NK>& t, int32_t k0, uint32_t miss) {
+  auto scores = [&]<bool VPRE, class Hook>(const Tile<NK>& t, int32_t k0, uint32_t miss,
+                                           const Tile<NK>& tv, Hook&& hook) {
     constexpr int kKAhead = 4;
     uint4 kop[8][KB];
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kop[ks][kb] = t.kv[0][16 * kb + r16][(4 * ks + q4) ^ r16];
+      for (int kb = 0; kb < KB; ++kb) kop[ks][kb] = t.kv[0][16 * kb + r16][(4 * ks + q4) ^ swz(r16)];
     __builtin_amdgcn_sched_barrier(0);
     floatx4_t sacc[KB][kRB];
 #pragma unroll
@@ -412,13 +465,24 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
       if (ks + kKAhead < 8) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          kop[ks + kKAhead][kb] = t.kv[0][16 * kb + r16][(4 * (ks + kKAhead) + q4) ^ r16];
+          kop[ks + kKAhead][kb] = t.kv[0][16 * kb + r16][(4 * (ks + kKAhead) + q4) ^ swz(r16)];
+      } else if constexpr (VPRE) {
+        // the K reads are all issued: start the first V operands of the
+        // tile whose products follow
+        if (ks >= 8 - kVAhead / 2) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int d = 2 * (ks - (8 - kVAhead / 2)) + j;
+            vpre[d] = read_v(tv, d);
+          }
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
           sacc[kb][rb] = mfma16(kop[ks][kb], qreg[rb][ks], sacc[kb][rb]);
+      hook(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -485,29 +549,33 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) negm[rb] = -m_run[rb];
     __builtin_amdgcn_sched_barrier(0);
+    // softmax item i = (row block i / 8, score i % 8) follows product 2i
 #pragma unroll
     for (int d = 0; d < 16; ++d) {
       const uint4 vop = vr[d % kVAhead];
       if (d + kVAhead < 16) vr[d % kVAhead] = read_v(t, d + kVAhead);
-      o[d][0] = mfma16(vop, pc[0], o[d][0]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SM) {
-        const int rb = d / 8, e = d % 8;         // score e of row block rb
-        float x = fast_exp2(fmaf(sv[rb][e], c2, negm[rb]));
-        // instruction selection orders pure arithmetic freely; the empty asm
-        // pins this exponential to its slot between the two products
-        asm volatile("" : "+v"(x));
-        if (e & 1) w[rb][e >> 1] = cvt_pk_bf16(xe, x);
-        else xe = x;
-        mx[rb] = e ? fmaxf(mx[rb], sv[rb][e]) : sv[rb][e];
-        if (d == 8) mxs[0] = quad_max(mx[0]) * c2;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        o[d][rb] = mfma16(vop, pc[rb], o[d][rb]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int m = d * kRB + rb;
+        if constexpr (SM) {
+          if (m % 2 == 0 && m / 2 < 8 * kRB) {
+            const int r = m / 16, e = (m / 2) % 8;
+            float x = fast_exp2(fmaf(sv[r][e], c2, negm[r]));
+            // instruction selection orders pure arithmetic freely; the
+            // empty asm pins this exponential to its slot between products
+            asm volatile("" : "+v"(x));
+            if (e & 1) w[r][e >> 1] = cvt_pk_bf16(xe, x);
+            else xe = x;
+            mx[r] = e ? fmaxf(mx[r], sv[r][e]) : sv[r][e];
+            if (e == 7) mxs[r] = quad_max(mx[r]) * c2;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      o[d][1] = mfma16(vop, pc[1], o[d][1]);
-      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SM) {
-      mxs[1] = quad_max(mx[1]) * c2;
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         pn[rb] = make_uint4(w[rb][0], w[rb][1], w[rb][2], w[rb][3]);
@@ -533,21 +601,27 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   wait_tile<NK, NST>(min(NST - 2, ntiles - 1));
   wg_barrier();
   any_missing |= missing & 3u;
-  read_v_first(ring[0]);
-  scores(ring[0], 0, missing & 3u);
+  scores.template operator()<false>(ring[0], 0, missing & 3u, ring[0], [](int) {});
   tile_max();
   uint4 pcur[kRB], pnext[kRB];
   int32_t it = 0;
   for (;;) {
+    float alpha[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const bool raise = mxs[rb] > m_run[rb] + kRescale;
-      const float alpha = raise ? fast_exp2(m_run[rb] - mxs[rb]) : 1.0f;
+      alpha[rb] = raise ? fast_exp2(m_run[rb] - mxs[rb]) : 1.0f;
       if (raise) m_run[rb] = mxs[rb];
-#pragma unroll
-      for (int d = 0; d < 16; ++d) o[d][rb] *= alpha;
-      lsum[rb] *= alpha;
+      lsum[rb] *= alpha[rb];
     }
+    // one accumulator at a time, so that O never needs VGPR copies at once
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        o[d][rb] *= alpha[rb];
+        __builtin_amdgcn_sched_barrier(0);
+      }
     make_p(pcur);
     // Pending scalar loads on entry would make every LDS wait in the loop a
     // full one: wait for them here (lgkmcnt only; tiles stay in flight).
@@ -558,16 +632,22 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
                      islot = (uint32_t)(it + NST - 1) & (NST - 1);
       wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
       wg_barrier();
-      if (it + NST - 1 < ntiles) {
-        const uint32_t m = issue_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
-                                             ring[islot], voff, stride_b);
+      // plan tile it+NST-1 into the slot tile it-1 used; its 8 loads go out
+      // one per 32-dim step of the products below
+      const bool load = it + NST - 1 < ntiles;
+      PageLoad pl;
+      if (load) {
+        const uint32_t m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
+                                            ring[islot], pl);
         missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
+        load_page(a, pl, voff, stride_b);
       }
       const uint32_t miss = (missing >> (2 * nslot)) & 3u;
       any_missing |= miss;
-      scores(ring[nslot], (it + 1) * NK, miss);
+      scores.template operator()<true>(ring[nslot], (it + 1) * NK, miss, ring[cslot], [&](int ks) {
+
+      });
       pv.template operator()<true>(ring[cslot], pcur, pnext);
-      read_v_first(ring[nslot]);
       ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
       bool r = false;
 #pragma unroll
@@ -582,6 +662,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     }
     if (!raised) break;
   }
+  read_v_first(ring[(uint32_t)it & (NST - 1)]);
   pv.template operator()<false>(ring[(uint32_t)it & (NST - 1)], pcur, pnext);
 
   if (any_missing && threadIdx.x == 0) set_error(a.err, kErrBlockId);
