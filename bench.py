@@ -159,7 +159,7 @@ def bench_prefill(W, Y, torch, dev, reps):
             "ms_per_chunk": ms, "tflops": tf, "flop_per_chunk": flops,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": None}}
+                         "traffic": measured_traffic("prefill_chunk_8192_over_1m.json")}}
 
 
 def main():
