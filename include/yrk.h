@@ -227,7 +227,10 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
 
 /*
  * yrk_prefill_workspace_size -- bytes of device workspace that
- * yrk_prefill_attention needs (0 in this build; kept so callers size it).
+ * yrk_prefill_attention needs for num_q_tokens queries of num_q_heads heads
+ * (GQA group 6): one 32-bit word per wave of its launch grid, 16 bytes per
+ * 192 (token, head) rows rounded up to the XCD grid.  0 for an empty chunk or
+ * an unsupported head_dim.
  */
 size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t head_dim);
 
@@ -243,9 +246,19 @@ size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int
  *   q_dev        bf16 [num_q_tokens][num_q_heads][head_dim] (already roped)
  *   block_table_dev  int32 [block_table_len]; NULL for contiguous
  *   out_dev      bf16 [num_q_tokens][num_q_heads][head_dim]
- * Errors: YRK_EINVAL, YRK_ERANGE (positions beyond table or capacity),
- * YRK_ENOTSUP (dtype other than bf16, head_dim != 256, group size other
- * than 6), YRK_ENOSPC.
+ *   workspace_dev  device memory of at least yrk_prefill_workspace_size()
+ *                bytes, 4-byte aligned, owned by the caller; the call writes
+ *                it (no initial contents needed) and reads it back within the
+ *                same stream.  The first launch subtracts from each row the
+ *                maximum of its first 32 keys throughout; a wave whose row
+ *                sums end above 2^64, or whose accumulators are not finite,
+ *                sets its word, and a second launch recomputes that wave's
+ *                workgroup with a rescaling running maximum.  Calls that
+ *                share a workspace must not overlap.
+ * Errors: YRK_EINVAL (also a null or misaligned workspace), YRK_ERANGE
+ * (positions beyond table or capacity), YRK_ENOTSUP (dtype other than bf16,
+ * head_dim != 256, group size other than 6), YRK_ENOSPC (workspace smaller
+ * than yrk_prefill_workspace_size()).
  */
 int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t num_q_tokens,
                           int32_t num_q_heads, int64_t q_start_position,

@@ -121,7 +121,8 @@ def test_prefill_validation():
     def call(**kw):
         a = args(**kw)
         return f(ctypes.byref(kw.get("layer", L)), a["q"], a["T"], a["Hq"], a["start"], a["bt"],
-                 a["bt_len"], 0.0, a["out"], None, 0, None, None)
+                 a["bt_len"], 0.0, a["out"], kw.get("ws", 0x1000), kw.get("ws_bytes", 1 << 20),
+                 None, None)
 
     assert call(start=64 * 16 - 63) == Y.ERANGE
     assert call(bt=None) == Y.EINVAL
@@ -130,6 +131,14 @@ def test_prefill_validation():
     assert call(layer=_layer(dtype=Y.KV_NVFP4, k_scale=0x1, v_scale=0x1,
                              k_tensor_scale_dev=0x10, v_tensor_scale_dev=0x10)) == Y.ENOTSUP
     assert call(T=0, q=None, out=None) == Y.OK
+    # the workspace holds one flag word per wave of the launch grid
+    assert call(ws=None) == Y.EINVAL
+    assert call(ws=0x1002) == Y.EINVAL
+    need = Y.prefill_workspace_size(64, 24)
+    assert need == 8 * 4 * 4      # 2 row tiles of 192 rows, 2 XCDs per KV head
+    assert call(ws_bytes=need - 1) == Y.ENOSPC
+    assert Y.prefill_workspace_size(8192, 24) == 1024 * 4 * 4
+    assert Y.prefill_workspace_size(0, 24) == 0
 
 
 def test_tensor_scale_validation():

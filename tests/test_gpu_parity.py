@@ -448,7 +448,11 @@ def test_decode_paged_equals_contiguous_and_repeats_bitwise(Y, W):
 
 # -- prefill ----------------------------------------------------------------------
 
-def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None):
+def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
+    """needle = (t, key, mul): after rope, key position `key` of every KV head
+    g is set to mul (a power of two) x the roped query of chunk token t, head
+    6g (exact in bf16), so that query's score there is far above its first
+    tile's maximum."""
     total = n_prior + T
     pages = -(-total // 16) + 1
     t = O.yarn_table()
@@ -462,6 +466,10 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None):
     pos_all = torch.arange(total, dtype=torch.int32, device=DEV)
     Y.yarn_rope_apply(yp, kt, pos_all)
     Y.yarn_rope_apply(yp, qt, pos_all[n_prior:])
+    if needle is not None:
+        nt, nk, mul = needle
+        for g in range(4):
+            kt[nk, g] = qt[nt, 6 * g] * mul
     L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=paged, device=DEV)
     table = synth.block_permutation(seed, pages) if paged else None
     bt = torch.from_numpy(table).to(DEV) if paged else None
@@ -471,19 +479,27 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None):
         bt[bad_page] = pages + 5
     out = torch.empty_like(qt)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    Y.prefill_attention(L, qt, n_prior, bt, out, err=err)
+    ws = torch.full((Y.prefill_workspace_size(T, 24) // 4,), 7, dtype=torch.int32, device=DEV)
+    Y.prefill_attention(L, qt, n_prior, bt, out, workspace=ws, err=err)
     torch.cuda.synchronize()
+    flags = ws.cpu().numpy()
     k = O.rope(k_raw, np.arange(total), t, bf16_out=True)
     q = O.rope(q_raw, np.arange(n_prior, total), t, bf16_out=True)
-    return _f64(out), O.bf16_to_f64(q), k, v_raw, int(err.item())
+    if needle is not None:
+        nt, nk, mul = needle
+        for g in range(4):      # a power-of-two multiple of a bf16 value is exact
+            src = q[nt, 6 * g].astype(np.uint32) << 16
+            k[nk, g] = ((src.view(np.float32) * mul).view(np.uint32) >> 16).astype(k.dtype)
+    return _f64(out), O.bf16_to_f64(q), k, v_raw, int(err.item()), flags
 
 
 @pytest.mark.parametrize("n_prior,T,paged", [(1000, 77, True), (0, 200, False),
                                              (4093, 130, True), (31, 1, True)])
 def test_prefill_small_matches_oracle(Y, n_prior, T, paged):
     _say(f"prefill n_prior={n_prior} T={T} paged={paged}")
-    got, q, k, v, err = _prefill_small(Y, n_prior, T, paged, seed=300 + T)
+    got, q, k, v, err, flags = _prefill_small(Y, n_prior, T, paged, seed=300 + T)
     assert err == 0
+    assert not flags.any()       # every wave stayed within its first tile's headroom
     ref = O.prefill_attention(q, np.arange(n_prior, n_prior + T), k, v)
     _compare_attention(f"prefill/{n_prior}+{T}", got, ref)
     if n_prior == 0:
@@ -494,7 +510,7 @@ def test_prefill_small_matches_oracle(Y, n_prior, T, paged):
 
 def test_prefill_flags_and_masks_a_bad_page(Y):
     n_prior, T = 500, 40
-    got, q, k, v, err = _prefill_small(Y, n_prior, T, True, seed=77, bad_page=3)
+    got, q, k, v, err, _ = _prefill_small(Y, n_prior, T, True, seed=77, bad_page=3)
     assert err == Y.DEVERR_BLOCK_ID
     keep = np.r_[0:48, 64:n_prior + T]
     refs = []
@@ -503,6 +519,31 @@ def test_prefill_flags_and_masks_a_bad_page(Y):
         kk = keep[keep <= p]
         refs.append(O.decode_attention(q[i], k[kk], v[kk]))
     _compare_attention("prefill/bad_page", got, np.stack(refs))
+
+
+@pytest.mark.parametrize("paged,mul,flagged", [(True, 2, False), (False, 2, False),
+                                                (True, 4, True), (False, 8, True)])
+def test_prefill_score_far_above_the_first_tile(Y, paged, mul, flagged):
+    """Key 500 of every KV head set to mul x the roped query of token 40,
+    head 6g: that query's score there lies 39-48 (mul 2), 80-98 (mul 4) or
+    162-199 (mul 8) log2 units above its first tile's maximum.  Up to 2^64
+    the fixed-maximum kernel keeps the row (no flag); beyond, the row sum
+    exceeds 2^64 or exp2 overflows, the wave is flagged and the rescaling
+    launch recomputes its workgroup.  Either way the output matches the
+    oracle."""
+    n_prior, T = 1000, 77
+    _say(f"prefill needle paged={paged} mul={mul}")
+    got, q, k, v, err, flags = _prefill_small(Y, n_prior, T, paged, seed=411,
+                                              needle=(40, 500, mul))
+    assert err == 0
+    assert set(np.unique(flags).tolist()) <= {0, 1}
+    assert bool(flags.any()) == flagged
+    ref = O.prefill_attention(q, np.arange(n_prior, n_prior + T), k, v)
+    _compare_attention("prefill/needle", got, ref)
+    # the needle dominates the softmax of query 40, head 6g: out ~ V[500, g]
+    vf = O.bf16_to_f64(v)
+    for g in range(4):
+        assert np.abs(got[40, 6 * g] - vf[500, g]).max() < 0.05
 
 
 def test_prefill_workload_sampled_rows(Y, W):

@@ -91,6 +91,10 @@ def _check(status, where):
         raise YrkError(status, where)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -208,7 +212,7 @@ def decode_attention(layer: KVLayer, q, block_tables, seq_lens, max_seq_len, out
     _check(_lib.yrk_decode_attention(ctypes.byref(lc), q.data_ptr(), S, Hq, _ptr(block_tables),
                                      bt_stride, seq_lens.data_ptr(), max_seq_len,
                                      softmax_scale, out.data_ptr(), out_dtype,
-                                     workspace.data_ptr(), workspace.numel(), _ptr(err),
+                                     workspace.data_ptr(), _nbytes(workspace), _ptr(err),
                                      _stream(q)), "yrk_decode_attention")
     return out
 
@@ -219,13 +223,18 @@ def prefill_workspace_size(num_q_tokens, num_q_heads, head_dim=HEAD_DIM):
 
 def prefill_attention(layer: KVLayer, q, q_start_position, block_table, out, workspace=None,
                       softmax_scale=0.0, err=None):
-    """q: bf16 [T, Hq, 256] at positions q_start_position + i; out: bf16 like q."""
+    """q: bf16 [T, Hq, 256] at positions q_start_position + i; out: bf16 like q.
+    workspace: device buffer of prefill_workspace_size(T, Hq) bytes (allocated
+    here when not given)."""
     T, Hq, _ = q.shape
+    if workspace is None and T > 0:
+        workspace = torch.empty(max(prefill_workspace_size(T, Hq), 4), dtype=torch.uint8,
+                                device=q.device)
     lc = layer.c()
     bt_len = block_table.numel() if block_table is not None else 0
     _check(_lib.yrk_prefill_attention(ctypes.byref(lc), q.data_ptr(), T, Hq, q_start_position,
                                       _ptr(block_table), bt_len, softmax_scale, out.data_ptr(),
                                       _ptr(workspace),
-                                      workspace.numel() if workspace is not None else 0,
+                                      _nbytes(workspace) if workspace is not None else 0,
                                       _ptr(err), _stream(q)), "yrk_prefill_attention")
     return out

@@ -238,10 +238,8 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
 }
 
 size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t head_dim) {
-  (void)num_q_tokens;
-  (void)num_q_heads;
-  (void)head_dim;
-  return 0;
+  if (num_q_tokens < 0 || num_q_heads <= 0 || head_dim != yrk::kHeadDim) return 0;
+  return yrk::prefill_workspace_bytes(num_q_tokens, num_q_heads);
 }
 
 int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t num_q_tokens,
@@ -249,8 +247,6 @@ int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t 
                           const int32_t* block_table_dev, int64_t block_table_len,
                           float softmax_scale, void* out_dev, void* workspace_dev,
                           size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream) {
-  (void)workspace_dev;
-  (void)workspace_bytes;
   int rc = check_layer(layer);
   if (rc) return rc;
   if (num_q_tokens < 0 || num_q_heads <= 0 || q_start_position < 0) return YRK_EINVAL;
@@ -268,6 +264,8 @@ int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t 
   if (layer->dtype != YRK_KV_BF16) return YRK_ENOTSUP;
   const int group = num_q_heads / layer->num_kv_heads;
   if (group != 6) return YRK_ENOTSUP;
+  if (!workspace_dev || ((uintptr_t)workspace_dev & 3u) != 0) return YRK_EINVAL;
+  if (workspace_bytes < yrk::prefill_workspace_bytes(num_q_tokens, num_q_heads)) return YRK_ENOSPC;
   if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
   yrk::PrefillArgs a;
   a.geo = geometry(layer);
@@ -283,6 +281,7 @@ int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t 
   a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
   a.out = static_cast<uint16_t*>(out_dev);
   a.err = dev_error_word;
+  a.flags = static_cast<uint32_t*>(workspace_dev);
   return launch_status(yrk::launch_prefill(a, stream));
 }
 

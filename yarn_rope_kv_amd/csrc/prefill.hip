@@ -69,6 +69,7 @@ constexpr int kRowsPerWG = kRowsPerWave * kWavesP;   // 192 (token, head) rows =
 constexpr int kRB = kRowsPerWave / 16;    // 3 row blocks per wave
 constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per row
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
+constexpr float kMaxRowSum = 0x1p64f;     // main kernel: largest row sum it accepts
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
 constexpr int kNK = 32;                   // keys per tile
 constexpr int kNST = 4;                   // tiles in the LDS ring
@@ -312,7 +313,20 @@ __device__ __forceinline__ void wait_tile(int32_t tiles_after) {
   else wait_vm<0>();
 }
 
-template <int NK, int NST, bool PAGED>
+// FALLBACK = false: the main kernel.  Each row's maximum is fixed at the
+// maximum of its first key tile (the softmax is the same for any constant
+// subtracted from a row's scores; only the range of exp2 limits the choice).
+// The tile loop then needs neither a running maximum nor its cross-lane
+// reduction, keeps O in AGPRs and spills nothing (a spill reloaded ahead of
+// the loop makes the compiler leave counter waits inside it that stall on
+// the tiles in flight).  After the loop each wave checks that its rows
+// stayed in range and records a flag in the workspace (one word per wave)
+// when they did not.
+// FALLBACK = true: launched right after on the same grid; a workgroup with
+// a flag set recomputes its rows with a running maximum that is raised (and
+// O rescaled) whenever a tile exceeds it by more than kRescale, and every
+// other workgroup returns at once.
+template <int NK, int NST, bool PAGED, bool FALLBACK>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, int32_t tiles,
                                                                int32_t xcd_share) {
   static_assert(NST == 4, "ring depth (slot arithmetic assumes a power of two)");
@@ -330,7 +344,16 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     g = b % a.geo.num_kv_heads;
     tile = b / a.geo.num_kv_heads;
   }
-  if (g >= a.geo.num_kv_heads || tile >= tiles) return;
+  if (g >= a.geo.num_kv_heads || tile >= tiles) {
+    // a workgroup of the rounded-up grid with no rows: its flags read clear
+    if (!FALLBACK && (threadIdx.x & 63) == 0) a.flags[4 * (int64_t)b + (threadIdx.x >> 6)] = 0;
+    return;
+  }
+  if constexpr (FALLBACK) {
+    // the same decision in every wave of the workgroup
+    const uint32_t* f = a.flags + 4 * (int64_t)b;
+    if ((f[0] | f[1] | f[2] | f[3]) == 0) return;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -432,7 +455,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     const uint2 w1 = __builtin_bit_cast(uint2, v1);
     return make_uint4(w0.x, w0.y, w1.x, w1.y);
   };
-  constexpr int kVAhead = 4;                     // V^T operands read ahead of their MFMAs
+  constexpr int kVAhead = 6;                     // V^T operands read ahead of their MFMAs (even, <= 16)
   uint4 vpre[kVAhead];
   auto read_v_first = [&](const Tile<NK>& t) {
 #pragma unroll
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   float mxs[kRB];
   auto scores = [&]<bool VPRE, class Hook>(const Tile<NK>& t, int32_t k0, uint32_t miss,
                                            const Tile<NK>& tv, Hook&& hook) {
-    constexpr int kKAhead = 4;
+    constexpr int kKAhead = 3;
     uint4 kop[8][KB];
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks)
@@ -466,9 +489,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
           kop[ks + kKAhead][kb] = t.kv[0][16 * kb + r16][(4 * (ks + kKAhead) + q4) ^ swz(r16)];
-      } else if constexpr (VPRE) {
-        // the K reads are all issued: start the first V operands of the
-        // tile whose products follow
+      }
+      if constexpr (VPRE) {
+        // the first V operands of the tile whose products follow, two per
+        // step over the last kVAhead / 2 steps
         if (ks >= 8 - kVAhead / 2) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -605,6 +629,37 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   tile_max();
   uint4 pcur[kRB], pnext[kRB];
   int32_t it = 0;
+  if constexpr (!FALLBACK) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) m_run[rb] = fmaxf(mxs[rb], kNegBig);
+    make_p(pcur);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // pending scalar loads only
+    for (; it + 1 < ntiles; ++it) {
+      const uint32_t cslot = (uint32_t)it & (NST - 1), nslot = (uint32_t)(it + 1) & (NST - 1),
+                     islot = (uint32_t)(it + NST - 1) & (NST - 1);
+      wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
+      wg_barrier();
+      // plan tile it+NST-1 into the slot tile it-1 used; its 8 loads go out
+      // one per 32-dim step of the products below
+      const bool load = it + NST - 1 < ntiles;
+      PageLoad pl;
+      if (load) {
+        const uint32_t m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
+                                            ring[islot], pl);
+        missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
+        load_page(a, pl, voff, stride_b);
+      }
+      const uint32_t miss = (missing >> (2 * nslot)) & 3u;
+      any_missing |= miss;
+      scores.template operator()<true>(ring[nslot], (it + 1) * NK, miss, ring[cslot], [&](int ks) {
+
+      });
+      pv.template operator()<true>(ring[cslot], pcur, pnext);
+      ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) pcur[rb] = pnext[rb];
+    }
+  } else {
   for (;;) {
     float alpha[kRB];
 #pragma unroll
@@ -662,10 +717,32 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
     }
     if (!raised) break;
   }
+  }
   read_v_first(ring[(uint32_t)it & (NST - 1)]);
   pv.template operator()<false>(ring[(uint32_t)it & (NST - 1)], pcur, pnext);
 
   if (any_missing && threadIdx.x == 0) set_error(a.err, kErrBlockId);
+
+  if constexpr (!FALLBACK) {
+    // With the maximum fixed, every p of a row is at most its row sum l (the
+    // first tile's maximum contributes exactly 1 and no p is negative): if l
+    // <= 2^64 and O is finite, no step overflowed and 1/l is a normal number,
+    // so the result is as accurate as with a running maximum.  Otherwise
+    // (scores far above the first tile's, or non-finite inputs) the wave is
+    // flagged and the second launch recomputes its workgroup.
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      bool rbad = !(lsum[rb][0] <= kMaxRowSum);
+#pragma unroll
+      for (int d = 0; d < 16; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rbad |= !__builtin_isfinite(o[d][rb][e]);
+      bad |= valid[rb] && rbad;
+    }
+    const bool flagged = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) a.flags[4 * (int64_t)b + wave] = flagged ? 1u : 0u;
+  }
 
   // normalise by the row sum and store dims 16d + 4q4 .. +3
 #pragma unroll
@@ -687,20 +764,43 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 
 }  // namespace
 
+namespace {
+// Launch grid: workgroups numbered so that each XCD (block id mod 8) serves
+// one KV head when the head count divides 8.
+struct PrefillGrid {
+  int32_t tiles, share;
+  int64_t blocks;
+};
+PrefillGrid prefill_grid(int64_t num_q_tokens, int32_t num_kv_heads) {
+  PrefillGrid gr;
+  gr.tiles = (int32_t)((num_q_tokens * kGroup + kRowsPerWG - 1) / kRowsPerWG);
+  gr.share = 0;
+  gr.blocks = (int64_t)gr.tiles * num_kv_heads;
+  if (num_kv_heads <= 8 && 8 % num_kv_heads == 0) {
+    gr.share = 8 / num_kv_heads;   // XCDs per KV head
+    gr.blocks = 8 * (((int64_t)gr.tiles + gr.share - 1) / gr.share);
+  }
+  return gr;
+}
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t num_q_tokens, int32_t num_q_heads) {
+  if (num_q_tokens <= 0 || num_q_heads % kGroup) return 0;
+  return (size_t)prefill_grid(num_q_tokens, num_q_heads / kGroup).blocks * kWavesP * sizeof(uint32_t);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.group != kGroup) return hipErrorInvalidValue;
-  const int64_t rows = a.num_q_tokens * kGroup;
-  const int32_t tiles = (int32_t)((rows + kRowsPerWG - 1) / kRowsPerWG);
-  const int H = a.geo.num_kv_heads;
-  int32_t share = 0;
-  int64_t blocks = (int64_t)tiles * H;
-  if (H <= 8 && 8 % H == 0) {
-    share = 8 / H;   // XCDs per KV head
-    blocks = 8 * (((int64_t)tiles + share - 1) / share);
-  }
-  auto kernel = a.geo.paged ? prefill_kernel<kNK, kNST, true> : prefill_kernel<kNK, kNST, false>;
-  return launch(kernel, dim3((unsigned)blocks), dim3(kPThreads), 0, s, a,
-                tiles, share);
+  const PrefillGrid gr = prefill_grid(a.num_q_tokens, a.geo.num_kv_heads);
+  auto main_kernel = a.geo.paged ? prefill_kernel<kNK, kNST, true, false>
+                                 : prefill_kernel<kNK, kNST, false, false>;
+  auto fallback = a.geo.paged ? prefill_kernel<kNK, kNST, true, true>
+                              : prefill_kernel<kNK, kNST, false, true>;
+  hipError_t e = launch(main_kernel, dim3((unsigned)gr.blocks), dim3(kPThreads), 0, s, a,
+                        gr.tiles, gr.share);
+  if (e != hipSuccess) return e;
+  return launch(fallback, dim3((unsigned)gr.blocks), dim3(kPThreads), 0, s, a, gr.tiles,
+                gr.share);
 }
 
 }  // namespace yrk

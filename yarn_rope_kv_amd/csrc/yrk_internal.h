@@ -105,7 +105,11 @@ struct PrefillArgs {
   float scale_log2;
   uint16_t* out;
   uint32_t* err;
+  uint32_t* flags;           // one word per wave of the main kernel (workspace)
 };
+// Bytes of prefill workspace: one flag word per wave of the launch grid
+// (0 when the shape is not supported; the call then fails on its own).
+size_t prefill_workspace_bytes(int64_t num_q_tokens, int32_t num_q_heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace yrk
