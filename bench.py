@@ -234,7 +234,9 @@ def main():
             "unit": "KV token-layers/s", "avg_launch_ms": kf,
             "roofline": {"bound": "hbm", "achieved": bplf / (kf * 1e-3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bplf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": bplf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_split_nvfp4_long_fp4_1m.json"),
+                         "bytes_per_launch": bplf}}
         del lf, stepf, evf
         torch.cuda.empty_cache()
     if not args.no_prefill:

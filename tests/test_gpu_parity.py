@@ -446,6 +446,129 @@ def test_decode_paged_equals_contiguous_and_repeats_bitwise(Y, W):
     assert torch.equal(out1, out2) and torch.equal(out1, out3)
 
 
+# -- decode: ragged batches in both cache formats and several GQA shapes -------------
+
+_LENS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1000, 4097]
+
+
+def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=None):
+    """One batched decode call over sequences of the given lengths.  Keys are
+    roped on the host by the oracle and appended (and, for NVFP4, quantised)
+    by the library, so the cache holds exactly what the oracle quantises.
+    q_mul (a power of two) scales q, and the softmax scale is divided by it:
+    the same attention.  Returns (gpu fp64 [S, hq, 256], per-sequence oracle
+    outputs, device error word)."""
+    S = len(lens)
+    max_len = max(max(lens), 1)
+    pages_per = -(-max_len // 16) + 1
+    pool = S * pages_per
+    t = O.yarn_table()
+    qs, ks, vs = [], [], []
+    for s, n in enumerate(lens):
+        q_raw = synth.host_fill(seed, synth.stream_id(s, synth.Q), 0, 1, hq, 256)
+        k_raw = synth.host_fill(seed, synth.stream_id(s, synth.K), 0, max(n, 1), hkv, 256)[:n]
+        v_raw = synth.host_fill(seed, synth.stream_id(s, synth.V), 0, max(n, 1), hkv, 256)[:n]
+        qs.append(O.rope(q_raw, [n], t, bf16_out=True)[0])
+        ks.append(O.rope(k_raw, np.arange(n), t, bf16_out=True) if n else k_raw)
+        vs.append(v_raw)
+    allk, allv = np.concatenate(ks), np.concatenate(vs)
+    L = Y.KVLayer.allocate(kv, hkv, pool, paged=paged, device=DEV)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(
+        torch.bfloat16)
+    nv = None
+    if kv == Y.KV_NVFP4:
+        Y.nvfp4_tensor_scale(dev(allk), L.k_tensor_scale)
+        Y.nvfp4_tensor_scale(dev(allv), L.v_tensor_scale)
+        kS, vS = O.nvfp4_tensor_scale(allk), O.nvfp4_tensor_scale(allv)
+        assert L.k_tensor_scale.item() == float(kS) and L.v_tensor_scale.item() == float(vS)
+    if paged:
+        table = synth.block_permutation(seed, pool).reshape(S, pages_per)
+        bt = torch.from_numpy(table).to(DEV)
+    else:
+        assert S == 1
+        bt = None
+    for s, n in enumerate(lens):
+        if n:
+            Y.kv_append_quantize(L, dev(ks[s]), dev(vs[s]), bt[s] if paged else None,
+                                 torch.arange(n, dtype=torch.int32, device=DEV))
+    q = dev(np.stack(qs))
+    if q_mul != 1.0:
+        q = q * q_mul
+    out = torch.empty((S, hq, 256), dtype=torch.float32, device=DEV)
+    ws = torch.empty(Y.decode_workspace_size(S, hq, hkv, max_len), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    tables = bt
+    keep = [np.arange(n) for n in lens]
+    if bad_page is not None:
+        s_bad, page = bad_page
+        tables = bt.clone()
+        tables[s_bad, page] = pool + 3
+        keep[s_bad] = keep[s_bad][keep[s_bad] // 16 != page]
+    Y.decode_attention(L, q, tables, torch.tensor(lens, dtype=torch.int32, device=DEV), max_len,
+                       out, ws, softmax_scale=1.0 / 16 / q_mul, err=err)
+    torch.cuda.synchronize()
+    refs = []
+    for s, n in enumerate(lens):
+        qf = O.bf16_to_f64(qs[s])
+        kk, vv = ks[s][keep[s]], vs[s][keep[s]]
+        if kv == Y.KV_NVFP4:
+            kc, ksc = O.nvfp4_quantize(kk, kS)
+            vc, vsc = O.nvfp4_quantize(vv, vS)
+            refs.append(O.decode_attention(qf, kc, vc, nvfp4=(ksc, vsc, kS, vS)) if n else
+                        np.zeros((hq, 256)))
+        else:
+            refs.append(O.decode_attention(qf, kk, vv) if n else np.zeros((hq, 256)))
+    return _f64(out), refs, int(err.item())
+
+
+@pytest.mark.parametrize("hq,hkv", [(24, 4), (4, 4), (8, 4), (12, 4), (16, 4), (12, 2)])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_decode_ragged_shapes(Y, fmt, hq, hkv):
+    """Lengths around the 16-token page and the 32-token NVFP4 step, an empty
+    sequence and multi-split ones, for every supported group size and the
+    12-query / 2-KV-head shape of one card's share of a two-way head split."""
+    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    _say(f"decode ragged {fmt} hq={hq} hkv={hkv}")
+    got, refs, err = _decode_batch(Y, kv, _LENS, hq, hkv, seed=700 + hq + 100 * hkv)
+    assert err == 0
+    assert np.all(got[0] == 0)
+    for s in range(1, len(_LENS)):
+        _compare_attention(f"ragged/{fmt}/{hq}x{hkv}/len{_LENS[s]}", got[s], refs[s],
+                           bf16_out=False)
+
+
+def test_decode_nvfp4_masks_and_flags_a_bad_page(Y):
+    _say("decode nvfp4 bad page")
+    got, refs, err = _decode_batch(Y, Y.KV_NVFP4, [300, 77], 24, 4, seed=810, bad_page=(0, 5))
+    assert err == Y.DEVERR_BLOCK_ID
+    for s in range(2):
+        _compare_attention(f"nvfp4_bad_page/{s}", got[s], refs[s], bf16_out=False)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_decode_contiguous_equals_paged_bitwise(Y, fmt):
+    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    _say(f"decode contiguous vs paged {fmt}")
+    a, refs, _ = _decode_batch(Y, kv, [1234], 24, 4, seed=820, paged=True)
+    b, _, _ = _decode_batch(Y, kv, [1234], 24, 4, seed=820, paged=False)
+    assert np.array_equal(a, b)
+    _compare_attention(f"contiguous/{fmt}", b[0], refs[0], bf16_out=False)
+
+
+@pytest.mark.parametrize("q_mul", [2.0 ** 20, 2.0 ** -30])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_decode_query_magnitude(Y, fmt, q_mul):
+    """q scaled by a power of two far outside [2^-14, 2^15] and the softmax
+    scale divided by it: the same attention, which the NVFP4 kernel computes
+    with q prescaled into fp16's range."""
+    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    _say(f"decode q x {q_mul} {fmt}")
+    got, refs, err = _decode_batch(Y, kv, [500, 33], 24, 4, seed=830, q_mul=q_mul)
+    assert err == 0
+    for s in range(2):
+        _compare_attention(f"q_mul/{fmt}/{q_mul:g}/{s}", got[s], refs[s], bf16_out=False)
+
+
 # -- prefill ----------------------------------------------------------------------
 
 def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):

@@ -1,7 +1,10 @@
 """Builds libyrk.so in place: every HIP source for gfx950, then one link.
 
 Device code is compiled with packed-fp32 instruction selection turned off
-(-Xclang -target-feature -Xclang -packed-fp32-ops)."""
+(-Xclang -target-feature -Xclang -packed-fp32-ops).  The decode kernels keep
+their MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the NVFP4 split
+kernel rescales its output accumulators with vector instructions every step,
+which on AGPRs would cost a read and a write per element."""
 import os
 import subprocess
 import sys
@@ -16,6 +19,7 @@ SOURCES = ["capi.cpp", "rope.hip", "kv_append.hip", "decode.hip", "prefill.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -35,7 +39,8 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append(["hipcc", *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append(["hipcc", *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(_run, cmds))

@@ -176,8 +176,12 @@ size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != yrk::kHeadDim ||
       max_seq_len < 0)
     return 0;
-  const yrk::DecodePlan p = yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len);
-  return yrk::decode_workspace_bytes(num_seqs, num_q_heads, p);
+  // the cache format is not an argument here: enough for either plan
+  const size_t b16 = yrk::decode_workspace_bytes(
+      num_seqs, num_q_heads, yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len, YRK_KV_BF16));
+  const size_t f4 = yrk::decode_workspace_bytes(
+      num_seqs, num_q_heads, yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len, YRK_KV_NVFP4));
+  return b16 > f4 ? b16 : f4;
 }
 
 int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
@@ -206,7 +210,7 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   }
   if (max_seq_len > INT32_MAX) return YRK_ERANGE;
   yrk::DecodeArgs a;
-  a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len);
+  a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len, layer->dtype);
   const size_t need = yrk::decode_workspace_bytes(num_seqs, num_q_heads, a.plan);
   if (workspace_bytes < need) return YRK_ENOSPC;
   if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);

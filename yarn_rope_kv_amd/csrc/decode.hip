@@ -51,7 +51,10 @@ __device__ __forceinline__ uint32_t err_flag(uint32_t* err, uint32_t bit) {
 __device__ __forceinline__ bool page_base(const DecodeArgs& a, int s, int g, int64_t page,
                                           int64_t row_elems, int64_t* base, int64_t* tstride) {
   if (a.geo.paged) {
-    const int64_t blk = a.block_tables[(int64_t)s * a.block_table_stride + page];
+    // one table entry for the whole wave: make that explicit, so the page
+    // test below is a scalar branch and not a per-lane one
+    const int64_t blk = __builtin_amdgcn_readfirstlane(
+        a.block_tables[(int64_t)s * a.block_table_stride + page]);
     if (blk < 0 || blk >= a.geo.num_blocks) return false;
     *base = ((blk * a.geo.num_kv_heads + g) * kBlockSize) * row_elems;
     *tstride = row_elems;
@@ -106,7 +109,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, int s, int g, 
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -163,7 +166,7 @@ template <int G>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int r = lane >> 4, c = lane & 15;
 
   int64_t len = a.seq_lens[s];
@@ -280,31 +283,130 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
                   [](int cc, int e) { return e < 8 ? 8 * cc + e : 128 + 8 * cc + (e - 8); });
 }
 
-// ---- NVFP4 ----------------------------------------------------------------
+// ---- NVFP4 on the matrix cores ----------------------------------------------
+//
+// With 6 query heads per KV head, the scores of a page are a 16 x 16 product
+// (16 tokens x 6 heads padded to 16) over the 256 head dims, and the output a
+// 256 x 16 product over the page's tokens: the kernel runs both on
+// v_mfma_f32_16x16x32_f16 and keeps only the dequantisation and the softmax
+// on the vector ALUs.  A wave takes 32 tokens (two pages) per step.
+//
+//   dequant   the scaled fp4 conversion multiplies by a power of two only (it
+//             takes the exponent of its fp32 scale), so a block scale q_s
+//             (e4m3) is applied as 2^E in the conversion and then (1 + m/8)
+//             in a packed fp16 multiply.  e2m1 x q_s has at most 6 significant
+//             bits and lies in [2^-10, 2688]: both steps are exact in fp16.
+//   S^T       = K Q^T.  Lane (t, kg) = (lane % 16, lane / 16) reads code bytes
+//             [32kg, 32kg+32) of token row t (head dims [64kg, 64kg+64), scale
+//             blocks 4kg..4kg+3: one scale dword) and supplies dims
+//             64kg + 8j .. +7 at MFMA step j; the Q^T operand holds the same
+//             dims of head t (zero for heads >= G), prescaled by a power of
+//             two so that |q| < 2^15 fits fp16 (bf16 values are then exact).
+//   softmax   lane (h, r) holds the scores of head h at tokens 4r..4r+3 of
+//             both pages: the accumulator layout is the P^T operand of the
+//             output product as it stands.  Online, log2 domain, with the
+//             running maximum m and the rescale of O applied on every step
+//             (a conditional rescale makes the compiler keep a second copy
+//             of the accumulators around the loop).  p = 2^(s - m + 14) is
+//             rounded to fp16 (nearest even); the row sums are a product of
+//             those same values with ones.
+//   O^T      += V^T P^T.  V is dequantised to fp16 into a per-wave LDS buffer
+//             (token rows, 16-byte chunks swizzled); ds_read_b64_tr_b16 turns
+//             4 rows x 4 dims per 16 lanes into the V^T operand: lane j of
+//             lane group r gets dim 16i + j at tokens 4r..4r+3.
+//   loads     the codes and scales of the wave's next 32 tokens are in flight
+//             while the current ones are computed.
 
-// Eight e2m1 codes (one 32-bit word, element 2j in the low nibble of byte j)
-// -> eight bf16 values as four packed pairs, via the gfx950 fp4 -> bf16
-// conversion with unit scale.
-__device__ __forceinline__ void fp4x8_to_bf16(uint32_t w, uint32_t (&out)[4]) {
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
-  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
-  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // (HIP's uint4 copies as a struct)
+
+constexpr int kUnitPages = 2;                            // pages per wave step
+constexpr int kRowBytesF16 = kHeadDim * 2;               // staged V row
+constexpr int kStageBytes = kWaves * kUnitPages * kBlockSize * kRowBytesF16;   // 64 KiB
+constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
+// p = 2^(s - m + kPShiftF4) <= 2^14 in fp16: the shift keeps probabilities
+// down to 2^-28 of the row maximum at full fp16 precision (and to 2^-38 as
+// subnormals); it cancels in O / l and is taken off the log-sum-exp.
+constexpr float kPShiftF4 = 14.0f;
+
+__device__ __forceinline__ floatx4_t mfma_f16(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// OCP E4M3FN scale byte (sign clear, not NaN) -> fp32, exact: normal codes
-// become (1 + m/8) 2^(e-7) by placing the fields, subnormals m 2^-9.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+// Two floats -> packed fp16, rounded to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, f16x2_t));
 }
+
+// Block scale (e4m3 byte SEL of w) as the power of two the scaled conversion
+// applies and the factor 1 + m/8 as a packed fp16 pair.  The hardware fp8
+// conversion decodes OCP E4M3FN exactly; the fp16 factor takes the top ten
+// mantissa bits of the fp32 value (e4m3 has three).  A zero scale gives 2^-127
+// in the conversion (which underflows to zero in fp16) times 1.
+struct BlockScale {
+  float pow2;
+  uint32_t mant2;
+};
+template <int SEL>
+__device__ __forceinline__ BlockScale split_scale(uint32_t w) {
+  const uint32_t b = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)w, SEL));
+  const uint32_t mh = 0x3C00u | ((b >> 13) & 0x3FFu);
+  return {__uint_as_float(b & 0x7F800000u), mh | (mh << 16)};
+}
+
+// Eight e2m1 codes (one dword; element 2j in the low nibble of byte j) ->
+// eight fp16 values code x q_s, exactly.
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, const BlockScale& bs) {
+  const f16x2_t m = __builtin_bit_cast(f16x2_t, bs.mant2);
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 0) * m;
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 1) * m;
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 2) * m;
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 3) * m;
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
+// Maximum over lanes l, l^16, l^32, l^48 (the four row groups of an MFMA
+// accumulator) with the gfx950 cross-row lane swaps.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Staged V row t keeps 16-byte chunk c at position c ^ vswz(t).  vswz is a
+// permutation of 0..7 on rows 0..7 and on rows 8..15 (so the 8 lanes of a
+// 128-byte write phase, rows t..t+7 with one chunk index, hit distinct banks)
+// and gives rows 4r..4r+3 distinct bits 1-2 (so the transposing reads, 4 rows
+// x 32 bytes per 16 lanes, fall into 4 distinct 32-byte bank groups).
+__device__ __forceinline__ int vswz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// One lane's share of the two pages of a wave step.
+struct F4Unit {
+  u32x4_t kc[kUnitPages][2], vc[kUnitPages][2]; // code bytes [32kg, 32kg+32) of row t
+  uint32_t ks[kUnitPages], vs[kUnitPages];      // scale bytes 4kg..4kg+3 of row t
+  bool ok[kUnitPages];                          // page present and inside the split
+};
 
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
+  static_assert((kWaves * G * kHeadDim + 2 * kWaves * G) * 4 <= kStageBytes,
+                "split combine reuses the staging buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytes];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int lo = lane & 15, hi = lane >> 4;
 
   int64_t len = a.seq_lens[s];
   if (len > a.max_seq_len) {
@@ -315,124 +417,242 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
   const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
   const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
 
-  float m[G], l[G], acc[G][16];
+  floatx4_t o[16];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
-  }
+  for (int i = 0; i < 16; ++i) o[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig;
+  float vS = 1.0f;
 
   if (tok1 > tok0) {
     const float kS = *a.k_tensor_scale;
-    const float vS = *a.v_tensor_scale;
-    const float qk_scale = a.scale_log2 * kS;
-    // q slice of this lane: dims [16c, 16c+16) of each head
-    uint4 qa[G][2];
-    const uint16_t* qbase = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * kHeadDim;
+    vS = *a.v_tensor_scale;
+    // Q^T operand: head lo, dims [64 hi, 64 hi + 64), 8 per MFMA step
+    uint4 qraw[8];
+    float qmax = 0.f;
+    const uint16_t* qrow = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G + lo) * kHeadDim + 64 * hi;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qa[h][0] = *reinterpret_cast<const uint4*>(qbase + h * kHeadDim + 16 * c);
-      qa[h][1] = *reinterpret_cast<const uint4*>(qbase + h * kHeadDim + 16 * c + 8);
+    for (int j = 0; j < 8; ++j) {
+      qraw[j] = lo < G ? *reinterpret_cast<const uint4*>(qrow + 8 * j) : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
     }
+    qmax = max_over_row_groups(qmax);
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
+    // 2^(14 - e): the largest |q| lands in [2^14, 2^15)
+    const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
+    const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
+    const float qpre = __uint_as_float((uint32_t)pe << 23);
+    uint4 qop[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = pk_f16(bf16_lo(w[e]) * qpre, bf16_hi(w[e]) * qpre);
+      qop[j] = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    // scores in log2 units: q.k * softmax scale * log2(e), with the K tensor
+    // scale and the q prescale (a power of two) folded in
+    const float c = a.scale_log2 * kS * __uint_as_float((uint32_t)(254 - pe) << 23);
+
     const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
     const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
     const int64_t page0 = tok0 / kBlockSize;
     const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-    for (int64_t pi = wave; pi < npages; pi += kWaves) {
-      const int64_t page = page0 + pi;
-      // rows are counted in 16-element scale blocks: 8 code bytes, 1 scale byte each
-      int64_t base = 0, ts = 0;
-      const bool ok = page_base(a, s, g, page, kHeadDim / 16, &base, &ts);
-      if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
-      uint2 kc[4], vc[4];
-      uint32_t ksc[4], vsc[4];
-      if (ok) {
+    const int64_t nunits = (npages + kUnitPages - 1) / kUnitPages;
+    uint8_t* my_stage = stage + wave * (kUnitPages * kBlockSize * kRowBytesF16);
+
+    auto load_unit = [&](int64_t u, F4Unit& U) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t blk = base + (4 * j + r) * ts + c;
-          kc[j] = *reinterpret_cast<const uint2*>(Kc + blk * 8);
-          vc[j] = *reinterpret_cast<const uint2*>(Vc + blk * 8);
-          ksc[j] = a.k_scale[blk];
-          vsc[j] = a.v_scale[blk];
+      for (int p = 0; p < kUnitPages; ++p) {
+        const int64_t pi = kUnitPages * u + p;
+        int64_t base = 0, ts = 0;
+        bool ok = false;
+        if (pi < npages) {
+          ok = page_base(a, s, g, page0 + pi, kHeadDim / 16, &base, &ts);
+          if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
         }
-      } else {
+        U.ok[p] = ok;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        u32x4_t k0 = z, k1 = z, v0 = z, v1 = z;
+        uint32_t ksc = 0, vsc = 0;
+        if (ok) {
+          const int64_t rowblk = base + lo * ts;   // row t's first 16-element block
+          const uint8_t* kp = Kc + rowblk * 8 + 32 * hi;
+          const uint8_t* vp = Vc + rowblk * 8 + 32 * hi;
+          k0 = *reinterpret_cast<const u32x4_t*>(kp);
+          k1 = *reinterpret_cast<const u32x4_t*>(kp + 16);
+          v0 = *reinterpret_cast<const u32x4_t*>(vp);
+          v1 = *reinterpret_cast<const u32x4_t*>(vp + 16);
+          ksc = *reinterpret_cast<const uint32_t*>(a.k_scale + rowblk + 4 * hi);
+          vsc = *reinterpret_cast<const uint32_t*>(a.v_scale + rowblk + 4 * hi);
+        }
+        U.kc[p][0] = k0;
+        U.kc[p][1] = k1;
+        U.vc[p][0] = v0;
+        U.vc[p][1] = v1;
+        U.ks[p] = ksc;
+        U.vs[p] = vsc;
+      }
+    };
+
+    const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    auto compute_unit = [&](int64_t u, F4Unit& U) {
+      const int64_t ut0 = (page0 + kUnitPages * u) * kBlockSize;   // first token of the step
+      // the same for every lane: both pages present and inside the split
+      bool full = ut0 + kUnitPages * kBlockSize <= tok1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kc[j] = vc[j] = make_uint2(0, 0);
-          ksc[j] = vsc[j] = 0;
+      for (int p = 0; p < kUnitPages; ++p) full = full && U.ok[p];
+      // tokens of the step that are attended: [0, nvalid) per page, or none
+      int nv[kUnitPages];
+#pragma unroll
+      for (int p = 0; p < kUnitPages; ++p)
+        nv[p] = U.ok[p] ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - ut0 - p * kBlockSize)) : 0;
+      if (!full) {
+        // V rows outside the split or the sequence, or of a masked page, get
+        // weight 0; stale bytes there may decode to NaN (0 * NaN is not 0),
+        // so they are staged as zeros
+#pragma unroll
+        for (int p = 0; p < kUnitPages; ++p) {
+          const bool keep = lo < nv[p];
+          U.vc[p][0] = keep ? U.vc[p][0] : u32x4_t{0u, 0u, 0u, 0u};
+          U.vc[p][1] = keep ? U.vc[p][1] : u32x4_t{0u, 0u, 0u, 0u};
+          U.vs[p] = keep ? U.vs[p] : 0u;
         }
       }
-      float sc[4][G];
+      // stage V as fp16: row lo, logical chunks 8 hi .. 8 hi + 7
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t kb[8];
-        fp4x8_to_bf16(kc[j].x, *reinterpret_cast<uint32_t(*)[4]>(&kb[0]));
-        fp4x8_to_bf16(kc[j].y, *reinterpret_cast<uint32_t(*)[4]>(&kb[4]));
-        const float bs = e4m3_to_f32(ksc[j]);
+      for (int p = 0; p < kUnitPages; ++p) {
+        const BlockScale b0 = split_scale<0>(U.vs[p]), b1 = split_scale<1>(U.vs[p]),
+                         b2 = split_scale<2>(U.vs[p]), b3 = split_scale<3>(U.vs[p]);
+        const BlockScale bs[4] = {b0, b1, b2, b3};
+        const uint32_t w[8] = {U.vc[p][0][0], U.vc[p][0][1], U.vc[p][0][2], U.vc[p][0][3],
+                               U.vc[p][1][0], U.vc[p][1][1], U.vc[p][1][2], U.vc[p][1][3]};
+        uint8_t* row = my_stage + (p * kBlockSize + lo) * kRowBytesF16;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float d = 0.f;
-          d = dot2_bf16(qa[h][0].x, kb[0], d);
-          d = dot2_bf16(qa[h][0].y, kb[1], d);
-          d = dot2_bf16(qa[h][0].z, kb[2], d);
-          d = dot2_bf16(qa[h][0].w, kb[3], d);
-          d = dot2_bf16(qa[h][1].x, kb[4], d);
-          d = dot2_bf16(qa[h][1].y, kb[5], d);
-          d = dot2_bf16(qa[h][1].z, kb[6], d);
-          d = dot2_bf16(qa[h][1].w, kb[7], d);
-          sc[j][h] = d * bs;
-        }
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) = fp4x8_to_f16(w[j], bs[j >> 1]);
+      }
+      // S^T = K Q^T, one accumulator chain per page
+      floatx4_t sacc[kUnitPages];
+#pragma unroll
+      for (int p = 0; p < kUnitPages; ++p) sacc[p] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      BlockScale kb[kUnitPages][4];
+#pragma unroll
+      for (int p = 0; p < kUnitPages; ++p) {
+        kb[p][0] = split_scale<0>(U.ks[p]);
+        kb[p][1] = split_scale<1>(U.ks[p]);
+        kb[p][2] = split_scale<2>(U.ks[p]);
+        kb[p][3] = split_scale<3>(U.ks[p]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t tok = page * kBlockSize + 4 * j + r;
-        const bool valid = ok && tok < tok1;
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float d = row16_sum(sc[j][h]);
-          sc[j][h] = valid ? d * qk_scale : -INFINITY;
+        for (int p = 0; p < kUnitPages; ++p) {
+          const uint32_t w = U.kc[p][j >> 2][j & 3];
+          sacc[p] = mfma_f16(fp4x8_to_f16(w, kb[p][j >> 1]), qop[j], sacc[p]);
         }
+      // online softmax over the unit's 32 tokens (lane: head lo, tokens 4hi..4hi+3 of each page)
+      float x[kUnitPages][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < kUnitPages; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = sacc[p][e] * c;
+          x[p][e] = full || 4 * hi + e < nv[p] ? v : -INFINITY;
+          mx = fmaxf(mx, x[p][e]);
+        }
+      mx = max_over_row_groups(mx);
+      // running maximum and rescale on every step (alpha is 1 unless the
+      // maximum rose): a branch here makes the compiler keep a second copy
+      // of the output accumulators around the loop
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] *= alpha;
+      lsum *= alpha;
+      const float mp = m - kPShiftF4;
+      uint4 pop;
+      pop.x = pk_f16(fast_exp2(x[0][0] - mp), fast_exp2(x[0][1] - mp));
+      pop.y = pk_f16(fast_exp2(x[0][2] - mp), fast_exp2(x[0][3] - mp));
+      pop.z = pk_f16(fast_exp2(x[1][0] - mp), fast_exp2(x[1][1] - mp));
+      pop.w = pk_f16(fast_exp2(x[1][2] - mp), fast_exp2(x[1][3] - mp));
+      lsum = mfma_f16(ones, pop, lsum);
+      // O^T += V^T P^T: k order = tokens 4hi..4hi+3 of page 0, then of page 1
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int trow = 4 * hi + (lo >> 2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int chunk = 2 * i + ((lo & 3) >> 1);
+        const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
+        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(void*)(my_stage + off));
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(void*)(my_stage + kBlockSize * kRowBytesF16 + off));
+        const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+        o[i] = mfma_f16(make_uint4(w0.x, w0.y, w1.x, w1.y), pop, o[i]);
       }
-      softmax_update<G>(sc, m, l, acc);
-      // Stale codes and scales decode to finite values, so p = 0 already
-      // cancels them; clearing keeps masked rows exactly out of the sum.
-      if (!ok || (page + 1) * kBlockSize > tok1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    F4Unit R[kAheadF4 + 1];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (!(ok && page * kBlockSize + 4 * j + r < tok1)) {
-            vc[j] = make_uint2(0, 0);
-            vsc[j] = 0;
-          }
-      }
+    for (int k = 0; k < kAheadF4; ++k) load_unit(wave + k * kWaves, R[k]);
+    for (int64_t u = wave; u < nunits; u += (kAheadF4 + 1) * kWaves) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float vf[16];
-        uint32_t vb[8];
-        fp4x8_to_bf16(vc[j].x, *reinterpret_cast<uint32_t(*)[4]>(&vb[0]));
-        fp4x8_to_bf16(vc[j].y, *reinterpret_cast<uint32_t(*)[4]>(&vb[4]));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          vf[2 * e] = bf16_lo(vb[e]);
-          vf[2 * e + 1] = bf16_hi(vb[e]);
-        }
-        const float bs = e4m3_to_f32(vsc[j]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = sc[j][h] * bs;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-        }
+      for (int b = 0; b <= kAheadF4; ++b) {
+        const int64_t uu = u + b * kWaves;
+        load_unit(uu + kAheadF4 * kWaves, R[(b + kAheadF4) % (kAheadF4 + 1)]);
+        if (uu < nunits) compute_unit(uu, R[b]);
       }
     }
-    // the V tensor scale multiplies every value: apply it once
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[h][e] *= vS;
   }
-  finish_split<G>(a, s, g, split, m, l, acc, [](int cc, int e) { return 16 * cc + e; });
+
+  // combine the 4 waves through LDS (the staging buffer, once every wave is
+  // done with it) and write one normalised partial + log2-sum-exp per head
+  __syncthreads();
+  float* sm_o = reinterpret_cast<float*>(stage);   // [kWaves][G][256]
+  float* sm_m = sm_o + kWaves * G * kHeadDim;      // [kWaves][G]
+  float* sm_l = sm_m + kWaves * G;                 // [kWaves][G]
+  if (lo < G) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<floatx4_t*>(sm_o + (wave * G + lo) * kHeadDim + 16 * i + 4 * hi) = o[i] * vS;
+    if (hi == 0) {
+      sm_m[wave * G + lo] = m - kPShiftF4;   // l and O carry a factor 2^kPShiftF4
+      sm_l[wave * G + lo] = lsum[0];
+    }
+  }
+  __syncthreads();
+  const int nsp = a.plan.num_splits;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+    const int h = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * G + h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = fast_exp2(sm_m[w * G + h] - M);
+      L += sm_l[w * G + h] * sc;
+      O += sm_o[(w * G + h) * kHeadDim + d] * sc;
+    }
+    const int qh = g * G + h;
+    const int64_t slot = ((int64_t)s * a.num_q_heads + qh) * nsp + split;
+    a.ws_o[slot * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
+  }
 }
 
 // ---- merge ------------------------------------------------------------------
@@ -517,10 +737,15 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len) {
-  // Enough workgroups to cover the 256 compute units twice over (two
-  // resident per CU), but never fewer than one page per wave per split.
-  const int64_t target_wgs = 1024;
+// Workgroups a decode launch aims for: both split kernels keep two resident
+// per CU; bf16 gets two rounds of them, NVFP4 a single round (fewer, longer
+// splits: its per-workgroup set-up and the merge weigh more against its
+// shorter stream).
+constexpr int64_t kTargetWgsBf16 = 1024;
+constexpr int64_t kTargetWgsF4 = 512;
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len, int32_t dtype) {
+  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : kTargetWgsF4;
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   const int64_t chunks = (max_seq_len + unit - 1) / unit;      // 64-token chunks

@@ -61,7 +61,8 @@ struct DecodePlan {
   int32_t num_splits;
   int64_t tokens_per_split;  // multiple of 4 * kBlockSize
 };
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len);
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len,
+                       int32_t dtype);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const DecodePlan& p);
 
 struct DecodeArgs {
