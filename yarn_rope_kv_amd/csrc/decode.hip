@@ -291,11 +291,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
 // v_mfma_f32_16x16x32_f16 and keeps only the dequantisation and the softmax
 // on the vector ALUs.  A wave takes 32 tokens (two pages) per step.
 //
-//   dequant   the scaled fp4 conversion multiplies by a power of two only (it
-//             takes the exponent of its fp32 scale), so a block scale q_s
-//             (e4m3) is applied as 2^E in the conversion and then (1 + m/8)
-//             in a packed fp16 multiply.  e2m1 x q_s has at most 6 significant
-//             bits and lies in [2^-10, 2688]: both steps are exact in fp16.
+//   dequant   the fp4 conversion with unit scale gives e2m1 in fp16 (the
+//             scaled form multiplies by a power of two only: it takes the
+//             exponent of its fp32 scale), and a packed fp16 multiply applies
+//             the block scale q_s (e4m3, exact in fp16).  e2m1 x q_s has at
+//             most 6 significant bits and lies in [2^-10, 2688]: exact.
 //   S^T       = K Q^T.  Lane (t, kg) = (lane % 16, lane / 16) reads code bytes
 //             [32kg, 32kg+32) of token row t (head dims [64kg, 64kg+64), scale
 //             blocks 4kg..4kg+3: one scale dword) and supplies dims
@@ -304,12 +304,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
 //             two so that |q| < 2^15 fits fp16 (bf16 values are then exact).
 //   softmax   lane (h, r) holds the scores of head h at tokens 4r..4r+3 of
 //             both pages: the accumulator layout is the P^T operand of the
-//             output product as it stands.  Online, log2 domain, with the
-//             running maximum m and the rescale of O applied on every step
-//             (a conditional rescale makes the compiler keep a second copy
-//             of the accumulators around the loop).  p = 2^(s - m + 14) is
-//             rounded to fp16 (nearest even); the row sums are a product of
-//             those same values with ones.
+//             output product as it stands.  Online, log2 domain; the running
+//             maximum m is raised (and O rescaled) only when a step exceeds
+//             it by more than 1.  p = 2^(s - m + 14) <= 2^15 is rounded to
+//             fp16 (nearest even); the row sums are a product of those same
+//             values with ones.
 //   O^T      += V^T P^T.  V is dequantised to fp16 into a per-wave LDS buffer
 //             (token rows, 16-byte chunks swizzled); ds_read_b64_tr_b16 turns
 //             4 rows x 4 dims per 16 lanes into the V^T operand: lane j of
@@ -328,9 +327,14 @@ constexpr int kUnitPages = 2;                            // pages per wave step
 constexpr int kRowBytesF16 = kHeadDim * 2;               // staged V row
 constexpr int kStageBytes = kWaves * kUnitPages * kBlockSize * kRowBytesF16;   // 64 KiB
 constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
-// p = 2^(s - m + kPShiftF4) <= 2^14 in fp16: the shift keeps probabilities
-// down to 2^-28 of the row maximum at full fp16 precision (and to 2^-38 as
-// subnormals); it cancels in O / l and is taken off the log-sum-exp.
+// The running maximum m is raised only when a step's maximum exceeds it by
+// more than kRescaleF4, so s - m <= kRescaleF4 and p = 2^(s - m + kPShiftF4)
+// <= 2^15 fits fp16.  The shift keeps probabilities down to 2^-28 of m at
+// full fp16 precision (2^-38 as subnormals); it cancels in O / l and is taken
+// off the log-sum-exp.  (A threshold of 6 with a shift of 9 ran at the same
+// speed and lost 13x in accuracy on the 1M-token outlier workload.)
+constexpr float kRescaleF4 = 1.0f;
+constexpr int kVtAhead = 4;                              // V^T operands in flight ahead of their products
 constexpr float kPShiftF4 = 14.0f;
 
 __device__ __forceinline__ floatx4_t mfma_f16(const uint4& a, const uint4& b, floatx4_t c) {
@@ -344,30 +348,26 @@ __device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, f16x2_t));
 }
 
-// Block scale (e4m3 byte SEL of w) as the power of two the scaled conversion
-// applies and the factor 1 + m/8 as a packed fp16 pair.  The hardware fp8
-// conversion decodes OCP E4M3FN exactly; the fp16 factor takes the top ten
-// mantissa bits of the fp32 value (e4m3 has three).  A zero scale gives 2^-127
-// in the conversion (which underflows to zero in fp16) times 1.
-struct BlockScale {
-  float pow2;
-  uint32_t mant2;
-};
+// Block scale (e4m3 byte SEL of w) as a packed fp16 pair.  The hardware fp8
+// conversion decodes OCP E4M3FN exactly, and every e4m3 value (0 and
+// 2^-9 .. 448) is an fp16 value, so the second conversion is exact too.
 template <int SEL>
-__device__ __forceinline__ BlockScale split_scale(uint32_t w) {
-  const uint32_t b = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)w, SEL));
-  const uint32_t mh = 0x3C00u | ((b >> 13) & 0x3FFu);
-  return {__uint_as_float(b & 0x7F800000u), mh | (mh << 16)};
+__device__ __forceinline__ uint32_t block_scale_f16x2(uint32_t w) {
+  const float sc = __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+  return pk_f16(sc, sc);
 }
 
 // Eight e2m1 codes (one dword; element 2j in the low nibble of byte j) ->
-// eight fp16 values code x q_s, exactly.
-__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, const BlockScale& bs) {
-  const f16x2_t m = __builtin_bit_cast(f16x2_t, bs.mant2);
-  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 0) * m;
-  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 1) * m;
-  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 2) * m;
-  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, bs.pow2, 3) * m;
+// eight fp16 values code x q_s, exactly: the unit-scale fp4 conversion gives
+// the e2m1 value (the scaled form multiplies by a power of two only, so the
+// block scale is applied separately), and e2m1 x q_s has at most 6
+// significant bits in [2^-10, 2688], which fp16 holds.
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, uint32_t qs2) {
+  const f16x2_t m = __builtin_bit_cast(f16x2_t, qs2);
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m;
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m;
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m;
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * m;
   return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
@@ -527,9 +527,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
       // stage V as fp16: row lo, logical chunks 8 hi .. 8 hi + 7
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) {
-        const BlockScale b0 = split_scale<0>(U.vs[p]), b1 = split_scale<1>(U.vs[p]),
-                         b2 = split_scale<2>(U.vs[p]), b3 = split_scale<3>(U.vs[p]);
-        const BlockScale bs[4] = {b0, b1, b2, b3};
+        const uint32_t bs[4] = {block_scale_f16x2<0>(U.vs[p]), block_scale_f16x2<1>(U.vs[p]),
+                                block_scale_f16x2<2>(U.vs[p]), block_scale_f16x2<3>(U.vs[p])};
         const uint32_t w[8] = {U.vc[p][0][0], U.vc[p][0][1], U.vc[p][0][2], U.vc[p][0][3],
                                U.vc[p][1][0], U.vc[p][1][1], U.vc[p][1][2], U.vc[p][1][3]};
         uint8_t* row = my_stage + (p * kBlockSize + lo) * kRowBytesF16;
@@ -541,13 +540,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
       floatx4_t sacc[kUnitPages];
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) sacc[p] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      BlockScale kb[kUnitPages][4];
+      uint32_t kb[kUnitPages][4];
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) {
-        kb[p][0] = split_scale<0>(U.ks[p]);
-        kb[p][1] = split_scale<1>(U.ks[p]);
-        kb[p][2] = split_scale<2>(U.ks[p]);
-        kb[p][3] = split_scale<3>(U.ks[p]);
+        kb[p][0] = block_scale_f16x2<0>(U.ks[p]);
+        kb[p][1] = block_scale_f16x2<1>(U.ks[p]);
+        kb[p][2] = block_scale_f16x2<2>(U.ks[p]);
+        kb[p][3] = block_scale_f16x2<3>(U.ks[p]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -568,15 +567,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
           mx = fmaxf(mx, x[p][e]);
         }
       mx = max_over_row_groups(mx);
-      // running maximum and rescale on every step (alpha is 1 unless the
-      // maximum rose): a branch here makes the compiler keep a second copy
-      // of the output accumulators around the loop
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
+      // the running maximum is raised (and O rescaled) only when a step
+      // exceeds it by more than kRescaleF4
+      const bool grow = mx > m + kRescaleF4;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] *= alpha;
-      lsum *= alpha;
+        for (int i = 0; i < 16; ++i) o[i] *= alpha;
+        lsum *= alpha;
+      }
       const float mp = m - kPShiftF4;
       uint4 pop;
       pop.x = pk_f16(fast_exp2(x[0][0] - mp), fast_exp2(x[0][1] - mp));
@@ -589,8 +590,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int trow = 4 * hi + (lo >> 2);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      auto read_vt = [&](int i) {
         const int chunk = 2 * i + ((lo & 3) >> 1);
         const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
         const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -598,7 +598,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
         const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_short4_t*)(void*)(my_stage + kBlockSize * kRowBytesF16 + off));
         const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-        o[i] = mfma_f16(make_uint4(w0.x, w0.y, w1.x, w1.y), pop, o[i]);
+        return make_uint4(w0.x, w0.y, w1.x, w1.y);
+      };
+      // V^T operands read kVtAhead products ahead, so that LDS latency overlaps
+      // the products (the compiler would otherwise read each just before use)
+      uint4 vt[kVtAhead];
+#pragma unroll
+      for (int i = 0; i < kVtAhead; ++i) vt[i] = read_vt(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o[i] = mfma_f16(vt[i % kVtAhead], pop, o[i]);
+        if (i + kVtAhead < 16) vt[i % kVtAhead] = read_vt(i + kVtAhead);
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
