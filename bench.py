@@ -47,13 +47,13 @@ def measured_traffic(record):
                      rec["write_kib_per_call"] * rec["write_scale"])
 
 
-def decode_bytes_per_launch(n_ctx, per_token):
-    # KV stream + q and out (24 heads x 256 x 2 B each) + the page table (4 B / 16 tokens)
-    return per_token * n_ctx + 2 * 24 * 256 * 2 + 4 * (n_ctx // 16)
+def decode_bytes_per_launch(n_ctx, per_token, hq=24):
+    # KV stream + q and out (hq heads x 256 x 2 B each) + the page table (4 B / 16 tokens)
+    return per_token * n_ctx + 2 * hq * 256 * 2 + 4 * (n_ctx // 16)
 
 
 def build_step(W, Y, w, torch, dev):
-    """The 16 layers of a decode workload plus the per-step inputs."""
+    """The layers of a decode workload plus the per-step inputs."""
     layers = []
     for l in range(w.layers):
         layers.append(W.build_decode_layer(w, l, device=dev, spare_page=True))
@@ -61,9 +61,9 @@ def build_step(W, Y, w, torch, dev):
             log(f"{w.name}: built layer {l + 1}/{w.layers}")
     N = w.n_ctx
     L = w.layers
-    q_in = torch.empty((L, 24, 256), dtype=torch.bfloat16, device=dev)
-    k_in = torch.empty((L, 4, 256), dtype=torch.bfloat16, device=dev)
-    v_in = torch.empty((L, 4, 256), dtype=torch.bfloat16, device=dev)
+    q_in = torch.empty((L, w.hq, 256), dtype=torch.bfloat16, device=dev)
+    k_in = torch.empty((L, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+    v_in = torch.empty((L, w.hkv, 256), dtype=torch.bfloat16, device=dev)
     for l in range(L):
         q_in[l:l + 1] = W.gen_q(w, l, 1, dev, token0=1)
         W.gen_kv(w, l, 1, 1, k_in[l:l + 1], token0=N)
@@ -135,8 +135,8 @@ def cpu_baseline(W, w):
                       f"fp64, {dt:.2f} s"}
 
 
-def bench_prefill(W, Y, torch, dev, reps):
-    w = W.WORKLOADS["prefill"]
+def bench_prefill(W, Y, torch, dev, reps, name="prefill"):
+    w = W.WORKLOADS[name]
     case = W.build_prefill(w, device=dev)
     out = torch.empty_like(case.q)
     T = case.q.shape[0]
@@ -152,14 +152,15 @@ def bench_prefill(W, Y, torch, dev, reps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     pairs = sum(case.q_start + i + 1 for i in range(T))
-    flops = 4.0 * 256 * pairs * 24
+    flops = 4.0 * 256 * pairs * w.hq
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": "prefill: 8,192-token causal chunk at 1,040,384..1,048,575 over a "
-                        "1,048,576-token paged cache, 24 q / 4 KV heads",
+    record = "prefill_chunk_8192_over_1m.json" if name == "prefill" else None
+    return {"workload": f"prefill: 8,192-token causal chunk at 1,040,384..1,048,575 over a "
+                        f"1,048,576-token paged cache, {w.hq} q / {w.hkv} KV heads",
             "ms_per_chunk": ms, "tflops": tf, "flop_per_chunk": flops,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": measured_traffic("prefill_chunk_8192_over_1m.json")}}
+                         "traffic": measured_traffic(record) if record else None}}
 
 
 def main():
@@ -170,6 +171,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nvfp4", action="store_true")
+    ap.add_argument("--no-tp2", action="store_true",
+                    help="skip one card's share of a two-way KV-head split (12 q / 2 KV heads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -246,6 +249,32 @@ def main():
         except Y.YrkError as e:
             result["prefill"] = {"error": str(e)}
         torch.cuda.empty_cache()
+    if not args.no_tp2:
+        # one card's share when the 4 KV heads are split over two cards: the
+        # same kernels at 12 query / 2 KV heads (nothing is exchanged inside
+        # attention, so this is the whole per-card decode and prefill work)
+        wt = W.WORKLOADS["long_tp2"]
+        log("building the 12 q / 2 KV-head share")
+        stept, evt, lt = build_step(W, Y, wt, torch, dev)
+        st = max(3, args.steps // 2)
+        wallt, kt = time_steps(stept, evt, st, args.warmup, torch)
+        bplt = decode_bytes_per_launch(wt.n_ctx, KV_BYTES_PER_TOKEN_LAYER * wt.hkv // 4, wt.hq)
+        share = {"decode": {
+            "workload": f"decode step, {wt.layers} layers x 1,048,576 cached tokens (bf16), "
+                        f"{wt.hq} q / {wt.hkv} KV heads",
+            "value": wt.layers * wt.n_ctx / (wallt / st), "unit": "KV token-layers/s",
+            "avg_launch_ms": kt,
+            "roofline": {"bound": "hbm", "achieved": bplt / (kt * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bplt / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_split_bf16_tp2_share_1m.json"),
+                         "bytes_per_launch": bplt}}}
+        del lt, stept, evt
+        torch.cuda.empty_cache()
+        if not args.no_prefill:
+            share["prefill"] = bench_prefill(W, Y, torch, dev, reps=3, name="prefill_tp2")
+            torch.cuda.empty_cache()
+        result["tp2_share"] = share
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(W, w)

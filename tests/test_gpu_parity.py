@@ -237,24 +237,24 @@ def _host_case(W, w, u, N=None):
     """The oracle side of one layer / session: roped q (bits), roped K, V."""
     N = w.n_ctx if N is None else N
     t = _oracle_table(w)
-    q_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, 24, 256)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256)
     q = O.rope(q_raw, [N], t, bf16_out=True)[0]
     kw = {}
     if w.elem_outlier_p:
         kw = dict(outlier_p=w.elem_outlier_p, outlier_mul=20.0)
-    k_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.K), 0, N, 4, 256,
+    k_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.K), 0, N, w.hkv, 256,
                             chan_mul=W.chan_mul(w, u, synth.K),
                             outlier_stream=synth.stream_id(u, synth.K_OUTLIER), **kw)
     k = O.rope(k_raw, np.arange(N), t, bf16_out=True)
     del k_raw
-    v = synth.host_fill(w.seed, synth.stream_id(u, synth.V), 0, N, 4, 256,
+    v = synth.host_fill(w.seed, synth.stream_id(u, synth.V), 0, N, w.hkv, 256,
                         chan_mul=W.chan_mul(w, u, synth.V),
                         outlier_stream=synth.stream_id(u, synth.V_OUTLIER), **kw)
     p_star = -1
     if w.needle:
         p_star = synth.needle_position(w.seed, u, N)
-        for g in range(4):
-            k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[6 * g]))
+        for g in range(w.hkv):
+            k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
     return q, k, v, p_star
 
 
@@ -279,7 +279,8 @@ def test_decode_tiny_contiguous_f32(Y, W):
     _compare_attention("tiny", _f64(out)[0], ref, atol=1e-4, bf16_out=False)
 
 
-@pytest.mark.parametrize("name,units", [("native", [0]), ("long", [0]), ("long", [11])])
+@pytest.mark.parametrize("name,units", [("native", [0]), ("long", [0]), ("long", [11]),
+                                        ("long_tp2", [2])])
 def test_decode_bf16_paged(Y, W, name, units):
     w = W.WORKLOADS[name]
     for u in units:
@@ -296,8 +297,8 @@ def test_decode_bf16_paged(Y, W, name, units):
         _compare_attention(f"{name}/layer{u}", got, ref)
         if p_star >= 0:
             vf = O.bf16_to_f64(v[p_star])
-            for g in range(4):
-                assert np.abs(got[6 * g] - vf[g]).max() < 0.05
+            for g in range(w.hkv):
+                assert np.abs(got[w.group * g] - vf[g]).max() < 0.05
 
 
 def test_decode_sessions_batched(Y, W):
@@ -571,7 +572,7 @@ def test_decode_query_magnitude(Y, fmt, q_mul):
 
 # -- prefill ----------------------------------------------------------------------
 
-def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
+def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None, hq=24, hkv=4):
     """needle = (t, key, mul): after rope, key position `key` of every KV head
     g is set to mul (a power of two) x the roped query of chunk token t, head
     6g (exact in bf16), so that query's score there is far above its first
@@ -579,9 +580,9 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
     total = n_prior + T
     pages = -(-total // 16) + 1
     t = O.yarn_table()
-    k_raw = synth.host_fill(seed, 1, 0, total, 4, 256)
-    v_raw = synth.host_fill(seed, 2, 0, total, 4, 256)
-    q_raw = synth.host_fill(seed, 0, 0, T, 24, 256)
+    k_raw = synth.host_fill(seed, 1, 0, total, hkv, 256)
+    v_raw = synth.host_fill(seed, 2, 0, total, hkv, 256)
+    q_raw = synth.host_fill(seed, 0, 0, T, hq, 256)
     yp = Y.YarnParams()
     kt = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
     vt = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
@@ -591,9 +592,9 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
     Y.yarn_rope_apply(yp, qt, pos_all[n_prior:])
     if needle is not None:
         nt, nk, mul = needle
-        for g in range(4):
+        for g in range(hkv):
             kt[nk, g] = qt[nt, 6 * g] * mul
-    L = Y.KVLayer.allocate(Y.KV_BF16, 4, pages, paged=paged, device=DEV)
+    L = Y.KVLayer.allocate(Y.KV_BF16, hkv, pages, paged=paged, device=DEV)
     table = synth.block_permutation(seed, pages) if paged else None
     bt = torch.from_numpy(table).to(DEV) if paged else None
     Y.kv_append_quantize(L, kt, vt, bt, pos_all)
@@ -602,7 +603,7 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
         bt[bad_page] = pages + 5
     out = torch.empty_like(qt)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ws = torch.full((Y.prefill_workspace_size(T, 24) // 4,), 7, dtype=torch.int32, device=DEV)
+    ws = torch.full((Y.prefill_workspace_size(T, hq) // 4,), 7, dtype=torch.int32, device=DEV)
     Y.prefill_attention(L, qt, n_prior, bt, out, workspace=ws, err=err)
     torch.cuda.synchronize()
     flags = ws.cpu().numpy()
@@ -610,24 +611,25 @@ def _prefill_small(Y, n_prior, T, paged, seed, bad_page=None, needle=None):
     q = O.rope(q_raw, np.arange(n_prior, total), t, bf16_out=True)
     if needle is not None:
         nt, nk, mul = needle
-        for g in range(4):      # a power-of-two multiple of a bf16 value is exact
+        for g in range(hkv):    # a power-of-two multiple of a bf16 value is exact
             src = q[nt, 6 * g].astype(np.uint32) << 16
             k[nk, g] = ((src.view(np.float32) * mul).view(np.uint32) >> 16).astype(k.dtype)
     return _f64(out), O.bf16_to_f64(q), k, v_raw, int(err.item()), flags
 
 
-@pytest.mark.parametrize("n_prior,T,paged", [(1000, 77, True), (0, 200, False),
-                                             (4093, 130, True), (31, 1, True)])
-def test_prefill_small_matches_oracle(Y, n_prior, T, paged):
-    _say(f"prefill n_prior={n_prior} T={T} paged={paged}")
-    got, q, k, v, err, flags = _prefill_small(Y, n_prior, T, paged, seed=300 + T)
+@pytest.mark.parametrize("n_prior,T,paged,hq,hkv", [(1000, 77, True, 24, 4), (0, 200, False, 24, 4),
+                                                    (4093, 130, True, 24, 4), (31, 1, True, 24, 4),
+                                                    (1000, 77, True, 12, 2), (517, 300, False, 12, 2)])
+def test_prefill_small_matches_oracle(Y, n_prior, T, paged, hq, hkv):
+    _say(f"prefill n_prior={n_prior} T={T} paged={paged} hq={hq} hkv={hkv}")
+    got, q, k, v, err, flags = _prefill_small(Y, n_prior, T, paged, seed=300 + T, hq=hq, hkv=hkv)
     assert err == 0
-    assert not flags.any()       # every wave stayed within its first tile's headroom
+    assert not flags.any()       # no wave needed the rescaling second launch
     ref = O.prefill_attention(q, np.arange(n_prior, n_prior + T), k, v)
-    _compare_attention(f"prefill/{n_prior}+{T}", got, ref)
+    _compare_attention(f"prefill/{hq}x{hkv}/{n_prior}+{T}", got, ref)
     if n_prior == 0:
         vf = O.bf16_to_f64(v)
-        for h in range(24):      # the first row sees only key 0
+        for h in range(hq):      # the first row sees only key 0
             assert np.abs(got[0, h] - vf[0, h // 6]).max() <= np.abs(vf[0]).max() * 2 ** -8
 
 
@@ -669,12 +671,14 @@ def test_prefill_score_far_above_the_first_tile(Y, paged, mul, flagged):
         assert np.abs(got[40, 6 * g] - vf[500, g]).max() < 0.05
 
 
-def test_prefill_workload_sampled_rows(Y, W):
+@pytest.mark.parametrize("name", ["prefill", "prefill_tp2"])
+def test_prefill_workload_sampled_rows(Y, W, name):
     """The full chunk (8,192 queries at 1,040,384..1,048,575 over a
-    1,048,576-token paged cache) in the bench's launch configuration; rows
-    checked one by one against the oracle."""
-    w = W.WORKLOADS["prefill"]
-    _say("prefill workload")
+    1,048,576-token paged cache) in the bench's launch configuration, with
+    24 q / 4 KV heads and with one card's share of a two-way head split
+    (12 q / 2 KV heads); rows checked one by one against the oracle."""
+    w = W.WORKLOADS[name]
+    _say(f"{name} workload")
     case = W.build_prefill(w, device=DEV)
     out = torch.empty_like(case.q)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -688,12 +692,12 @@ def test_prefill_workload_sampled_rows(Y, W):
     torch.cuda.empty_cache()
     N, q0 = w.n_ctx, w.n_ctx - w.prefill_chunk
     t = _oracle_table(w)
-    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, 4, 256), np.arange(N),
-               t, bf16_out=True)
-    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, 4, 256)
+    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, w.hkv, 256),
+               np.arange(N), t, bf16_out=True)
+    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, w.hkv, 256)
     for j, r in enumerate(rows):
-        q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0 + r, 1, 24, 256)
+        q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0 + r, 1, w.hq, 256)
         q = O.rope(q_raw, [q0 + r], t, bf16_out=True)[0]
         assert np.array_equal(q, qg[j])
         ref = O.decode_attention(O.bf16_to_f64(q), k[: q0 + r + 1], v[: q0 + r + 1])
-        _compare_attention(f"prefill_workload/row{r}", got[j], ref)
+        _compare_attention(f"{name}/row{r}", got[j], ref)

@@ -23,6 +23,10 @@ Workloads (sizes from the model the pages describe: 4 KV heads x head dim
             of 122,880 pages, one decode query each (one batched call).
   prefill   one 8,192-token causal chunk at positions 1,040,384..1,048,575
             over a 1,048,576-token cache (65,536 permuted pages).
+  long_tp2, prefill_tp2
+            one card's share when the 4 KV heads are split over two cards
+            (12 query / 2 KV heads): 4 layers x 1,048,576 cached tokens with
+            a needle, and the 8,192-token prefill chunk.
 """
 from __future__ import annotations
 
@@ -52,6 +56,12 @@ class Workload:
     needle: bool = False
     f32_out: bool = False
     prefill_chunk: int = 0
+    hq: int = HQ                  # query heads
+    hkv: int = HKV                # KV heads
+
+    @property
+    def group(self):
+        return self.hq // self.hkv
 
     def yarn(self) -> Y.YarnParams:
         return Y.YarnParams(rope_theta=1e7, head_dim=D, rotary_dim=64, factor=4.0,
@@ -69,27 +79,29 @@ WORKLOADS = {
     "long_fp4": Workload("long_fp4", 1004, 1048576, layers=16, nvfp4=True, elem_outlier_p=0.01),
     "sessions": Workload("sessions", 1005, 131072, seqs=15),
     "prefill": Workload("prefill", 1005, 1048576, prefill_chunk=8192),
+    "long_tp2": Workload("long_tp2", 1006, 1048576, layers=4, needle=True, hq=12, hkv=2),
+    "prefill_tp2": Workload("prefill_tp2", 1007, 1048576, prefill_chunk=8192, hq=12, hkv=2),
 }
 
 
 def chan_mul(w: Workload, layer: int, tensor: int):
     if not w.chan_outliers:
         return None
-    return synth.outlier_channels(w.seed, layer, tensor, HKV, D, w.chan_outliers, 8.0)
+    return synth.outlier_channels(w.seed, layer, tensor, w.hkv, D, w.chan_outliers, 8.0)
 
 
 def gen_kv(w: Workload, unit: int, tensor: int, ntok: int, out: torch.Tensor, token0: int = 0):
-    """Raw (un-roped) K or V rows [ntok, 4, 256] of one layer / session."""
+    """Raw (un-roped) K or V rows [ntok, hkv, 256] of one layer / session."""
     ostream = synth.K_OUTLIER if tensor == synth.K else synth.V_OUTLIER
-    synth.dev_fill(out, w.seed, synth.stream_id(unit, tensor), token0, ntok, HKV, D,
+    synth.dev_fill(out, w.seed, synth.stream_id(unit, tensor), token0, ntok, w.hkv, D,
                    chan_mul=chan_mul(w, unit, tensor), outlier_stream=synth.stream_id(unit, ostream),
                    outlier_p=w.elem_outlier_p, outlier_mul=20.0)
     return out
 
 
 def gen_q(w: Workload, unit: int, ntok: int, device, token0: int = 0):
-    q = torch.empty((ntok, HQ, D), dtype=torch.bfloat16, device=device)
-    synth.dev_fill(q, w.seed, synth.stream_id(unit, synth.Q), token0, ntok, HQ, D)
+    q = torch.empty((ntok, w.hq, D), dtype=torch.bfloat16, device=device)
+    synth.dev_fill(q, w.seed, synth.stream_id(unit, synth.Q), token0, ntok, w.hq, D)
     return q
 
 
@@ -105,7 +117,7 @@ def page_table(w: Workload, unit: int):
 @dataclasses.dataclass
 class DecodeLayer:
     layer: Y.KVLayer
-    q: torch.Tensor               # roped [S, 24, 256] bf16
+    q: torch.Tensor               # roped [S, hq, 256] bf16
     block_tables: torch.Tensor | None
     seq_lens: torch.Tensor
     max_seq_len: int
@@ -124,13 +136,13 @@ def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, sp
         spare = np.arange(num_blocks, num_blocks + S, dtype=np.int32).reshape(S, 1)
         tables = np.ascontiguousarray(np.concatenate([tables, spare], axis=1))
         num_blocks += S
-    layer = Y.KVLayer.allocate(Y.KV_NVFP4 if w.nvfp4 else Y.KV_BF16, HKV, num_blocks,
+    layer = Y.KVLayer.allocate(Y.KV_NVFP4 if w.nvfp4 else Y.KV_BF16, w.hkv, num_blocks,
                                paged=w.paged, device=device)
     yp = w.yarn()
-    q = torch.empty((S, HQ, D), dtype=torch.bfloat16, device=device)
+    q = torch.empty((S, w.hq, D), dtype=torch.bfloat16, device=device)
     pos_q = torch.full((1,), N, dtype=torch.int32, device=device)
     positions = torch.arange(N, dtype=torch.int32, device=device)
-    k = torch.empty((N, HKV, D), dtype=torch.bfloat16, device=device)
+    k = torch.empty((N, w.hkv, D), dtype=torch.bfloat16, device=device)
     v = torch.empty_like(k)
     bt_dev = torch.from_numpy(tables).to(device) if tables is not None else None
     needle = -1
@@ -143,8 +155,8 @@ def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, sp
         Y.yarn_rope_apply(yp, k, positions)
         if w.needle:
             needle = synth.needle_position(w.seed, u, N)
-            for g in range(HKV):
-                k[needle, g] = q[s, 6 * g] * 2          # exact doubling of a bf16 value
+            for g in range(w.hkv):
+                k[needle, g] = q[s, w.group * g] * 2    # exact doubling of a bf16 value
         if w.nvfp4:
             Y.nvfp4_tensor_scale(k, layer.k_tensor_scale)
             Y.nvfp4_tensor_scale(v, layer.v_tensor_scale)
@@ -160,9 +172,9 @@ def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, sp
 
 def decode_outputs(w: Workload, dl: DecodeLayer, device="cuda"):
     S = dl.q.shape[0]
-    out = torch.empty((S, HQ, D), dtype=torch.float32 if w.f32_out else torch.bfloat16,
+    out = torch.empty((S, w.hq, D), dtype=torch.float32 if w.f32_out else torch.bfloat16,
                       device=device)
-    ws = torch.empty(Y.decode_workspace_size(S, HQ, HKV, dl.max_seq_len), dtype=torch.uint8,
+    ws = torch.empty(Y.decode_workspace_size(S, w.hq, w.hkv, dl.max_seq_len), dtype=torch.uint8,
                      device=device)
     return out, ws
 
@@ -175,7 +187,7 @@ def run_decode(dl: DecodeLayer, out, ws, err=None):
 @dataclasses.dataclass
 class PrefillCase:
     layer: Y.KVLayer
-    q: torch.Tensor               # roped [T, 24, 256]
+    q: torch.Tensor               # roped [T, hq, 256]
     block_table: torch.Tensor
     q_start: int
 
@@ -185,10 +197,10 @@ def build_prefill(w: Workload, device="cuda", chunk_tokens=1 << 18):
     included) and the chunk's roped queries."""
     N, T = w.n_ctx, w.prefill_chunk
     tables = page_table(w, 0)
-    layer = Y.KVLayer.allocate(Y.KV_BF16, HKV, w.pages_per_seq, paged=True, device=device)
+    layer = Y.KVLayer.allocate(Y.KV_BF16, w.hkv, w.pages_per_seq, paged=True, device=device)
     bt = torch.from_numpy(tables[0]).to(device)
     yp = w.yarn()
-    k = torch.empty((chunk_tokens, HKV, D), dtype=torch.bfloat16, device=device)
+    k = torch.empty((chunk_tokens, w.hkv, D), dtype=torch.bfloat16, device=device)
     v = torch.empty_like(k)
     for t0 in range(0, N, chunk_tokens):
         n = min(chunk_tokens, N - t0)
