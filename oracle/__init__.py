@@ -44,6 +44,10 @@ def lib():
         "orc_nvfp4_quantize": ([_p, _i64, _i32, _i32, _f, _p, _p], None),
         "orc_nvfp4_pack": ([_p, _i64, _p], None),
         "orc_nvfp4_dequantize": ([_p, _p, _i64, _i32, _i32, _f, _p], None),
+        "orc_f16_value": ([ctypes.c_uint16], _d),
+        "orc_f64_to_f16_sat": ([_d], ctypes.c_uint16),
+        "orc_int8_quantize": ([_p, _i64, _i32, _i32, _p, _p], None),
+        "orc_int8_dequantize": ([_p, _p, _i64, _i32, _i32, _p], None),
         "orc_decode_attention": ([_p, _i32, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _f, _f, _d,
                                   _p, _p], _i32),
         "orc_prefill_attention": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _f, _f,
@@ -168,25 +172,57 @@ def nvfp4_dequantize(codes, scales, S) -> np.ndarray:
     return out
 
 
+def f16_value(bits: int) -> float:
+    return lib().orc_f16_value(bits)
+
+
+def f64_to_f16_sat(x: float) -> int:
+    """Non-negative x -> nearest binary16 bit pattern, ties to even, saturating at 65504."""
+    return int(lib().orc_f64_to_f16_sat(x))
+
+
+def int8_quantize(x_bits):
+    """INT8 group-64: x_bits uint16 [T, H, D] -> (codes int8 [T, H, D], scales
+    uint16 binary16 bits [T, H, D/64])."""
+    x, p = _c(x_bits, np.uint16)
+    T, H, D = x.shape
+    codes = np.empty((T, H, D), dtype=np.int8)
+    scales = np.empty((T, H, D // 64), dtype=np.uint16)
+    lib().orc_int8_quantize(p, T, H, D, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def int8_dequantize(codes, scales) -> np.ndarray:
+    c, pc = _c(codes, np.int8)
+    s, ps = _c(scales, np.uint16)
+    T, H, D = c.shape
+    out = np.empty((T, H, D), dtype=np.float64)
+    lib().orc_int8_dequantize(pc, ps, T, H, D, out.ctypes.data)
+    return out
+
+
 # --- C5 / C6 --------------------------------------------------------------------
 
-def decode_attention(q, k, v, scale=None, nvfp4=None, with_lse=False):
+def _kv_args(k, v, nvfp4, int8):
+    """(kind, k array, v array, k scales, v scales, kS, vS) for the C oracle."""
+    if nvfp4 is not None:
+        return (1, _c(k, np.uint8), _c(v, np.uint8), _c(nvfp4[0], np.uint8),
+                _c(nvfp4[1], np.uint8), float(nvfp4[2]), float(nvfp4[3]))
+    if int8 is not None:
+        return (2, _c(k, np.int8), _c(v, np.int8), _c(int8[0], np.uint16), _c(int8[1], np.uint16),
+                1.0, 1.0)
+    return 0, _c(k, np.uint16), _c(v, np.uint16), (None, None), (None, None), 1.0, 1.0
+
+
+def decode_attention(q, k, v, scale=None, nvfp4=None, int8=None, with_lse=False):
     """q: fp64 [Hq, D] (roped).  bf16 cache: k, v uint16 [N, Hkv, D].
-    NVFP4 cache: nvfp4=(k_scales, v_scales, kS, vS) and k, v are codes [N, Hkv, D]."""
+    NVFP4 cache: nvfp4=(k_scales, v_scales, kS, vS) and k, v are codes [N, Hkv, D].
+    INT8 cache: int8=(k_scales, v_scales) (binary16 bits [N, Hkv, D/64]) and
+    k, v are int8 codes [N, Hkv, D]."""
     qa, pq = _c(q, np.float64)
     Hq, D = qa.shape
-    kind = 0 if nvfp4 is None else 1
-    dt = np.uint16 if kind == 0 else np.uint8
-    ka, pk = _c(k, dt)
-    va, pv = _c(v, dt)
+    kind, (ka, pk), (va, pv), (_, pks), (_, pvs), kS, vS = _kv_args(k, v, nvfp4, int8)
     N, Hkv, _ = ka.shape
-    ks = vs = None
-    pks = pvs = None
-    kS = vS = 1.0
-    if kind == 1:
-        ks, pks = _c(nvfp4[0], np.uint8)
-        vs, pvs = _c(nvfp4[1], np.uint8)
-        kS, vS = float(nvfp4[2]), float(nvfp4[3])
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     out = np.empty((Hq, D), dtype=np.float64)
@@ -198,23 +234,14 @@ def decode_attention(q, k, v, scale=None, nvfp4=None, with_lse=False):
     return (out, lse) if with_lse else out
 
 
-def prefill_attention(q, positions, k, v, scale=None, nvfp4=None):
+def prefill_attention(q, positions, k, v, scale=None, nvfp4=None, int8=None):
     """q fp64 [R, Hq, D]; row r attends to cached tokens 0..positions[r]."""
     qa, pq = _c(q, np.float64)
     R, Hq, D = qa.shape
     pos, pp = _c(positions, np.int64)
-    kind = 0 if nvfp4 is None else 1
-    dt = np.uint16 if kind == 0 else np.uint8
-    ka, pk = _c(k, dt)
-    va, pv = _c(v, dt)
+    kind, (ka, pk), (va, pv), (_, pks), (_, pvs), kS, vS = _kv_args(k, v, nvfp4, int8)
     Hkv = ka.shape[1]
     assert ka.shape[0] >= int(pos.max()) + 1
-    pks = pvs = None
-    kS = vS = 1.0
-    if kind == 1:
-        ks, pks = _c(nvfp4[0], np.uint8)
-        vs, pvs = _c(nvfp4[1], np.uint8)
-        kS, vS = float(nvfp4[2]), float(nvfp4[3])
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     out = np.empty((R, Hq, D), dtype=np.float64)

@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain fp64 CPU oracle for YaRN-roped, GQA, paged long-context
- * attention (decode and chunked prefill) over a bf16 or NVFP4 KV cache.
+ * attention (decode and chunked prefill) over a bf16, NVFP4 or INT8 KV cache.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
  * CPU-baseline leg load this library.  The product path (the HIP library)
@@ -378,6 +378,110 @@ void orc_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n
 }
 
 /* ------------------------------------------------------------------------ */
+/* INT8 group-64 KV cache                                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * [P3] "NInfer -- Windows 11 TP2 fork" (memory table) and [P1] "And the
+ * memory picture": the deployed 1M-token cache is INT8 with groups of 64 and
+ * takes 16.5 KiB per token per device, quantisation-scale planes included.
+ * With 16 full-attention layers x 2 KV heads per device x 256 dims x (K, V)
+ * one byte per element is 16 KiB, which leaves 512 B for 16 x 2 x 2 x 4
+ * group scales: 2 bytes each.  The pages fix nothing else, so:
+ * READING (symmetric absmax groups, the plainest scheme with one scale per
+ * group): a group is 64 consecutive head dims of one (token, KV head);
+ *   s    = RNE_fp16(max |x_i| / 127), saturating at 65504 (fp16 scales:
+ *          READING, bf16 would give the same size)
+ *   code = clamp(RNE(x_i / s), -127, 127) as a two's-complement byte, and 0
+ *          when s == 0
+ *   x^   = code * s
+ */
+
+/* IEEE binary16 bit pattern -> exact fp64 value (finite patterns). */
+double orc_f16_value(uint16_t h) {
+    int e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v = e ? ldexp(1.0 + m / 1024.0, e - 15) : ldexp((double)m, -24);
+    if (e == 31) v = m ? NAN : INFINITY;
+    return (h & 0x8000) ? -v : v;
+}
+
+/*
+ * Non-negative fp64 -> nearest binary16, ties to even, saturating at the
+ * largest finite value 65504 (READING).  Every step before the single
+ * nearbyint() is an exact scaling by a power of two, so the result is the
+ * correct rounding of x.
+ */
+uint16_t orc_f64_to_f16_sat(double x) {
+    if (!(x < 65504.0)) return 0x7BFF;
+    if (x < ldexp(1.0, -14))                       /* subnormal: step 2^-24 */
+        return (uint16_t)nearbyint(ldexp(x, 24)); /* 1024 is the smallest normal, 0x0400 */
+    int e;
+    double f = frexp(x, &e);                        /* x = 2f * 2^(e-1), 2f in [1, 2) */
+    int ex = e - 1;
+    double mant = nearbyint((2.0 * f - 1.0) * 1024.0); /* 0 .. 1024 */
+    if (mant == 1024.0) { mant = 0.0; ex += 1; }
+    if (ex > 15) return 0x7BFF;
+    return (uint16_t)(((ex + 15) << 10) | (int)mant);
+}
+
+/*
+ * Quantise one bf16 tensor [ntok][nheads][head_dim] (head_dim % 64 == 0)
+ * into codes [ntok][nheads][head_dim] (int8) and scales
+ * [ntok][nheads][head_dim/64] (binary16 bits), by the rule above.
+ * amax / 127 is an fp64 quotient: amax has 8 significant bits, so the exact
+ * quotient is either an fp16 rounding midpoint exactly (and then so is the
+ * fp64 value) or at least ~2^-20 of itself away from every midpoint, far
+ * beyond fp64's error.  Likewise x / s (8 by 11 significant bits) is either
+ * exactly a half-integer or at least 2^-12 away from one, so nearbyint of the
+ * fp64 quotient is the rounding of the exact one.
+ */
+void orc_int8_quantize(const uint16_t *x, int64_t ntok, int nheads, int head_dim, int8_t *codes,
+                       uint16_t *scales) {
+    const int ngrp = head_dim / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t) {
+        for (int h = 0; h < nheads; ++h) {
+            const uint16_t *xr = x + (t * nheads + h) * (int64_t)head_dim;
+            int8_t *cr = codes + (t * nheads + h) * (int64_t)head_dim;
+            uint16_t *sr = scales + (t * nheads + h) * (int64_t)ngrp;
+            for (int grp = 0; grp < ngrp; ++grp) {
+                double amax = 0.0;
+                for (int i = 0; i < 64; ++i) {
+                    double a = fabs(orc_bf16_to_f64(xr[grp * 64 + i]));
+                    if (a > amax) amax = a;
+                }
+                uint16_t sb = orc_f64_to_f16_sat(amax / 127.0);
+                sr[grp] = sb;
+                double sv = orc_f16_value(sb);
+                for (int i = 0; i < 64; ++i) {
+                    int c = 0;
+                    if (sv > 0.0) {
+                        double q = nearbyint(orc_bf16_to_f64(xr[grp * 64 + i]) / sv);
+                        if (q > 127.0) q = 127.0;
+                        if (q < -127.0) q = -127.0;
+                        c = (int)q;
+                    }
+                    cr[grp * 64 + i] = (int8_t)c;
+                }
+            }
+        }
+    }
+}
+
+/* Dequantised value x^ = code * s, exact in fp64. */
+void orc_int8_dequantize(const int8_t *codes, const uint16_t *scales, int64_t ntok, int nheads,
+                         int head_dim, double *out) {
+    const int ngrp = head_dim / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t)
+        for (int h = 0; h < nheads; ++h)
+            for (int d = 0; d < head_dim; ++d) {
+                int64_t r = t * nheads + h;
+                out[r * head_dim + d] = (double)codes[r * head_dim + d] *
+                                        orc_f16_value(scales[r * ngrp + d / 64]);
+            }
+}
+
+/* ------------------------------------------------------------------------ */
 /* C5 / C6: attention                                                        */
 /* ------------------------------------------------------------------------ */
 
@@ -386,7 +490,8 @@ void orc_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n
  * the stored bf16 value, or the NVFP4 dequantised value.
  */
 typedef struct {
-    int kind; /* 0 = bf16 [N][Hkv][D] bit patterns; 1 = NVFP4 codes [N][Hkv][D] + scales [N][Hkv][D/16] */
+    int kind; /* 0 = bf16 [N][Hkv][D] bit patterns; 1 = NVFP4 codes [N][Hkv][D] + scales [N][Hkv][D/16];
+                 2 = INT8 codes [N][Hkv][D] + binary16 scales [N][Hkv][D/64] */
     const uint16_t *bf16;
     const uint8_t *codes;
     const uint8_t *scales;
@@ -398,11 +503,15 @@ static void kv_row(const orc_kv_view *kv, int64_t n, int g, int Hkv, int D, doub
     if (kv->kind == 0) {
         const uint16_t *p = kv->bf16 + r * D;
         for (int d = 0; d < D; ++d) row[d] = orc_bf16_to_f64(p[d]);
-    } else {
+    } else if (kv->kind == 1) {
         const uint8_t *c = kv->codes + r * D;
         const uint8_t *s = kv->scales + r * (D / 16);
         for (int d = 0; d < D; ++d)
             row[d] = orc_e2m1_value(c[d]) * orc_e4m3_value(s[d / 16]) * kv->S;
+    } else {
+        const int8_t *c = (const int8_t *)kv->codes + r * D;
+        const uint16_t *s = (const uint16_t *)kv->scales + r * (D / 64);
+        for (int d = 0; d < D; ++d) row[d] = (double)c[d] * orc_f16_value(s[d / 64]);
     }
 }
 
@@ -453,6 +562,8 @@ static void attend_one_head(const double *qh, const orc_kv_view *kview, const or
  * kernel sees it), cache of N tokens, out [Hq][D], lse [Hq] (nullable).
  * kv_kind 0: k/v are bf16 [N][Hkv][D].  kv_kind 1: k/v are NVFP4 codes (one
  * per byte) [N][Hkv][D] with scales [N][Hkv][D/16] and tensor scales kS/vS.
+ * kv_kind 2: k/v are INT8 codes [N][Hkv][D] with binary16 scales
+ * [N][Hkv][D/64] (passed as bytes; kS/vS unused).
  * Heads are independent and run in parallel.
  */
 int orc_decode_attention(const double *q, int Hq, int Hkv, int D, int64_t N, int kv_kind,
@@ -460,7 +571,9 @@ int orc_decode_attention(const double *q, int Hq, int Hkv, int D, int64_t N, int
                          const uint8_t *v_scales, float kS, float vS, double scale, double *out,
                          double *lse) {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || N < 0) return -1;
+    if (kv_kind < 0 || kv_kind > 2) return -1;
     if (kv_kind == 1 && D % 16) return -1;
+    if (kv_kind == 2 && D % 64) return -1;
     orc_kv_view kview = {kv_kind, (const uint16_t *)k, (const uint8_t *)k, k_scales, (double)kS};
     orc_kv_view vview = {kv_kind, (const uint16_t *)v, (const uint8_t *)v, v_scales, (double)vS};
     const int group = Hq / Hkv;
