@@ -25,6 +25,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 KV_BYTES_PER_TOKEN_LAYER = 4096           # 4 KV heads x 256 x 2 B x (K, V)
 NVFP4_BYTES_PER_TOKEN_LAYER = 1152        # 4 x (128 code + 16 scale bytes) x (K, V)
+INT8_BYTES_PER_TOKEN_LAYER = 2112         # 4 x (256 code + 4 x 2 scale bytes) x (K, V)
 
 
 def log(msg):
@@ -171,6 +172,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nvfp4", action="store_true")
+    ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-tp2", action="store_true",
                     help="skip one card's share of a two-way KV-head split (12 q / 2 KV heads)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -241,6 +243,25 @@ def main():
                          "traffic": measured_traffic("decode_split_nvfp4_long_fp4_1m.json"),
                          "bytes_per_launch": bplf}}
         del lf, stepf, evf
+        torch.cuda.empty_cache()
+    if not args.no_int8:
+        wi = W.WORKLOADS["long_int8"]
+        log("building the INT8 16-layer cache")
+        stepi, evi, li = build_step(W, Y, wi, torch, dev)
+        si = max(3, args.steps // 2)
+        walli, ki = time_steps(stepi, evi, si, args.warmup, torch)
+        bpli = decode_bytes_per_launch(wi.n_ctx, INT8_BYTES_PER_TOKEN_LAYER)
+        result["int8_decode"] = {
+            "workload": "decode step, 16 layers x 1,048,576 cached tokens, INT8 group-64 cache "
+                        "(2,112 B per token-layer), 24 q / 4 KV heads",
+            "value": wi.layers * wi.n_ctx / (walli / si),
+            "unit": "KV token-layers/s", "avg_launch_ms": ki,
+            "roofline": {"bound": "hbm", "achieved": bpli / (ki * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bpli / (ki * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_split_int8_long_int8_1m.json"),
+                         "bytes_per_launch": bpli}}
+        del li, stepi, evi
         torch.cuda.empty_cache()
     if not args.no_prefill:
         log("prefill")

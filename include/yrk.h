@@ -3,7 +3,7 @@
  * for AMD Instinct MI355X (gfx950).
  *
  * One data-parallel hot path: rotate queries and keys with a YaRN-stretched
- * rotary table, append keys and values to a paged bf16 or NVFP4 KV cache,
+ * rotary table, append keys and values to a paged bf16, NVFP4 or INT8 KV cache,
  * and run split-K decode attention and chunked causal prefill attention over
  * that cache.
  *
@@ -52,6 +52,7 @@ extern "C" {
 
 #define YRK_KV_BF16 0
 #define YRK_KV_NVFP4 1
+#define YRK_KV_INT8 2
 
 #define YRK_OUT_BF16 0
 #define YRK_OUT_F32 1
@@ -94,6 +95,8 @@ typedef struct yrk_yarn_params {
  *   bf16:  k, v          [num_blocks][num_kv_heads][block_size][head_dim]       bf16
  *   NVFP4: k, v          [num_blocks][num_kv_heads][block_size][head_dim / 2]   packed e2m1
  *          k_scale, v_scale [num_blocks][num_kv_heads][block_size][head_dim / 16] e4m3
+ *   INT8:  k, v          [num_blocks][num_kv_heads][block_size][head_dim]       int8
+ *          k_scale, v_scale [num_blocks][num_kv_heads][block_size][head_dim / 64] binary16
  *   Logical token n of a sequence is block table[n / block_size], slot
  *   n % block_size.
  * paged = 0 (contiguous): the same rows as [capacity][num_kv_heads][row];
@@ -105,10 +108,18 @@ typedef struct yrk_yarn_params {
  * fp32 tensor scale S of each tensor (device memory, one float).  The
  * dequantised value is e2m1(code) * e4m3(scale) * S.
  *
+ * INT8 group-64 ([P3] memory table, [P1] "And the memory picture": the
+ * deployed 1M-token format, 16.5 KiB per token per device with the scale
+ * planes, which fixes 2-byte scales): one binary16 scale per 64 consecutive
+ * head-dim elements of a row, s = RNE(max |x| / 127) saturating at 65504,
+ * and two's-complement codes clamp(RNE(x / s), -127, 127) (0 when s is 0);
+ * the dequantised value is code * s.  The rounding rules are this library's
+ * reading.  The tensor-scale pointers are not used.
+ *
  * This build supports head_dim 256 and block_size 16.
  */
 typedef struct yrk_kv_layer {
-  int32_t dtype;          /* YRK_KV_BF16 or YRK_KV_NVFP4 */
+  int32_t dtype;          /* YRK_KV_BF16, YRK_KV_NVFP4 or YRK_KV_INT8 */
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
@@ -176,6 +187,11 @@ int yrk_nvfp4_tensor_scale(const void* x_dev, int64_t n, float* scale_out_dev,
  *                ties to the even code, saturating at 6 ([P5] "Why NVFP4 KV
  *                changes the math").  The decisions are exact: they equal
  *                rounding the exact real quotients.
+ *   INT8 cache:  per 64-element group, scale = RNE_binary16(max|x| / 127),
+ *                saturating at 65504; codes = clamp(RNE(x / scale), -127,
+ *                127), 0 for a zero scale (the reading stated at
+ *                yrk_kv_layer).  Both quotients are fp64 divisions rounded
+ *                once, which equals rounding the exact quotients.
  *   block_table_dev   int32 [block_table_len] (paged); NULL for contiguous
  *   dev_error_word    nullable device uint32; positions outside the table or
  *                     capacity, or table entries outside the pool, set a bit
@@ -205,7 +221,12 @@ size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * "YaRN, and matching what vLLM actually does").  The cache is split into
  * token ranges processed in parallel across compute units and merged by
  * log-sum-exp ([P3] "Limitations": the decode split policy).
- * seq_lens[s] == 0 gives a zero output row.
+ * seq_lens[s] == 0 gives a zero output row.  Over an NVFP4 cache the keys
+ * and values are dequantised to fp16 exactly for the matrix cores.  Over an
+ * INT8 cache the codes enter the matrix cores as exact fp16 integers: each
+ * scale group's partial key products are scaled in fp32, and the value
+ * scales multiply the (fp16) attention weights, so no dequantised value is
+ * ever rounded.
  *   q_dev            bf16 [num_seqs][num_q_heads][head_dim] (already roped)
  *   block_tables_dev int32 [num_seqs][block_table_stride] (paged); NULL for
  *                    contiguous (num_seqs must then be 1)

@@ -80,6 +80,9 @@ def test_decode_validation():
     assert _decode(_layer(dtype=7)) == Y.EINVAL
     assert _decode(_layer(reserved=1)) == Y.EINVAL
     assert _decode(_layer(dtype=Y.KV_NVFP4)) == Y.EINVAL     # scale planes missing
+    assert _decode(_layer(dtype=Y.KV_INT8)) == Y.EINVAL      # group-scale planes missing
+    assert _decode(_layer(dtype=Y.KV_INT8, k_scale=0x1, v_scale=None)) == Y.EINVAL
+    assert _decode(_layer(dtype=3)) == Y.EINVAL
     assert _decode(L, Hq=22) == Y.EINVAL                     # not a multiple of KV heads
     assert _decode(L, Hq=40) == Y.ENOTSUP                    # group of 10
     assert _decode(L, max_len=64 * 16 + 1) == Y.ERANGE       # beyond the block table
@@ -110,6 +113,11 @@ def test_append_validation():
     assert f(ctypes.byref(L), None, None, 0, 0x400, 4, None, None, None) == Y.OK
     assert f(ctypes.byref(_layer(head_dim=64)), 0x100, 0x200, 4, 0x400, 4, 0x300, None,
              None) == Y.ENOTSUP
+    # INT8 needs both group-scale planes, not the NVFP4 tensor scales
+    assert f(ctypes.byref(_layer(dtype=Y.KV_INT8)), 0x100, 0x200, 4, 0x400, 4, 0x300, None,
+             None) == Y.EINVAL
+    i8 = _layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50000)
+    assert f(ctypes.byref(i8), None, None, 0, 0x400, 4, None, None, None) == Y.OK
 
 
 def test_prefill_validation():
@@ -130,6 +138,7 @@ def test_prefill_validation():
     assert call(T=-1) == Y.EINVAL
     assert call(layer=_layer(dtype=Y.KV_NVFP4, k_scale=0x1, v_scale=0x1,
                              k_tensor_scale_dev=0x10, v_tensor_scale_dev=0x10)) == Y.ENOTSUP
+    assert call(layer=_layer(dtype=Y.KV_INT8, k_scale=0x1, v_scale=0x1)) == Y.ENOTSUP
     assert call(T=0, q=None, out=None) == Y.OK
     # the workspace holds one flag word per wave of the launch grid
     assert call(ws=None) == Y.EINVAL

@@ -231,6 +231,42 @@ def test_append_nvfp4_bit_exact(Y, paged):
         assert np.array_equal(got_c.reshape(packed_ref.shape), packed_ref)
 
 
+@pytest.mark.parametrize("paged", [True, False])
+def test_append_int8_bit_exact(Y, paged):
+    T, pages = 300, 32
+    k_raw = synth.host_fill(92, 1, 0, T, 4, 256, outlier_stream=3, outlier_p=0.01,
+                            outlier_mul=20.0)
+    v_raw = synth.host_fill(92, 2, 0, T, 4, 256, outlier_stream=4, outlier_p=0.01,
+                            outlier_mul=20.0)
+    v_raw[5, 1, :64] = 0                       # an all-zero group
+    v_raw[6, 2, 3] = 0x8000                    # -0
+    # a group 2^-16 smaller (binary16-subnormal scale) and one 2^24 larger
+    # (the scale saturates at 65504 and the codes clamp at +-127)
+    for raw, e in ((k_raw, -16), (v_raw, 24)):
+        x = (raw[7, 0, 64:128].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** e)
+        raw[7, 0, 64:128] = (x.view(np.uint32) >> 16).astype(np.uint16)
+    k = torch.from_numpy(k_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    v = torch.from_numpy(v_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    L = Y.KVLayer.allocate(Y.KV_INT8, 4, pages, paged=paged, device=DEV)
+    table = synth.block_permutation(92, pages)
+    pos = np.arange(T, dtype=np.int32)
+    Y.kv_append_quantize(L, k, v, torch.from_numpy(table).to(DEV) if paged else None,
+                         torch.from_numpy(pos).to(DEV))
+    for raw, codes_t, scales_t in ((k_raw, L.k, L.k_scale), (v_raw, L.v, L.v_scale)):
+        c_ref, s_ref = O.int8_quantize(raw)
+        cb = codes_t.cpu().numpy().view(np.uint8)
+        sb = scales_t.cpu().numpy().view(np.uint8)
+        if paged:
+            got_c = O.gather_paged(cb.reshape(-1), pages, 4, 16, 256, table, T)
+            got_s = O.gather_paged(sb.reshape(-1), pages, 4, 16, 8, table, T)
+        else:
+            got_c, got_s = cb[:T], sb[:T]
+        assert np.array_equal(got_s.reshape(-1).view(np.uint16).reshape(s_ref.shape), s_ref)
+        assert np.array_equal(got_c.reshape(-1).view(np.int8).reshape(c_ref.shape), c_ref)
+    assert 0 < O.f16_value(int(O.int8_quantize(k_raw[7:8])[1][0, 0, 1])) < 2.0 ** -14
+    assert O.int8_quantize(v_raw[7:8])[1][0, 0, 1] == 0x7BFF
+
+
 # -- decode -----------------------------------------------------------------------
 
 def _host_case(W, w, u, N=None):
@@ -352,6 +388,51 @@ def test_decode_long_nvfp4_sampled_layer(Y, W):
                              nvfp4=(k_scales, v_scales, kS, vS))
     _compare_attention("long_fp4/layer5", out[0], ref)
     _compare_attention("long_fp4/layer5/f32", out32[0], ref, bf16_out=False)
+
+
+def test_decode_long_int8_sampled_layer(Y, W):
+    """One layer of the 16 x 1,048,576-token INT8 workload: the cache's codes
+    and scales bit-exact against the oracle's quantisation of the same roped
+    keys (rows where the GPU rope agrees bit for bit), then attention."""
+    w = W.WORKLOADS["long_int8"]
+    u = 3
+    _say("decode long_int8 layer 3")
+    dl = W.build_decode_layer(w, u, device=DEV, keep_raw=True)
+    out32 = torch.empty((1, 24, 256), dtype=torch.float32, device=DEV)
+    _, ws = W.decode_outputs(w, dl, device=DEV)
+    W.run_decode(dl, out32, ws)
+    torch.cuda.synchronize()
+    out32 = _f64(out32)
+    kg = _bits(dl.k_roped)
+    L = dl.layer
+    table = dl.block_tables[0].cpu().numpy()
+    pages = L.num_blocks
+    kc = O.gather_paged(L.k.cpu().numpy().view(np.uint8).reshape(-1), pages, 4, 16, 256, table,
+                        w.n_ctx)
+    ks = O.gather_paged(L.k_scale.cpu().numpy().view(np.uint8).reshape(-1), pages, 4, 16, 8,
+                        table, w.n_ctx)
+    vc = O.gather_paged(L.v.cpu().numpy().view(np.uint8).reshape(-1), pages, 4, 16, 256, table,
+                        w.n_ctx)
+    vs = O.gather_paged(L.v_scale.cpu().numpy().view(np.uint8).reshape(-1), pages, 4, 16, 8,
+                        table, w.n_ctx)
+    del dl, L
+    torch.cuda.empty_cache()
+    q, k, v, _ = _host_case(W, w, u)
+    same = kg == k
+    _record("long_int8/rope_k", mismatches=int((~same).sum()))
+    assert (~same).sum() <= k.size // 100000
+    del kg
+    k_codes, k_scales = O.int8_quantize(k)
+    v_codes, v_scales = O.int8_quantize(v)
+    rows_ok = same.all(axis=-1)
+    assert np.array_equal(vs.reshape(-1).view(np.uint16).reshape(v_scales.shape), v_scales)
+    assert np.array_equal(vc.reshape(-1).view(np.int8).reshape(v_codes.shape), v_codes)
+    assert np.array_equal(ks.reshape(-1).view(np.uint16).reshape(k_scales.shape)[rows_ok],
+                          k_scales[rows_ok])
+    assert np.array_equal(kc.reshape(-1).view(np.int8).reshape(k_codes.shape)[rows_ok],
+                          k_codes[rows_ok])
+    ref = O.decode_attention(O.bf16_to_f64(q), k_codes, v_codes, int8=(k_scales, v_scales))
+    _compare_attention("long_int8/layer3/f32", out32[0], ref, bf16_out=False)
 
 
 def test_decode_ragged_batch_and_empty(Y, W):
@@ -476,7 +557,6 @@ def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=No
     L = Y.KVLayer.allocate(kv, hkv, pool, paged=paged, device=DEV)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(
         torch.bfloat16)
-    nv = None
     if kv == Y.KV_NVFP4:
         Y.nvfp4_tensor_scale(dev(allk), L.k_tensor_scale)
         Y.nvfp4_tensor_scale(dev(allv), L.v_tensor_scale)
@@ -517,18 +597,26 @@ def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=No
             vc, vsc = O.nvfp4_quantize(vv, vS)
             refs.append(O.decode_attention(qf, kc, vc, nvfp4=(ksc, vsc, kS, vS)) if n else
                         np.zeros((hq, 256)))
+        elif kv == Y.KV_INT8:
+            kc, ksc = O.int8_quantize(kk)
+            vc, vsc = O.int8_quantize(vv)
+            refs.append(O.decode_attention(qf, kc, vc, int8=(ksc, vsc)) if n else
+                        np.zeros((hq, 256)))
         else:
             refs.append(O.decode_attention(qf, kk, vv) if n else np.zeros((hq, 256)))
     return _f64(out), refs, int(err.item())
 
 
+_FMT = {"bf16": 0, "nvfp4": 1, "int8": 2}
+
+
 @pytest.mark.parametrize("hq,hkv", [(24, 4), (4, 4), (8, 4), (12, 4), (16, 4), (12, 2)])
-@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
 def test_decode_ragged_shapes(Y, fmt, hq, hkv):
     """Lengths around the 16-token page and the 32-token NVFP4 step, an empty
     sequence and multi-split ones, for every supported group size and the
     12-query / 2-KV-head shape of one card's share of a two-way head split."""
-    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    kv = _FMT[fmt]
     _say(f"decode ragged {fmt} hq={hq} hkv={hkv}")
     got, refs, err = _decode_batch(Y, kv, _LENS, hq, hkv, seed=700 + hq + 100 * hkv)
     assert err == 0
@@ -538,17 +626,18 @@ def test_decode_ragged_shapes(Y, fmt, hq, hkv):
                            bf16_out=False)
 
 
-def test_decode_nvfp4_masks_and_flags_a_bad_page(Y):
-    _say("decode nvfp4 bad page")
-    got, refs, err = _decode_batch(Y, Y.KV_NVFP4, [300, 77], 24, 4, seed=810, bad_page=(0, 5))
+@pytest.mark.parametrize("fmt", ["nvfp4", "int8"])
+def test_decode_quantised_masks_and_flags_a_bad_page(Y, fmt):
+    _say(f"decode {fmt} bad page")
+    got, refs, err = _decode_batch(Y, _FMT[fmt], [300, 77], 24, 4, seed=810, bad_page=(0, 5))
     assert err == Y.DEVERR_BLOCK_ID
     for s in range(2):
-        _compare_attention(f"nvfp4_bad_page/{s}", got[s], refs[s], bf16_out=False)
+        _compare_attention(f"{fmt}_bad_page/{s}", got[s], refs[s], bf16_out=False)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
 def test_decode_contiguous_equals_paged_bitwise(Y, fmt):
-    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    kv = _FMT[fmt]
     _say(f"decode contiguous vs paged {fmt}")
     a, refs, _ = _decode_batch(Y, kv, [1234], 24, 4, seed=820, paged=True)
     b, _, _ = _decode_batch(Y, kv, [1234], 24, 4, seed=820, paged=False)
@@ -557,12 +646,12 @@ def test_decode_contiguous_equals_paged_bitwise(Y, fmt):
 
 
 @pytest.mark.parametrize("q_mul", [2.0 ** 20, 2.0 ** -30])
-@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
 def test_decode_query_magnitude(Y, fmt, q_mul):
     """q scaled by a power of two far outside [2^-14, 2^15] and the softmax
-    scale divided by it: the same attention, which the NVFP4 kernel computes
-    with q prescaled into fp16's range."""
-    kv = Y.KV_BF16 if fmt == "bf16" else Y.KV_NVFP4
+    scale divided by it: the same attention, which the NVFP4 and INT8 kernels
+    compute with q prescaled into fp16's range."""
+    kv = _FMT[fmt]
     _say(f"decode q x {q_mul} {fmt}")
     got, refs, err = _decode_batch(Y, kv, [500, 33], 24, 4, seed=830, q_mul=q_mul)
     assert err == 0

@@ -19,6 +19,8 @@ Workloads (sizes from the model the pages describe: 4 KV heads x head dim
             query of head 6g.
   long_fp4  the same shapes over an NVFP4 cache; 1% of K and V elements are
             x20 outliers; tensor scale amax / 2688 per (layer, K or V).
+  long_int8 the same shapes over an INT8 group-64 cache, with the same x20
+            element outliers.
   sessions  15 sessions x 131,072 cached tokens dealt from one shared pool
             of 122,880 pages, one decode query each (one batched call).
   prefill   one 8,192-token causal chunk at positions 1,040,384..1,048,575
@@ -50,6 +52,7 @@ class Workload:
     seqs: int = 1
     paged: bool = True
     nvfp4: bool = False
+    int8: bool = False
     orig: int = 262144
     chan_outliers: int = 0        # per-head outlier channels (x8) in K and V
     elem_outlier_p: float = 0.0   # element outliers (x20) in K and V
@@ -77,6 +80,7 @@ WORKLOADS = {
     "native": Workload("native", 1002, 262144, chan_outliers=4),
     "long": Workload("long", 1003, 1048576, layers=16, needle=True),
     "long_fp4": Workload("long_fp4", 1004, 1048576, layers=16, nvfp4=True, elem_outlier_p=0.01),
+    "long_int8": Workload("long_int8", 1008, 1048576, layers=16, int8=True, elem_outlier_p=0.01),
     "sessions": Workload("sessions", 1005, 131072, seqs=15),
     "prefill": Workload("prefill", 1005, 1048576, prefill_chunk=8192),
     "long_tp2": Workload("long_tp2", 1006, 1048576, layers=4, needle=True, hq=12, hkv=2),
@@ -126,7 +130,7 @@ class DecodeLayer:
 
 def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, spare_page=False):
     """One layer of a decode workload on the GPU: roped query (position n_ctx)
-    and a cache filled by rope + append (+ NVFP4 quantisation).  spare_page
+    and a cache filled by rope + append (+ NVFP4 or INT8 quantisation).  spare_page
     adds one more page per sequence (table column pages_per_seq) so a decode
     step can append its own token at position n_ctx."""
     S, N = w.seqs, w.n_ctx
@@ -136,7 +140,8 @@ def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, sp
         spare = np.arange(num_blocks, num_blocks + S, dtype=np.int32).reshape(S, 1)
         tables = np.ascontiguousarray(np.concatenate([tables, spare], axis=1))
         num_blocks += S
-    layer = Y.KVLayer.allocate(Y.KV_NVFP4 if w.nvfp4 else Y.KV_BF16, w.hkv, num_blocks,
+    kv = Y.KV_NVFP4 if w.nvfp4 else (Y.KV_INT8 if w.int8 else Y.KV_BF16)
+    layer = Y.KVLayer.allocate(kv, w.hkv, num_blocks,
                                paged=w.paged, device=device)
     yp = w.yarn()
     q = torch.empty((S, w.hq, D), dtype=torch.bfloat16, device=device)

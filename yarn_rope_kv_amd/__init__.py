@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libyrk.so")
 
 OK, EINVAL, ERANGE, ENOTSUP, ENOSPC, EDEVICE = 0, -1, -2, -3, -4, -5
 DEVERR_BLOCK_ID, DEVERR_POSITION = 1, 2
-KV_BF16, KV_NVFP4 = 0, 1
+KV_BF16, KV_NVFP4, KV_INT8 = 0, 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 HEAD_DIM, BLOCK_SIZE = 256, 16
 
@@ -170,6 +170,12 @@ class KVLayer:
             k = torch.empty(shape + (HEAD_DIM,), dtype=torch.bfloat16, device=device)
             v = torch.empty_like(k)
             return cls(dtype, num_kv_heads, num_blocks, paged, k, v)
+        if dtype == KV_INT8:
+            k = torch.empty(shape + (HEAD_DIM,), dtype=torch.int8, device=device)
+            v = torch.empty_like(k)
+            ks = torch.empty(shape + (HEAD_DIM // 64,), dtype=torch.float16, device=device)
+            vs = torch.empty_like(ks)
+            return cls(dtype, num_kv_heads, num_blocks, paged, k, v, ks, vs)
         k = torch.empty(shape + (HEAD_DIM // 2,), dtype=torch.uint8, device=device)
         v = torch.empty_like(k)
         ks = torch.empty(shape + (HEAD_DIM // 16,), dtype=torch.uint8, device=device)

@@ -63,7 +63,8 @@ int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32
 
 int check_layer(const yrk_kv_layer* L) {
   if (!L) return YRK_EINVAL;
-  if (L->dtype != YRK_KV_BF16 && L->dtype != YRK_KV_NVFP4) return YRK_EINVAL;
+  if (L->dtype != YRK_KV_BF16 && L->dtype != YRK_KV_NVFP4 && L->dtype != YRK_KV_INT8)
+    return YRK_EINVAL;
   if (L->num_kv_heads <= 0 || L->head_dim <= 0 || L->block_size <= 0 || L->num_blocks <= 0)
     return YRK_EINVAL;
   if (L->paged != 0 && L->paged != 1) return YRK_EINVAL;
@@ -72,6 +73,7 @@ int check_layer(const yrk_kv_layer* L) {
   if (L->dtype == YRK_KV_NVFP4 &&
       (!L->k_scale || !L->v_scale || !L->k_tensor_scale_dev || !L->v_tensor_scale_dev))
     return YRK_EINVAL;
+  if (L->dtype == YRK_KV_INT8 && (!L->k_scale || !L->v_scale)) return YRK_EINVAL;
   if (L->head_dim != yrk::kHeadDim || L->block_size != yrk::kBlockSize) return YRK_ENOTSUP;
   return YRK_OK;
 }
@@ -181,7 +183,10 @@ size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
       num_seqs, num_q_heads, yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len, YRK_KV_BF16));
   const size_t f4 = yrk::decode_workspace_bytes(
       num_seqs, num_q_heads, yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len, YRK_KV_NVFP4));
-  return b16 > f4 ? b16 : f4;
+  const size_t i8 = yrk::decode_workspace_bytes(
+      num_seqs, num_q_heads, yrk::plan_decode(num_seqs, num_kv_heads, max_seq_len, YRK_KV_INT8));
+  const size_t m = b16 > f4 ? b16 : f4;
+  return m > i8 ? m : i8;
 }
 
 int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,

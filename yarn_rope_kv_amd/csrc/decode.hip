@@ -397,6 +397,91 @@ struct F4Unit {
   bool ok[kUnitPages];                          // page present and inside the split
 };
 
+// Q^T operand of the score product for lane (lo, hi): head lo of the group
+// (zero for heads >= G), 8 dims per MFMA step (dims 64 hi .. 64 hi + 63, or
+// the per-group order of the INT8 kernel), in fp16
+// after a power-of-two prescale that puts the largest |q| of the group in
+// [2^14, 2^15) (bf16 values are then exact in fp16).  Returns the factor that
+// undoes the prescale.
+template <int G>
+__device__ __forceinline__ float load_q_f16(const DecodeArgs& a, int s, int g, int lo, int hi,
+                                            uint4 (&qop)[8], bool grouped = false) {
+  uint4 qraw[8];
+  float qmax = 0.f;
+  const uint16_t* qrow = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G + lo) * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // step j: dims 64 hi + 8 j .. +7, or (grouped) 64 (j / 2) + 32 (j % 2) + 8 hi .. +7
+    const int d0 = grouped ? 64 * (j >> 1) + 32 * (j & 1) + 8 * hi : 64 * hi + 8 * j;
+    qraw[j] = lo < G ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+  }
+  qmax = max_over_row_groups(qmax);
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
+  // 2^(14 - e): the largest |q| lands in [2^14, 2^15)
+  const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
+  const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
+  const float qpre = __uint_as_float((uint32_t)pe << 23);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = pk_f16(bf16_lo(w[e]) * qpre, bf16_hi(w[e]) * qpre);
+    qop[j] = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+  return __uint_as_float((uint32_t)(254 - pe) << 23);
+}
+
+// End of a split of the matrix-core kernels: combine the 4 waves through LDS
+// (the staging buffer, once every wave is done with it) and write one
+// normalised partial + log2-sum-exp per query head.  Lane (lo, hi) holds
+// O^T rows 16 i + 4 hi .. +3 of head lo; l and O carry a factor
+// 2^kPShiftF4; vS multiplies every value (1 for a cache without one).
+template <int G>
+__device__ __forceinline__ void finish_split_mfma(const DecodeArgs& a, int s, int g, int split,
+                                                  uint8_t* stage, const floatx4_t (&o)[16],
+                                                  const floatx4_t& lsum, float m, float vS,
+                                                  int wave, int lo, int hi) {
+  __syncthreads();
+  float* sm_o = reinterpret_cast<float*>(stage);   // [kWaves][G][256]
+  float* sm_m = sm_o + kWaves * G * kHeadDim;      // [kWaves][G]
+  float* sm_l = sm_m + kWaves * G;                 // [kWaves][G]
+  if (lo < G) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<floatx4_t*>(sm_o + (wave * G + lo) * kHeadDim + 16 * i + 4 * hi) = o[i] * vS;
+    if (hi == 0) {
+      sm_m[wave * G + lo] = m - kPShiftF4;
+      sm_l[wave * G + lo] = lsum[0];
+    }
+  }
+  __syncthreads();
+  const int nsp = a.plan.num_splits;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+    const int h = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * G + h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = fast_exp2(sm_m[w * G + h] - M);
+      L += sm_l[w * G + h] * sc;
+      O += sm_o[(w * G + h) * kHeadDim + d] * sc;
+    }
+    const int qh = g * G + h;
+    const int64_t slot = ((int64_t)s * a.num_q_heads + qh) * nsp + split;
+    a.ws_o[slot * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
@@ -427,37 +512,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
   if (tok1 > tok0) {
     const float kS = *a.k_tensor_scale;
     vS = *a.v_tensor_scale;
-    // Q^T operand: head lo, dims [64 hi, 64 hi + 64), 8 per MFMA step
-    uint4 qraw[8];
-    float qmax = 0.f;
-    const uint16_t* qrow = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G + lo) * kHeadDim + 64 * hi;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qraw[j] = lo < G ? *reinterpret_cast<const uint4*>(qrow + 8 * j) : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
-    }
-    qmax = max_over_row_groups(qmax);
-#pragma unroll
-    for (int sh = 1; sh < 16; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
-    // 2^(14 - e): the largest |q| lands in [2^14, 2^15)
-    const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
-    const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
-    const float qpre = __uint_as_float((uint32_t)pe << 23);
     uint4 qop[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
-      uint32_t h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = pk_f16(bf16_lo(w[e]) * qpre, bf16_hi(w[e]) * qpre);
-      qop[j] = make_uint4(h[0], h[1], h[2], h[3]);
-    }
     // scores in log2 units: q.k * softmax scale * log2(e), with the K tensor
     // scale and the q prescale (a power of two) folded in
-    const float c = a.scale_log2 * kS * __uint_as_float((uint32_t)(254 - pe) << 23);
+    const float c = a.scale_log2 * kS * load_q_f16<G>(a, s, g, lo, hi, qop);
 
     const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
     const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
@@ -629,41 +687,255 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
     }
   }
 
-  // combine the 4 waves through LDS (the staging buffer, once every wave is
-  // done with it) and write one normalised partial + log2-sum-exp per head
-  __syncthreads();
-  float* sm_o = reinterpret_cast<float*>(stage);   // [kWaves][G][256]
-  float* sm_m = sm_o + kWaves * G * kHeadDim;      // [kWaves][G]
-  float* sm_l = sm_m + kWaves * G;                 // [kWaves][G]
-  if (lo < G) {
+  finish_split_mfma<G>(a, s, g, split, stage, o, lsum, m, vS, wave, lo, hi);
+}
+
+// ---- INT8 group-64 on the matrix cores ------------------------------------------
+//
+// The NVFP4 kernel's structure with 16-token steps (the codes take twice the
+// registers per token) and v_mfma_f32_16x16x16_f16 for the output product.
+// Everything stays exact up to the fp32 accumulation: the codes go to the
+// matrix cores as fp16 integers, and the group scales are applied on the
+// other side of each product.
+//   codes     a byte c turns into fp16 1152 + c exactly (0x64 placed above
+//             c ^ 0x80 by a byte permute) and one packed subtraction gives c.
+//   S^T       = sum over the 4 scale groups g of s_tg * (K_g Q_g^T): each
+//             MFMA step covers 32 dims of one group (lane group kg supplies
+//             dims 64g + 32j + 8kg .. +7), so a group's two steps accumulate
+//             T_g alone and the scales multiply T_g in fp32 (lane (h, r)
+//             holds tokens 4r..4r+3, whose scale rows it reads).
+//   O^T      += V^T (P o s_g)^T: V is staged as exact fp16 codes; 16 output
+//             dims lie in one group, and the P^T operand of those products is
+//             P times the token's group scale (rounded to fp16 like P; the
+//             largest p is 2^14 and its product with s is exact).  The row
+//             sums use P itself.  K = 16 tokens: the S^T accumulator is the
+//             P^T operand, one transposing LDS read per 16 dims is V^T.
+
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
+constexpr int kAheadI8 = 1;                                        // steps in flight
+
+__device__ __forceinline__ floatx4_t mfma_f16_k16(const uint2& a, const uint2& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                               __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// Eight int8 codes (two dwords, element i in byte i) -> eight fp16 integers.
+__device__ __forceinline__ uint4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
+  auto two = [&](uint32_t t, uint32_t sel) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, t, sel));
+    return __builtin_bit_cast(uint32_t, h - off);
+  };
+  return make_uint4(two(t0, 0x04010400u), two(t0, 0x04030402u), two(t1, 0x04010400u),
+                    two(t1, 0x04030402u));
+}
+
+// One lane's share of one page.
+struct I8Unit {
+  u32x2_t kc[8];            // K: step j's 8 code bytes of row t (dims of group j / 2)
+  u32x4_t vc[4];            // V: code bytes [64 kg, 64 kg + 64) of row t
+  u32x2_t ks[4], vs[4];     // binary16 scales (4 groups) of rows 4 kg .. 4 kg + 3
+  bool ok;                  // page present and inside the split
+};
+
+template <int G>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
+  static_assert((kWaves * G * kHeadDim + 2 * kWaves * G) * 4 <= kStageBytesI8,
+                "split combine reuses the staging buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytesI8];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int lo = lane & 15, hi = lane >> 4;
+
+  int64_t len = a.seq_lens[s];
+  if (len > a.max_seq_len) {
+    if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+    len = a.max_seq_len;
+  }
+  if (len < 0) len = 0;
+  const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
+  const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
+
+  floatx4_t o[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<floatx4_t*>(sm_o + (wave * G + lo) * kHeadDim + 16 * i + 4 * hi) = o[i] * vS;
-    if (hi == 0) {
-      sm_m[wave * G + lo] = m - kPShiftF4;   // l and O carry a factor 2^kPShiftF4
-      sm_l[wave * G + lo] = lsum[0];
+  for (int i = 0; i < 16; ++i) o[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig;
+
+  if (tok1 > tok0) {
+    uint4 qop[8];   // step j = 2 g + j2: dims 64 g + 32 j2 + 8 hi .. +7 of head lo
+    const float c = a.scale_log2 * load_q_f16<G>(a, s, g, lo, hi, qop, true);
+
+    const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
+    const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(a.k_scale);
+    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(a.v_scale);
+    const int64_t page0 = tok0 / kBlockSize;
+    const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+    uint8_t* my_stage = stage + wave * (kBlockSize * kRowBytesF16);
+
+    auto load_unit = [&](int64_t pi, I8Unit& U) {
+      int64_t base = 0, ts = 0;   // in rows
+      bool ok = false;
+      if (pi < npages) {
+        ok = page_base(a, s, g, page0 + pi, 1, &base, &ts);
+        if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
+      }
+      U.ok = ok;
+      const u32x2_t z2 = {0u, 0u};
+      const u32x4_t z4 = {0u, 0u, 0u, 0u};
+      u32x2_t kc[8], ks[4], vs[4];
+      u32x4_t vc[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kc[j] = z2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { vc[i] = z4; ks[i] = z2; vs[i] = z2; }
+      if (ok) {
+        const int64_t row = base + lo * ts;
+        const uint8_t* kp = Kc + row * kHeadDim + 8 * hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          kc[j] = *reinterpret_cast<const u32x2_t*>(kp + 64 * (j >> 1) + 32 * (j & 1));
+        const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(Vc + row * kHeadDim + 64 * hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vc[i] = vp[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t srow = base + (4 * hi + e) * ts;
+          ks[e] = *reinterpret_cast<const u32x2_t*>(Ks + srow * (kHeadDim / 64));
+          vs[e] = *reinterpret_cast<const u32x2_t*>(Vs + srow * (kHeadDim / 64));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) U.kc[j] = kc[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { U.vc[i] = vc[i]; U.ks[i] = ks[i]; U.vs[i] = vs[i]; }
+    };
+
+    const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
+    auto compute_unit = [&](int64_t pi, I8Unit& U) {
+      const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
+      const bool full = U.ok && pt0 + kBlockSize <= tok1;   // the same for every lane
+      const int nv = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
+      if (!full) {
+        // rows outside the split or the sequence, or of a masked page, get
+        // weight 0; their stale codes and scales become zeros (0 * NaN is not 0)
+        const bool keep = lo < nv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ke = 4 * hi + e < nv;
+          U.vs[e] = ke ? U.vs[e] : u32x2_t{0u, 0u};
+          U.ks[e] = ke ? U.ks[e] : u32x2_t{0u, 0u};
+        }
+      }
+      // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
+      {
+        uint8_t* row = my_stage + lo * kRowBytesF16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) =
+              i8x8_to_f16(U.vc[j >> 1][2 * (j & 1)], U.vc[j >> 1][2 * (j & 1) + 1]);
+      }
+      // T_g = K_g Q_g^T per scale group, then S^T = sum_g s_tg T_g in fp32
+      floatx4_t tg[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        tg[j >> 1] = mfma_f16(i8x8_to_f16(U.kc[j][0], U.kc[j][1]), qop[j], tg[j >> 1]);
+      float x[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // copy the vector elements out first: a bit cast of a vector element
+        // lvalue reads the vector's first element whatever the index
+        const uint32_t w01 = U.ks[e].x, w23 = U.ks[e].y;
+        const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
+        const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
+        float v = tg[0][e] * (float)s01[0];
+        v = fmaf(tg[1][e], (float)s01[1], v);
+        v = fmaf(tg[2][e], (float)s23[0], v);
+        v = fmaf(tg[3][e], (float)s23[1], v);
+        x[e] = full || 4 * hi + e < nv ? v * c : -INFINITY;
+        mx = fmaxf(mx, x[e]);
+      }
+      mx = max_over_row_groups(mx);
+      const bool grow = mx > m + kRescaleF4;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] *= alpha;
+        lsum *= alpha;
+      }
+      const float mp = m - kPShiftF4;
+      uint2 pop;
+      pop.x = pk_f16(fast_exp2(x[0] - mp), fast_exp2(x[1] - mp));
+      pop.y = pk_f16(fast_exp2(x[2] - mp), fast_exp2(x[3] - mp));
+      lsum = mfma_f16_k16(ones, pop, lsum);
+      // P^T operands with the V group scales of tokens 4hi .. 4hi+3 folded in
+      uint2 pg[4];
+      {
+        const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop.x);
+        const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop.y);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int dw = gg >> 1;
+          const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
+          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(U.vs[1][dw], U.vs[0][dw], sel));
+          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(U.vs[3][dw], U.vs[2][dw], sel));
+          pg[gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
+                              __builtin_bit_cast(uint32_t, p23 * s23));
+        }
+      }
+      // O^T += V^T (P o s_g)^T
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int trow = 4 * hi + (lo >> 2);
+      auto read_vt = [&](int i) {
+        const int chunk = 2 * i + ((lo & 3) >> 1);
+        const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
+        const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(void*)(my_stage + off));
+        return __builtin_bit_cast(uint2, v);
+      };
+      uint2 vt[kVtAhead];
+#pragma unroll
+      for (int i = 0; i < kVtAhead; ++i) vt[i] = read_vt(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o[i] = mfma_f16_k16(vt[i % kVtAhead], pg[i >> 2], o[i]);
+        if (i + kVtAhead < 16) vt[i % kVtAhead] = read_vt(i + kVtAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    I8Unit R[kAheadI8 + 1];
+#pragma unroll
+    for (int k = 0; k < kAheadI8; ++k) load_unit(wave + k * kWaves, R[k]);
+    for (int64_t u = wave; u < npages; u += (kAheadI8 + 1) * kWaves) {
+#pragma unroll
+      for (int b = 0; b <= kAheadI8; ++b) {
+        const int64_t uu = u + b * kWaves;
+        load_unit(uu + kAheadI8 * kWaves, R[(b + kAheadI8) % (kAheadI8 + 1)]);
+        if (uu < npages) compute_unit(uu, R[b]);
+      }
     }
   }
-  __syncthreads();
-  const int nsp = a.plan.num_splits;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
-    const int h = idx / kHeadDim;
-    const int d = idx % kHeadDim;
-    float M = kNegBig;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * G + h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = fast_exp2(sm_m[w * G + h] - M);
-      L += sm_l[w * G + h] * sc;
-      O += sm_o[(w * G + h) * kHeadDim + d] * sc;
-    }
-    const int qh = g * G + h;
-    const int64_t slot = ((int64_t)s * a.num_q_heads + qh) * nsp + split;
-    a.ws_o[slot * kHeadDim + d] = L > 0.f ? O / L : 0.f;
-    if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
-  }
+  finish_split_mfma<G>(a, s, g, split, stage, o, lsum, m, 1.0f, wave, lo, hi);
 }
 
 // ---- merge ------------------------------------------------------------------
@@ -743,6 +1015,7 @@ template <int G>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.plan.num_splits, a.geo.num_kv_heads, a.num_seqs);
   if (a.dtype == 0) return launch(decode_split_bf16<G>, grid, dim3(kThreads), 0, st, a);
+  if (a.dtype == 2) return launch(decode_split_int8<G>, grid, dim3(kThreads), 0, st, a);
   return launch(decode_split_nvfp4<G>, grid, dim3(kThreads), 0, st, a);
 }
 
@@ -754,9 +1027,10 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
 // KV heads, where each split then holds only 2,048 tokens).
 constexpr int64_t kTargetWgsBf16 = 512;
 constexpr int64_t kTargetWgsF4 = 512;
+constexpr int64_t kTargetWgsI8 = 512;
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len, int32_t dtype) {
-  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : kTargetWgsF4;
+  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : (dtype == 1 ? kTargetWgsF4 : kTargetWgsI8);
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   const int64_t chunks = (max_seq_len + unit - 1) / unit;      // 64-token chunks

@@ -1,12 +1,16 @@
-// KV append into the paged cache: an exact bf16 copy, or NVFP4 quantisation
-// on the way in; plus the per-tensor NVFP4 scale.
+// KV append into the paged cache: an exact bf16 copy, or NVFP4 or INT8
+// group-64 quantisation on the way in; plus the per-tensor NVFP4 scale.
 //
 // Paging follows [P1] "Things that bit me" (per-sequence page lists), [P3]
 // "Current limits" (one shared pool fixed at start-up) and the HND page
 // layout of [P5] "Validation before vibes": a page holds, per KV head, 16
 // consecutive token rows.  The NVFP4 format is the one of [P5] "Why NVFP4 KV
 // changes the math": e2m1 element codes, one e4m3 scale per 16 contiguous
-// head-dim elements, one fp32 tensor scale S = amax / (6 * 448).
+// head-dim elements, one fp32 tensor scale S = amax / (6 * 448).  The INT8
+// cache is the deployed 1M-token format of [P3] (memory table) and [P1] "And
+// the memory picture": groups of 64 with 2-byte scales, 16.5 KiB per token
+// per device; its rounding rules are readings (symmetric absmax groups,
+// binary16 scale RNE(amax / 127), codes clamp(RNE(x / s), +-127)).
 #include "device_common.h"
 #include "yrk_internal.h"
 
@@ -161,6 +165,105 @@ __global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
   }
 }
 
+// ---- INT8 group-64 ---------------------------------------------------------
+
+constexpr int kI8Groups = kHeadDim / 64;   // scale groups per row
+
+// Nearest binary16 pattern to q >= 0 (ties to even), saturating at 65504.
+// Works on the binary64 fields of q: keep 1 + 10 significand bits (or the
+// subnormal multiple of 2^-24) and round the dropped bits half-to-even.
+__device__ __forceinline__ uint32_t f16_encode_sat(double q) {
+  if (!(q < 65504.0)) return 0x7BFFu;
+  if (q == 0.0) return 0u;
+  const uint64_t u = (uint64_t)__double_as_longlong(q);
+  const int E = (int)(u >> 52) - 1023;            // q is a normal fp64 here
+  const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  if (E >= -14) {
+    uint64_t keep = sig >> 42;                      // 1 + 10 bits
+    const uint64_t rest = sig & ((1ull << 42) - 1);
+    const uint64_t half = 1ull << 41;
+    if (rest > half || (rest == half && (keep & 1))) ++keep;   // may carry to 2048
+    const uint32_t code = (uint32_t)(((E + 15) << 10) + (int)(keep - 1024));
+    return code > 0x7BFFu ? 0x7BFFu : code;
+  }
+  const int shift = 28 - E;                         // RNE(q * 2^24) = RNE(sig * 2^(E - 28))
+  if (shift >= 64) return 0u;
+  uint64_t keep = sig >> shift;
+  const uint64_t rest = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rest > half || (rest == half && (keep & 1))) ++keep;
+  return (uint32_t)keep;                            // 1024 is the smallest normal, 0x0400
+}
+
+__device__ __forceinline__ double f16_decode(uint32_t h) {
+  const int e = (int)((h >> 10) & 31u), m = (int)(h & 1023u);
+  return e ? ldexp((double)(1024 + m), e - 25) : ldexp((double)m, -24);
+}
+
+// Largest of x over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false));
+  return x;
+}
+
+// Four bf16 values (one lane's share of a group) -> four packed int8 codes
+// and, in every lane, the group's binary16 scale bits.  The lanes of one DPP
+// row (16 lanes x 4 = 64 elements) hold one group.  Both quotients are fp64
+// divisions (correctly rounded) followed by one rounding to nearest even.
+__device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits) {
+  const uint32_t e[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, e[i] & 0x7fffu);   // |x| orders like its bits
+  m = row16_max_u32(m);
+  const uint32_t sb = f16_encode_sat((double)bf16_to_f32((uint16_t)m) / 127.0);
+  *scale_bits = sb;
+  const double sv = f16_decode(sb);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int c = 0;
+    if (sv > 0.0) {
+      double q = rint((double)bf16_to_f32((uint16_t)e[i]) / sv);
+      q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+      c = (int)q;
+    }
+    packed |= ((uint32_t)c & 0xffu) << (8 * i);
+  }
+  return packed;
+}
+
+// One wave per (token, head) row: lane l quantises elements 4l .. 4l+3 of K
+// and of V; group l / 16.
+__global__ __launch_bounds__(256) void append_int8_kernel(AppendArgs a) {
+  const int H = a.geo.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = a.num_tokens * H;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows;
+       r += wstride) {
+    const int64_t t = r / H;
+    const int h = (int)(r - t * H);
+    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
+                                  a.err, lane == 0);
+    if (row < 0) continue;
+    const uint2 kw = reinterpret_cast<const uint2*>(a.k_src)[r * (kHeadDim / 4) + lane];
+    const uint2 vw = reinterpret_cast<const uint2*>(a.v_src)[r * (kHeadDim / 4) + lane];
+    uint32_t ksb, vsb;
+    const uint32_t kc = quantize_i8x4(kw, &ksb);
+    const uint32_t vc = quantize_i8x4(vw, &vsb);
+    reinterpret_cast<uint32_t*>(a.k_dst)[row * (kHeadDim / 4) + lane] = kc;
+    reinterpret_cast<uint32_t*>(a.v_dst)[row * (kHeadDim / 4) + lane] = vc;
+    if ((lane & 15) == 0) {
+      reinterpret_cast<uint16_t*>(a.k_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)ksb;
+      reinterpret_cast<uint16_t*>(a.v_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)vsb;
+    }
+  }
+}
+
 // ---- tensor scale ----------------------------------------------------------
 
 __global__ void store_word_kernel(uint32_t* p, uint32_t v) {
@@ -215,6 +318,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.dtype == 0) {
     const int64_t work = a.num_tokens * a.geo.num_kv_heads * kChunksPerRow;
     return launch(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+  }
+  if (a.dtype == 2) {
+    const int64_t waves = a.num_tokens * a.geo.num_kv_heads;   // one wave per row
+    return launch(append_int8_kernel, dim3(grid_for(waves * 64, 1 << 18)), dim3(256), 0, s, a);
   }
   const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
   return launch(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
