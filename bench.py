@@ -98,6 +98,77 @@ def build_step(W, Y, w, torch, dev):
     return step, ev, layers
 
 
+def build_verify_step(W, Y, w, layers, nq, torch, dev):
+    """A speculative verify step over a decode workload's layers: per layer,
+    nq new tokens roped and appended at n_ctx .. n_ctx + nq - 1 (the spare
+    page), then their nq queries, roped at the same positions, attend to the
+    n_ctx + nq cached tokens causally."""
+    N, L = w.n_ctx, w.layers
+    q_in = torch.empty((L, nq, w.hq, 256), dtype=torch.bfloat16, device=dev)
+    k_in = torch.empty((L, nq, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+    v_in = torch.empty_like(k_in)
+    for l in range(L):
+        q_in[l], k_in[l], v_in[l] = W.verify_inputs(w, l, nq, dev)
+    q_work = torch.empty_like(q_in)
+    k_work = torch.empty_like(k_in)
+    pos_all = torch.arange(N, N + nq, dtype=torch.int32, device=dev).repeat(L)
+    pos_new = pos_all[:nq]
+    lens = torch.full((1,), N + nq, dtype=torch.int32, device=dev)
+    outs = [torch.empty((1, nq, w.hq, 256), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ws = torch.empty(Y.verify_workspace_size(1, nq, w.hq, w.hkv, N + nq), dtype=torch.uint8,
+                     device=dev)
+    yp = w.yarn()
+    ev = []
+
+    def step(timing=False):
+        q_work.copy_(q_in)
+        k_work.copy_(k_in)
+        Y.yarn_rope_apply(yp, q_work.view(L * nq, w.hq, 256), pos_all)
+        Y.yarn_rope_apply(yp, k_work.view(L * nq, w.hkv, 256), pos_all)
+        for l, dl in enumerate(layers):
+            Y.kv_append_quantize(dl.layer, k_work[l], v_in[l], dl.block_tables[0], pos_new)
+            if timing:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            Y.verify_attention(dl.layer, q_work[l:l + 1], dl.block_tables, lens, N + nq, outs[l],
+                               ws)
+            if timing:
+                e1.record()
+                ev.append((e0, e1))
+
+    return step, ev
+
+
+def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2, 4, 6)):
+    """Verify steps at several query counts over the decode layers; the entry
+    for main_nq (3 draft tokens) is the headline, the others are listed."""
+    res = {}
+    for nq in sweep:
+        step, ev = build_verify_step(W, Y, w, layers, nq, torch, dev)
+        wall, kms = time_steps(step, ev, steps, warmup, torch)
+        ctx = w.n_ctx + nq
+        bpl = decode_bytes_per_launch(ctx, KV_BYTES_PER_TOKEN_LAYER, w.hq * nq)
+        res[nq] = {"value": w.layers * ctx / (wall / steps), "avg_launch_ms": kms,
+                   "ms_per_step": wall / steps * 1e3, "bytes_per_launch": bpl,
+                   "frac": bpl / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del step, ev
+        torch.cuda.empty_cache()
+    m = res[main_nq]
+    return {
+        "workload": f"speculative verify step, {w.layers} layers x 1,048,576 + {main_nq} cached "
+                    f"tokens (bf16), {main_nq} causal queries x 24 q / 4 KV heads",
+        "value": m["value"], "unit": "KV token-layers/s", "ms_per_step": m["ms_per_step"],
+        "avg_launch_ms": m["avg_launch_ms"],
+        "roofline": {"bound": "hbm", "achieved": m["bytes_per_launch"] / (m["avg_launch_ms"] * 1e-3)
+                     / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["frac"],
+                     "traffic": measured_traffic(f"verify_split_bf16_long_q{main_nq}_1m.json"),
+                     "bytes_per_launch": m["bytes_per_launch"]},
+        "by_queries": {str(nq): {"avg_launch_ms": r["avg_launch_ms"], "frac": r["frac"]}
+                       for nq, r in res.items()},
+    }
+
+
 def time_steps(step, ev, steps, warmup, torch):
     for _ in range(warmup):
         step()
@@ -173,6 +244,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nvfp4", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-tp2", action="store_true",
                     help="skip one card's share of a two-way KV-head split (12 q / 2 KV heads)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -226,7 +298,12 @@ def main():
                      "kernel": "decode_attention (split + merge), per layer",
                      "bytes_per_launch": bpl, "avg_launch_ms": kern_ms},
     }
-    del layers, step, ev
+    del step, ev
+    if not args.no_verify:
+        log("timing verify steps")
+        result["verify"] = bench_verify(W, Y, w, layers, torch, dev, max(3, args.steps // 2),
+                                        args.warmup)
+    del layers
     torch.cuda.empty_cache()
     if not args.no_nvfp4:
         wf = W.WORKLOADS["long_fp4"]

@@ -247,6 +247,53 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
                          uint32_t* dev_error_word, hipStream_t stream);
 
 /*
+ * yrk_verify_workspace_size -- bytes of device workspace that
+ * yrk_verify_attention needs for these shapes (the split partials of every
+ * (sequence, query, query head)); 0 for invalid sizes.
+ */
+size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int64_t max_seq_len);
+
+/*
+ * yrk_verify_attention -- multi-query decode for speculative verify: the
+ * last num_queries cached tokens of each sequence (the last accepted token
+ * and the drafted ones) attend to the cache at once, causally among
+ * themselves ([P1] "Things that bit me", [P3] "Limitations": a verify round
+ * evaluates K + 1 query columns; [P3] "Usage": 1 to 5 draft tokens).
+ * seq_lens[s] counts the sequence's cached tokens including those
+ * num_queries, whose keys and values must be appended before the call;
+ * query i sits at position seq_lens[s] - num_queries + i and attends to keys
+ * 0 .. seq_lens[s] - num_queries + i.  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads); logits are softmax_scale * <q, k> (0
+ * selects 1/sqrt(head_dim)).  The split-K plan and the log-sum-exp merge are
+ * those of yrk_decode_attention.  Both products run on bf16 matrix cores
+ * with fp32 accumulation; the attention weights enter the value product as
+ * two bf16 terms (16 significant bits).
+ *   q_dev            bf16 [num_seqs][num_queries][num_q_heads][head_dim]
+ *                    (already roped at the queries' positions), 16-byte aligned
+ *   block_tables_dev int32 [num_seqs][block_table_stride] (paged); NULL for
+ *                    contiguous (num_seqs must then be 1)
+ *   seq_lens_dev     int32 [num_seqs], each in [num_queries, max_seq_len];
+ *                    larger values are clamped to max_seq_len and smaller
+ *                    ones leave the queries at negative positions with zero
+ *                    rows, both flagged (YRK_DEVERR_POSITION)
+ *   out_dev          [num_seqs][num_queries][num_q_heads][head_dim], bf16 or
+ *                    fp32 (out_dtype)
+ *   workspace_dev    >= yrk_verify_workspace_size(...) bytes, 16-byte aligned
+ *   dev_error_word   nullable; see the conventions above
+ * Errors: YRK_EINVAL, YRK_ERANGE (max_seq_len beyond table or capacity),
+ * YRK_ENOTSUP (a cache other than bf16, head_dim != 256, group size not in
+ * {1,2,3,4,6}, or more than 48 query rows per KV head:
+ * num_queries * num_q_heads / num_kv_heads > 48), YRK_ENOSPC.
+ */
+int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                         int32_t num_queries, int32_t num_q_heads,
+                         const int32_t* block_tables_dev, int64_t block_table_stride,
+                         const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
+                         void* out_dev, int32_t out_dtype, void* workspace_dev,
+                         size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream);
+
+/*
  * yrk_prefill_workspace_size -- bytes of device workspace that
  * yrk_prefill_attention needs for num_q_tokens queries of num_q_heads heads
  * (GQA group 6): one 32-bit word per wave of its launch grid, 16 bytes per

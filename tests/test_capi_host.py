@@ -104,6 +104,42 @@ def test_decode_workspace_size_is_stable():
     assert Y.decode_workspace_size(15, 24, 4, 131072) >= 15 * 24 * 257 * 4
 
 
+def _verify(layer, S=1, nq=4, Hq=24, bt=0x3000, stride=64, lens=0x4000, max_len=1024,
+            out=0x5000, out_dtype=Y.OUT_BF16, ws=0x6000, ws_bytes=1 << 30, q=0x7000, scale=0.0):
+    return Y._lib.yrk_verify_attention(ctypes.byref(layer), q, S, nq, Hq, bt, stride, lens,
+                                       max_len, scale, out, out_dtype, ws, ws_bytes, None, None)
+
+
+def test_verify_validation():
+    L = _layer()
+    assert _verify(_layer(head_dim=128)) == Y.ENOTSUP
+    assert _verify(_layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50000)) == Y.ENOTSUP
+    assert _verify(_layer(dtype=Y.KV_NVFP4)) == Y.EINVAL     # scale planes missing
+    assert _verify(L, nq=0) == Y.EINVAL
+    assert _verify(L, nq=9) == Y.ENOTSUP                     # 9 x 6 = 54 rows > 48
+    # 12 x 4 = 48 rows is accepted: the call gets as far as the workspace check
+    assert _verify(L, nq=12, Hq=16, ws_bytes=16) == Y.ENOSPC
+    assert _verify(L, Hq=22) == Y.EINVAL
+    assert _verify(L, Hq=40) == Y.ENOTSUP
+    assert _verify(L, max_len=64 * 16 + 1) == Y.ERANGE
+    assert _verify(L, q=0x7008) == Y.EINVAL                  # misaligned
+    assert _verify(L, out_dtype=5) == Y.EINVAL
+    assert _verify(L, scale=float("nan")) == Y.EINVAL
+    assert _verify(L, bt=None) == Y.EINVAL
+    assert _verify(L, ws_bytes=16) == Y.ENOSPC
+    assert _verify(_layer(paged=0), S=2, bt=None) == Y.EINVAL
+
+
+def test_verify_workspace_size():
+    a = Y.verify_workspace_size(1, 6, 24, 4, 1048576)
+    assert a > 0 and a == Y.verify_workspace_size(1, 6, 24, 4, 1048576)
+    assert Y.verify_workspace_size(1, 9, 24, 4, 1048576) == 0     # 54 rows per KV head
+    assert Y.verify_workspace_size(1, 0, 24, 4, 1048576) == 0
+    assert Y.verify_workspace_size(1, 2, 24, 5, 1048576) == 0     # 24 heads over 5 KV heads
+    # one partial (256 + 1 floats) per (sequence, query, head, split), at least one split
+    assert Y.verify_workspace_size(3, 6, 24, 4, 64) >= 3 * 6 * 24 * 257 * 4
+
+
 def test_append_validation():
     L = _layer()
     f = Y._lib.yrk_kv_append_quantize

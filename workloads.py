@@ -109,6 +109,35 @@ def gen_q(w: Workload, unit: int, ntok: int, device, token0: int = 0):
     return q
 
 
+# Verify-step queries take their own slice of the query stream (decode's
+# query is token 0, the bench step's new one token 1).
+VERIFY_Q_TOKEN0 = 8
+
+
+def verify_inputs(w: Workload, unit: int, nq: int, device):
+    """Raw (un-roped) inputs of one layer's verify step: nq queries [nq, hq, 256]
+    and the nq new keys and values [nq, hkv, 256] that take positions
+    n_ctx .. n_ctx + nq - 1."""
+    q = gen_q(w, unit, nq, device, token0=VERIFY_Q_TOKEN0)
+    k = torch.empty((nq, w.hkv, D), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    gen_kv(w, unit, synth.K, nq, k, token0=w.n_ctx)
+    gen_kv(w, unit, synth.V, nq, v, token0=w.n_ctx)
+    return q, k, v
+
+
+def verify_inputs_host(w: Workload, unit: int, nq: int):
+    """The same inputs as verify_inputs, drawn by the host generator (bf16 bits)."""
+    q = synth.host_fill(w.seed, synth.stream_id(unit, synth.Q), VERIFY_Q_TOKEN0, nq, w.hq, D)
+    kw = dict(outlier_p=w.elem_outlier_p, outlier_mul=20.0) if w.elem_outlier_p else {}
+    kv = []
+    for tensor, ostream in ((synth.K, synth.K_OUTLIER), (synth.V, synth.V_OUTLIER)):
+        kv.append(synth.host_fill(w.seed, synth.stream_id(unit, tensor), w.n_ctx, nq, w.hkv, D,
+                                  chan_mul=chan_mul(w, unit, tensor),
+                                  outlier_stream=synth.stream_id(unit, ostream), **kw))
+    return q, kv[0], kv[1]
+
+
 def page_table(w: Workload, unit: int):
     """Page table(s) of one layer: [seqs, pages_per_seq] int32 (numpy)."""
     if not w.paged:

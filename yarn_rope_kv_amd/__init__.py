@@ -72,6 +72,9 @@ _SIGS = {
     "yrk_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i64], ctypes.c_size_t),
     "yrk_decode_attention": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _P, _i64, _P, _i64, _f,
                               _P, _i32, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "yrk_verify_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i64], ctypes.c_size_t),
+    "yrk_verify_attention": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _i32, _P, _i64, _P, _i64,
+                              _f, _P, _i32, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
     "yrk_prefill_workspace_size": ([_i64, _i32, _i32], ctypes.c_size_t),
     "yrk_prefill_attention": ([ctypes.POINTER(_KvLayerC), _P, _i64, _i32, _i64, _P, _i64, _f, _P,
                                _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
@@ -220,6 +223,31 @@ def decode_attention(layer: KVLayer, q, block_tables, seq_lens, max_seq_len, out
                                      softmax_scale, out.data_ptr(), out_dtype,
                                      workspace.data_ptr(), _nbytes(workspace), _ptr(err),
                                      _stream(q)), "yrk_decode_attention")
+    return out
+
+
+def verify_workspace_size(num_seqs, num_queries, num_q_heads, num_kv_heads, max_seq_len,
+                          head_dim=HEAD_DIM):
+    return int(_lib.yrk_verify_workspace_size(num_seqs, num_queries, num_q_heads, num_kv_heads,
+                                              head_dim, max_seq_len))
+
+
+def verify_attention(layer: KVLayer, q, block_tables, seq_lens, max_seq_len, out, workspace,
+                     softmax_scale=0.0, err=None):
+    """q: bf16 [S, Q, Hq, 256], the last Q cached tokens of each sequence (query
+    i at position seq_lens[s] - Q + i); block_tables: int32 [S, stride] (or
+    None, contiguous); seq_lens: int32 [S]; out: bf16 or fp32 [S, Q, Hq, 256];
+    workspace: uint8 tensor of verify_workspace_size() bytes."""
+    import torch
+    S, Q, Hq, _ = q.shape
+    lc = layer.c()
+    bt_stride = block_tables.shape[1] if block_tables is not None else 0
+    out_dtype = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(_lib.yrk_verify_attention(ctypes.byref(lc), q.data_ptr(), S, Q, Hq, _ptr(block_tables),
+                                     bt_stride, seq_lens.data_ptr(), max_seq_len,
+                                     softmax_scale, out.data_ptr(), out_dtype,
+                                     workspace.data_ptr(), _nbytes(workspace), _ptr(err),
+                                     _stream(q)), "yrk_verify_attention")
     return out
 
 

@@ -1,0 +1,91 @@
+// Device pieces shared by the split-K attention kernels over the KV cache
+// (single-query decode and multi-query verify): workgroup shape, page lookup,
+// MFMA operand types, the cross-row maximum of an MFMA accumulator and the
+// swizzled V staging layout with its transposing read.
+#pragma once
+
+#include "device_common.h"
+#include "yrk_internal.h"
+
+namespace yrk {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+constexpr int kRowBytesF16 = kHeadDim * 2;   // one staged 16-bit V row
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // (HIP's uint4 copies as a struct)
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t err_flag(uint32_t* err, uint32_t bit) {
+  set_error(err, bit);
+  return bit;
+}
+
+// Logical page -> element offset of its first row for KV head g, and the
+// element stride between consecutive token rows of the page.  Returns false
+// (page masked) for a table entry outside the pool.
+__device__ __forceinline__ bool page_base(const DecodeArgs& a, int s, int g, int64_t page,
+                                          int64_t row_elems, int64_t* base, int64_t* tstride) {
+  if (a.geo.paged) {
+    // one table entry for the whole wave: make that explicit, so the page
+    // test below is a scalar branch and not a per-lane one
+    const int64_t blk = __builtin_amdgcn_readfirstlane(
+        a.block_tables[(int64_t)s * a.block_table_stride + page]);
+    if (blk < 0 || blk >= a.geo.num_blocks) return false;
+    *base = ((blk * a.geo.num_kv_heads + g) * kBlockSize) * row_elems;
+    *tstride = row_elems;
+  } else {
+    *base = (page * kBlockSize * a.geo.num_kv_heads + g) * row_elems;
+    *tstride = (int64_t)a.geo.num_kv_heads * row_elems;
+  }
+  return true;
+}
+
+// Maximum over lanes l, l^16, l^32, l^48 (the four row groups of an MFMA
+// accumulator) with the gfx950 cross-row lane swaps.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Staged V row t keeps 16-byte chunk c at position c ^ vswz(t).  vswz is a
+// permutation of 0..7 on rows 0..7 and on rows 8..15 (so the 8 lanes of a
+// 128-byte write phase, rows t..t+7 with one chunk index, hit distinct banks)
+// and gives rows 4r..4r+3 distinct bits 1-2 (so the transposing reads, 4 rows
+// x 32 bytes per 16 lanes, fall into 4 distinct 32-byte bank groups).
+__device__ __forceinline__ int vswz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// The V^T operand of a 16-token staged page (16 rows of kRowBytesF16 bytes,
+// swizzled as above) for head dims 16 i .. 16 i + 15: ds_read_b64_tr_b16
+// gives lane (lo, hi) dim 16 i + lo at tokens 4 hi .. 4 hi + 3.
+__device__ __forceinline__ uint2 vt_operand(const uint8_t* page_stage, int i, int lo, int hi) {
+  const int trow = 4 * hi + (lo >> 2);
+  const int chunk = 2 * i + ((lo & 3) >> 1);
+  const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_t*)(void*)(page_stage + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Orders one wave's LDS writes before its later reads of the same buffer
+// (the staging buffers are private to a wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace
+}  // namespace yrk

@@ -246,6 +246,82 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   return launch_status(yrk::launch_decode(a, stream));
 }
 
+size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int64_t max_seq_len) {
+  if (num_seqs <= 0 || num_queries <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim != yrk::kHeadDim || max_seq_len < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const int64_t rows = (int64_t)num_queries * (num_q_heads / num_kv_heads);
+  if (rows > yrk::kVerifyMaxRows) return 0;
+  const yrk::DecodePlan p = yrk::plan_verify(num_seqs, num_kv_heads, (int32_t)rows, max_seq_len);
+  return yrk::decode_workspace_bytes(num_seqs, num_queries * num_q_heads, p);
+}
+
+int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                         int32_t num_queries, int32_t num_q_heads,
+                         const int32_t* block_tables_dev, int64_t block_table_stride,
+                         const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
+                         void* out_dev, int32_t out_dtype, void* workspace_dev,
+                         size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream) {
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  if (num_seqs <= 0 || num_queries <= 0 || num_q_heads <= 0 || max_seq_len < 0)
+    return YRK_EINVAL;
+  if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
+  if (!q_dev || !seq_lens_dev || !out_dev || !workspace_dev) return YRK_EINVAL;
+  if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
+  if (!aligned16(q_dev) || !aligned16(workspace_dev) || !aligned16(layer->k) ||
+      !aligned16(layer->v))
+    return YRK_EINVAL;
+  if (layer->dtype != YRK_KV_BF16) return YRK_ENOTSUP;
+  const int group = num_q_heads / layer->num_kv_heads;
+  if (group != 1 && group != 2 && group != 3 && group != 4 && group != 6)
+    return YRK_ENOTSUP;
+  if ((int64_t)num_queries * group > yrk::kVerifyMaxRows) return YRK_ENOTSUP;
+  if (layer->paged) {
+    if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
+    if (max_seq_len > block_table_stride * yrk::kBlockSize) return YRK_ERANGE;
+  } else {
+    if (num_seqs != 1) return YRK_EINVAL;
+    if (max_seq_len > layer->num_blocks * yrk::kBlockSize) return YRK_ERANGE;
+  }
+  if (max_seq_len > INT32_MAX) return YRK_ERANGE;
+  yrk::VerifyArgs va;
+  yrk::DecodeArgs& a = va.d;
+  va.num_queries = num_queries;
+  a.plan = yrk::plan_verify(num_seqs, layer->num_kv_heads, num_queries * group, max_seq_len);
+  const int32_t rows_per_seq = num_queries * num_q_heads;
+  const size_t need = yrk::decode_workspace_bytes(num_seqs, rows_per_seq, a.plan);
+  if (workspace_bytes < need) return YRK_ENOSPC;
+  if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
+  a.geo = geometry(layer);
+  a.dtype = layer->dtype;
+  a.group = group;
+  a.num_q_heads = num_q_heads;
+  a.num_seqs = num_seqs;
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.k = layer->k;
+  a.v = layer->v;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
+  a.k_tensor_scale = nullptr;
+  a.v_tensor_scale = nullptr;
+  a.block_tables = layer->paged ? block_tables_dev : nullptr;
+  a.block_table_stride = layer->paged ? block_table_stride : 0;
+  a.seq_lens = seq_lens_dev;
+  a.max_seq_len = max_seq_len;
+  a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
+  a.out = out_dev;
+  a.out_f32 = out_dtype == YRK_OUT_F32;
+  const size_t slots = (size_t)num_seqs * rows_per_seq * a.plan.num_splits;
+  a.ws_o = static_cast<float*>(workspace_dev);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace_dev) +
+                                      ((slots * yrk::kHeadDim * sizeof(float) + 255) / 256) * 256);
+  a.err = dev_error_word;
+  return launch_status(yrk::launch_verify(va, stream));
+}
+
 size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t head_dim) {
   if (num_q_tokens < 0 || num_q_heads <= 0 || head_dim != yrk::kHeadDim) return 0;
   return yrk::prefill_workspace_bytes(num_q_tokens, num_q_heads);

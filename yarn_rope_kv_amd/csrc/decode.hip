@@ -30,40 +30,10 @@
 // registers (the hardware fp4 -> bf16 conversion, then a bf16 dot with q and
 // one scale multiply per 16 elements; the tensor scales are folded into the
 // softmax scale and the output).
-#include "device_common.h"
-#include "yrk_internal.h"
+#include "attn_common.h"
 
 namespace yrk {
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
-
-__device__ __forceinline__ uint32_t err_flag(uint32_t* err, uint32_t bit) {
-  set_error(err, bit);
-  return bit;
-}
-
-// Logical page -> element offset of its first row for KV head g, and the
-// element stride between consecutive token rows of the page.  Returns false
-// (page masked) for a table entry outside the pool.
-__device__ __forceinline__ bool page_base(const DecodeArgs& a, int s, int g, int64_t page,
-                                          int64_t row_elems, int64_t* base, int64_t* tstride) {
-  if (a.geo.paged) {
-    // one table entry for the whole wave: make that explicit, so the page
-    // test below is a scalar branch and not a per-lane one
-    const int64_t blk = __builtin_amdgcn_readfirstlane(
-        a.block_tables[(int64_t)s * a.block_table_stride + page]);
-    if (blk < 0 || blk >= a.geo.num_blocks) return false;
-    *base = ((blk * a.geo.num_kv_heads + g) * kBlockSize) * row_elems;
-    *tstride = row_elems;
-  } else {
-    *base = (page * kBlockSize * a.geo.num_kv_heads + g) * row_elems;
-    *tstride = (int64_t)a.geo.num_kv_heads * row_elems;
-  }
-  return true;
-}
 
 // Per-row online softmax update for one page: scores sc[j][h] already in the
 // log2 domain (masked tokens at -inf).  Returns the probabilities in sc.
@@ -316,15 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
 //   loads     the codes and scales of the wave's next 32 tokens are in flight
 //             while the current ones are computed.
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // (HIP's uint4 copies as a struct)
-
 constexpr int kUnitPages = 2;                            // pages per wave step
-constexpr int kRowBytesF16 = kHeadDim * 2;               // staged V row
 constexpr int kStageBytes = kWaves * kUnitPages * kBlockSize * kRowBytesF16;   // 64 KiB
 constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
 // The running maximum m is raised only when a step's maximum exceeds it by
@@ -371,24 +333,6 @@ __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, uint32_t qs2) {
   return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
-
-// Maximum over lanes l, l^16, l^32, l^48 (the four row groups of an MFMA
-// accumulator) with the gfx950 cross-row lane swaps.
-__device__ __forceinline__ float max_over_row_groups(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// Staged V row t keeps 16-byte chunk c at position c ^ vswz(t).  vswz is a
-// permutation of 0..7 on rows 0..7 and on rows 8..15 (so the 8 lanes of a
-// 128-byte write phase, rows t..t+7 with one chunk index, hit distinct banks)
-// and gives rows 4r..4r+3 distinct bits 1-2 (so the transposing reads, 4 rows
-// x 32 bytes per 16 lanes, fall into 4 distinct 32-byte bank groups).
-__device__ __forceinline__ int vswz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 // One lane's share of the two pages of a wave step.
 struct F4Unit {
@@ -644,18 +588,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
       pop.w = pk_f16(fast_exp2(x[1][2] - mp), fast_exp2(x[1][3] - mp));
       lsum = mfma_f16(ones, pop, lsum);
       // O^T += V^T P^T: k order = tokens 4hi..4hi+3 of page 0, then of page 1
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int trow = 4 * hi + (lo >> 2);
+      wave_lds_sync();
       auto read_vt = [&](int i) {
-        const int chunk = 2 * i + ((lo & 3) >> 1);
-        const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
-        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(void*)(my_stage + off));
-        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(void*)(my_stage + kBlockSize * kRowBytesF16 + off));
-        const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+        const uint2 w0 = vt_operand(my_stage, i, lo, hi);
+        const uint2 w1 = vt_operand(my_stage + kBlockSize * kRowBytesF16, i, lo, hi);
         return make_uint4(w0.x, w0.y, w1.x, w1.y);
       };
       // V^T operands read kVtAhead products ahead, so that LDS latency overlaps
@@ -669,9 +605,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
         if (i + kVtAhead < 16) vt[i % kVtAhead] = read_vt(i + kVtAhead);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_lds_sync();
     };
 
     F4Unit R[kAheadF4 + 1];
@@ -712,7 +646,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 //             P^T operand, one transposing LDS read per 16 dims is V^T.
 
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
 constexpr int kAheadI8 = 1;                                        // steps in flight
@@ -898,17 +831,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         }
       }
       // O^T += V^T (P o s_g)^T
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int trow = 4 * hi + (lo >> 2);
-      auto read_vt = [&](int i) {
-        const int chunk = 2 * i + ((lo & 3) >> 1);
-        const int off = trow * kRowBytesF16 + ((chunk ^ vswz(trow)) * 16) + 8 * (lo & 1);
-        const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(void*)(my_stage + off));
-        return __builtin_bit_cast(uint2, v);
-      };
+      wave_lds_sync();
+      auto read_vt = [&](int i) { return vt_operand(my_stage, i, lo, hi); };
       uint2 vt[kVtAhead];
 #pragma unroll
       for (int i = 0; i < kVtAhead; ++i) vt[i] = read_vt(i);
@@ -918,9 +842,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         if (i + kVtAhead < 16) vt[i % kVtAhead] = read_vt(i + kVtAhead);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_lds_sync();
     };
 
     I8Unit R[kAheadI8 + 1];
@@ -1063,6 +985,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  return launch_decode_merge(a, st);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st) {
   return launch(decode_merge, dim3(4 * a.num_q_heads, a.num_seqs), dim3(256), 0, st, a);
 }
 

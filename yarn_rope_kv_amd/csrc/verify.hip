@@ -1,0 +1,333 @@
+// Multi-query split-K decode attention over a paged bf16 KV cache (gfx950):
+// the verify step of speculative decoding, where num_queries consecutive
+// tokens of a sequence (the last accepted one and the drafted ones) attend
+// to the cache at once ([P1] "Things that bit me" and [P3] "Limitations":
+// a verify round evaluates K + 1 query columns; [P3] "Usage": 1 to 5 draft
+// tokens, so 2 to 6 queries).  Their keys and values are in
+// the cache already; query i of a sequence of len cached tokens sits at
+// position len - num_queries + i and sees keys 0 .. len - num_queries + i.
+//
+// With G query heads per KV head, one KV head serves R = num_queries x G
+// query rows (row r = query r / G, head r % G of the group).  Every key is
+// used by all R rows, so the rows share each load, and with R up to 48 the
+// two products are dense enough for the matrix cores:
+//
+//   grid      (split, kv_head, seq), 4 waves; a split owns a contiguous token
+//             range and wave w takes its pages w, w + 4, ... (16 tokens each),
+//             with the next page's loads in flight while one is computed.
+//   S^T       = K Q^T on v_mfma_f32_16x16x32_bf16, one 16-row column block of
+//             Q at a time (C = ceil(R / 16) blocks).  Lane (t, kg) loads 16
+//             bytes of key row t per step (head dims 32 j + 8 kg .. +7; every
+//             load instruction reads 64 contiguous bytes of 16 rows), which is
+//             the A operand as loaded.  The Q^T operands of the workgroup's R
+//             rows sit in LDS, read once per step and block.
+//   softmax   per row, log2 domain, in the accumulator layout: lane (h, r)
+//             holds tokens 4r .. 4r + 3 of row h.  The running maximum is
+//             raised (and O rescaled) only when a page exceeds it by more
+//             than 1, so p = 2^(s - m) <= 2.  Keys past a row's own position
+//             and past the split get p = 0.
+//   O^T      += V^T P^T on the same instruction with its 32-long inner
+//             dimension holding each token twice: p is split into
+//             p_hi = bf16(p) and p_lo = bf16(p - p_hi), and the operand pair
+//             (V^T, V^T) x (P_hi^T ; P_lo^T) sums V (p_hi + p_lo), so the
+//             weights keep 16 significant bits instead of bf16's 8 at no
+//             extra instruction.  V is staged into per-wave LDS (swizzled
+//             rows) and read back transposed with ds_read_b64_tr_b16.  The
+//             row sums are the same product with a ones operand.
+//   finish    the 4 waves' partials of a column block are combined through
+//             LDS into one normalised partial and log2-sum-exp per (query,
+//             head, split); the decode merge then combines the splits.
+#include "attn_common.h"
+
+namespace yrk {
+namespace {
+
+constexpr int kColRows = 16;                                        // rows per MFMA column block
+constexpr int kStageBytesV = kWaves * kBlockSize * kRowBytesF16;    // 32 KiB: one V page per wave
+constexpr int kQOpBytes = 8 * 64 * 16;                              // Q^T operands of a block: 8 KiB
+constexpr int kFinishBytes = (kWaves * kColRows * kHeadDim + 2 * kWaves * kColRows) * 4;
+constexpr int kLdsBytes = kFinishBytes;                             // 64.5 KiB
+static_assert(kStageBytesV + 3 * kQOpBytes <= kLdsBytes, "V staging and Q^T fit the buffer");
+constexpr float kRescaleV = 1.0f;
+
+__device__ __forceinline__ floatx4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16, rounded to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
+}
+
+// The P^T operand of 4 weights: bf16 high parts, then the bf16 residuals.
+__device__ __forceinline__ u32x4_t split_weights(const float (&p)[4]) {
+  const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
+  const uint32_t l01 = pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+  const uint32_t l23 = pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+  return u32x4_t{h01, h23, l01, l23};
+}
+
+// One lane's share of one page: 16-byte chunks 4 j + kg of key and value
+// row t (head dims 32 j + 8 kg .. +7).
+struct VUnit {
+  u32x4_t k[8], v[8];
+  bool ok;                  // page present and inside the split
+};
+
+template <int C, int AHEAD>
+__global__ __launch_bounds__(kThreads, (C == 1 ? 2 : 1)) void verify_split_bf16(VerifyArgs va) {
+  static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 1, "verify kernel shape");
+  const DecodeArgs& a = va.d;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int lo = lane & 15, hi = lane >> 4;
+  const int G = a.group, nq = va.num_queries, R = nq * G;
+
+  int64_t len = a.seq_lens[s];
+  if (len > a.max_seq_len) {
+    if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+    len = a.max_seq_len;
+  }
+  if (len < nq && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+  if (len < 0) len = 0;
+  const int64_t qpos0 = len - nq;   // position of query 0 (negative only when flagged)
+  const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
+  const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
+
+  // Q^T operands: block c, step j, lane l at ((c * 8 + j) * 64 + l) * 16
+  // bytes: row 16 c + l % 16, head dims 32 j + 8 (l / 16) .. +7 (zero rows
+  // beyond R)
+  u32x4_t* qop = reinterpret_cast<u32x4_t*>(lds + kStageBytesV);
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+    const int l = idx & 63, j = (idx >> 6) & 7, c = idx >> 9;
+    const int r = kColRows * c + (l & 15);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      const int64_t h = (int64_t)g * G + r % G;
+      const uint16_t* qrow = a.q + (((int64_t)s * nq + r / G) * a.num_q_heads + h) * kHeadDim;
+      v = *reinterpret_cast<const u32x4_t*>(qrow + 32 * j + 8 * (l >> 4));
+    }
+    qop[idx] = v;
+  }
+  // the last key position lane lo's row of each block may see
+  int64_t last[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int r = kColRows * c + lo;
+    last[c] = qpos0 + (r < R ? r / G : nq - 1);
+  }
+  __syncthreads();
+
+  floatx4_t o[C][16], lsum[C];
+  float m[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[c][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m[c] = kNegBig;
+  }
+
+  if (tok1 > tok0) {
+    const uint16_t* K = static_cast<const uint16_t*>(a.k);
+    const uint16_t* V = static_cast<const uint16_t*>(a.v);
+    const int64_t page0 = tok0 / kBlockSize;
+    const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+    uint8_t* my_stage = lds + wave * (kBlockSize * kRowBytesF16);
+    const float cl2 = a.scale_log2;
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+
+    auto load_unit = [&](int64_t pi, VUnit& U) {
+      int64_t base = 0, ts = 0;   // in elements
+      bool ok = false;
+      if (pi < npages) {
+        ok = page_base(a, s, g, page0 + pi, kHeadDim, &base, &ts);
+        if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
+      }
+      U.ok = ok;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      u32x4_t k[8], v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) k[j] = v[j] = z;
+      if (ok) {
+        const int64_t row = base + lo * ts;
+        const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(K + row) + hi;
+        const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(V + row) + hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          k[j] = kp[4 * j];
+          v[j] = vp[4 * j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        U.k[j] = k[j];
+        U.v[j] = v[j];
+      }
+    };
+
+    auto compute_unit = [&](int64_t pi, VUnit& U) {
+      const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
+      const int nv = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
+      // every row sees every token of the page (the same for all lanes)
+      const bool full = nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
+      if (nv < kBlockSize) {
+        // rows outside the split or the sequence, or of a masked page, get
+        // weight 0; their stale values become zeros (0 * NaN is not 0)
+        const bool keep = lo < nv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) U.v[j] = keep ? U.v[j] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      // stage V: row lo, logical chunks 4 j + hi
+      {
+        uint8_t* row = my_stage + lo * kRowBytesF16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<u32x4_t*>(row + ((4 * j + hi) ^ vswz(lo)) * 16) = U.v[j];
+      }
+      floatx4_t sc[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) sc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) sc[c] = mfma_bf16(U.k[j], qop[(c * 8 + j) * 64 + lane], sc[c]);
+      }
+      u32x4_t pop[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = full || (4 * hi + e < nv && pt0 + 4 * hi + e <= last[c]);
+          x[e] = vis ? sc[c][e] * cl2 : -INFINITY;
+          mx = fmaxf(mx, x[e]);
+        }
+        mx = max_over_row_groups(mx);
+        const bool grow = mx > m[c] + kRescaleV;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mn = grow ? mx : m[c];
+          const float alpha = fast_exp2(m[c] - mn);
+          m[c] = mn;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
+          lsum[c] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - m[c]);
+        pop[c] = split_weights(p);
+        lsum[c] = mfma_bf16(ones, pop[c], lsum[c]);
+      }
+      // O^T += V^T (P_hi + P_lo)^T
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint2 vt = vt_operand(my_stage, i, lo, hi);
+        const u32x4_t av = {vt.x, vt.y, vt.x, vt.y};
+#pragma unroll
+        for (int c = 0; c < C; ++c) o[c][i] = mfma_bf16(av, pop[c], o[c][i]);
+      }
+      wave_lds_sync();
+    };
+
+    VUnit U[AHEAD + 1];
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * kWaves, U[k]);
+    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * kWaves) {
+#pragma unroll
+      for (int b = 0; b <= AHEAD; ++b) {
+        const int64_t uu = u + b * kWaves;
+        load_unit(uu + AHEAD * kWaves, U[(b + AHEAD) % (AHEAD + 1)]);
+        if (uu < npages) compute_unit(uu, U[b]);
+      }
+    }
+  }
+
+  // combine the 4 waves, one column block at a time
+  float* sm_o = reinterpret_cast<float*>(lds);     // [kWaves][16][256]
+  float* sm_m = sm_o + kWaves * kColRows * kHeadDim;
+  float* sm_l = sm_m + kWaves * kColRows;
+  const int nsp = a.plan.num_splits;
+  const int64_t rows_per_seq = (int64_t)nq * a.num_q_heads;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<floatx4_t*>(sm_o + (wave * kColRows + lo) * kHeadDim + 16 * i + 4 * hi) =
+          o[c][i];
+    if (hi == 0) {
+      sm_m[wave * kColRows + lo] = m[c];
+      sm_l[wave * kColRows + lo] = lsum[c][0];
+    }
+    __syncthreads();
+    // 256 threads: one row of the block per pass, thread = head dim
+    for (int row = 0; row < kColRows; ++row) {
+      const int r = kColRows * c + row;
+      if (r >= R) break;
+      const int d = threadIdx.x;
+      float M = kNegBig;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
+      float L = 0.f, Ov = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(sm_m[w * kColRows + row] - M);
+        L += sm_l[w * kColRows + row] * sc;
+        Ov += sm_o[(w * kColRows + row) * kHeadDim + d] * sc;
+      }
+      const int64_t hh = (int64_t)(r / G) * a.num_q_heads + (int64_t)g * G + r % G;
+      const int64_t slot = ((int64_t)s * rows_per_seq + hh) * nsp + split;
+      a.ws_o[slot * kHeadDim + d] = L > 0.f ? Ov / L : 0.f;
+      if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
+int column_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
+
+}  // namespace
+
+// One round of workgroups: two per CU where a column block's accumulators
+// leave room for a second workgroup, else one.
+DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len) {
+  const int64_t target_wgs = column_blocks(rows) == 1 ? 512 : 256;
+  const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t chunks = (max_seq_len + unit - 1) / unit;
+  int64_t splits = (target_wgs + units - 1) / units;
+  if (splits > chunks) splits = chunks;
+  if (splits < 1) splits = 1;
+  const int64_t per = (chunks + splits - 1) / splits;
+  DecodePlan p;
+  p.tokens_per_split = per * unit;
+  p.num_splits = (int32_t)((chunks + per - 1) / per);
+  if (p.num_splits < 1) p.num_splits = 1;
+  return p;
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
+  const DecodeArgs& d = a.d;
+  const int rows = a.num_queries * d.group;
+  const dim3 grid(d.plan.num_splits, d.geo.num_kv_heads, d.num_seqs);
+  hipError_t e;
+  switch (column_blocks(rows)) {
+    case 1: e = launch(verify_split_bf16<1, 1>, grid, dim3(kThreads), 0, st, a); break;
+    case 2: e = launch(verify_split_bf16<2, 1>, grid, dim3(kThreads), 0, st, a); break;
+    case 3: e = launch(verify_split_bf16<3, 1>, grid, dim3(kThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  DecodeArgs m = d;
+  m.num_q_heads = a.num_queries * d.num_q_heads;   // output rows [seq][query][head]
+  return launch_decode_merge(m, st);
+}
+
+}  // namespace yrk

@@ -91,6 +91,20 @@ struct DecodeArgs {
   DecodePlan plan;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// The log-sum-exp merge of the split partials alone: one output row per
+// (sequence, a.num_q_heads row) from a.ws_o / a.ws_lse.
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
+
+// Multi-query decode (speculative verify): num_queries consecutive queries
+// per sequence, causal among themselves; the rows of one KV head's group are
+// (query i, head j) = i * group + j, at most kVerifyMaxRows of them.
+constexpr int kVerifyMaxRows = 48;
+struct VerifyArgs {
+  DecodeArgs d;           // d.num_q_heads: query heads per token
+  int32_t num_queries;
+};
+DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 
 struct PrefillArgs {
   KvGeometry geo;
