@@ -70,21 +70,17 @@ def build_step(W, Y, w, torch, dev):
         W.gen_kv(w, l, 1, 1, k_in[l:l + 1], token0=N)
         W.gen_kv(w, l, 2, 1, v_in[l:l + 1], token0=N)
     q_work = torch.empty_like(q_in)
-    k_work = torch.empty_like(k_in)
     outs, wss = zip(*[W.decode_outputs(w, dl, device=dev) for dl in layers])
-    pos_q = torch.full((L,), N, dtype=torch.int32, device=dev)
     pos_new = torch.full((1,), N, dtype=torch.int32, device=dev)
     yp = w.yarn()
     ev = []
 
     def step(timing=False):
-        q_work.copy_(q_in)
-        k_work.copy_(k_in)
-        Y.yarn_rope_apply(yp, q_work, pos_q)             # all layers' queries, one launch
-        Y.yarn_rope_apply(yp, k_work, pos_q)             # all layers' new keys
+        q_work.copy_(q_in)                               # roped in place below
         for l, dl in enumerate(layers):
-            Y.kv_append_quantize(dl.layer, k_work[l:l + 1], v_in[l:l + 1], dl.block_tables[0],
-                                 pos_new)
+            # the new query and key roped at position N, key and value appended
+            Y.rope_append(dl.layer, yp, q_work[l:l + 1], k_in[l:l + 1], v_in[l:l + 1],
+                          dl.block_tables[0], pos_new)
             if timing:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -110,9 +106,7 @@ def build_verify_step(W, Y, w, layers, nq, torch, dev):
     for l in range(L):
         q_in[l], k_in[l], v_in[l] = W.verify_inputs(w, l, nq, dev)
     q_work = torch.empty_like(q_in)
-    k_work = torch.empty_like(k_in)
-    pos_all = torch.arange(N, N + nq, dtype=torch.int32, device=dev).repeat(L)
-    pos_new = pos_all[:nq]
+    pos_new = torch.arange(N, N + nq, dtype=torch.int32, device=dev)
     lens = torch.full((1,), N + nq, dtype=torch.int32, device=dev)
     outs = [torch.empty((1, nq, w.hq, 256), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     ws = torch.empty(Y.verify_workspace_size(1, nq, w.hq, w.hkv, N + nq), dtype=torch.uint8,
@@ -121,12 +115,9 @@ def build_verify_step(W, Y, w, layers, nq, torch, dev):
     ev = []
 
     def step(timing=False):
-        q_work.copy_(q_in)
-        k_work.copy_(k_in)
-        Y.yarn_rope_apply(yp, q_work.view(L * nq, w.hq, 256), pos_all)
-        Y.yarn_rope_apply(yp, k_work.view(L * nq, w.hkv, 256), pos_all)
+        q_work.copy_(q_in)                               # roped in place below
         for l, dl in enumerate(layers):
-            Y.kv_append_quantize(dl.layer, k_work[l], v_in[l], dl.block_tables[0], pos_new)
+            Y.rope_append(dl.layer, yp, q_work[l], k_in[l], v_in[l], dl.block_tables[0], pos_new)
             if timing:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

@@ -204,6 +204,39 @@ int yrk_kv_append_quantize(const yrk_kv_layer* layer, const void* k_dev, const v
                            uint32_t* dev_error_word, hipStream_t stream);
 
 /*
+ * yrk_rope_append -- one pass for the new tokens of a step: their queries
+ * are roped in place and their keys roped on the way into the cache (then
+ * copied or quantised as yrk_kv_append_quantize does), values appended
+ * unroped.  The results are bit-identical to yrk_yarn_rope_apply on q and
+ * on k followed by yrk_kv_append_quantize; the pass saves writing and
+ * re-reading the roped keys and one launch per tensor ([P1] "YaRN, and
+ * matching what vLLM actually does": mscale on cos/sin inside the rope, on
+ * the rotary dimensions only).  Token t's query and key share position
+ * positions_dev[t] (a decode step's query and its own key; the queries of
+ * a verify round and their keys).
+ *   params           YaRN parameters; this pass needs head_dim 256 and
+ *                    rotary_dim 64 (yrk_yarn_rope_apply takes others)
+ *   q_dev            nullable: bf16 [num_tokens] rows of num_q_heads heads
+ *                    of head_dim, q_token_stride elements apart (a multiple
+ *                    of 4, at least num_q_heads * head_dim), 8-byte aligned;
+ *                    roped in place whatever the table says
+ *   k_dev, v_dev     bf16 [num_tokens][num_kv_heads][head_dim], contiguous,
+ *                    16-byte aligned, keys not yet roped; not modified
+ *   block_table_dev  int32 [block_table_len] (paged); NULL for contiguous
+ *   dev_error_word   nullable; positions outside the table or capacity, or
+ *                    table entries outside the pool, set a bit and that
+ *                    token's key and value are skipped
+ * Errors: YRK_EINVAL (parameters as for yrk_yarn_rope_apply, nulls, shapes,
+ * alignment), YRK_ENOTSUP (head_dim or rotary_dim other than 256 / 64, or
+ * a layout other than head_dim 256 / block 16).
+ */
+int yrk_rope_append(const yrk_kv_layer* layer, const yrk_yarn_params* params, void* q_dev,
+                    int32_t num_q_heads, int64_t q_token_stride, const void* k_dev,
+                    const void* v_dev, int64_t num_tokens, const int32_t* block_table_dev,
+                    int64_t block_table_len, const int32_t* positions_dev,
+                    uint32_t* dev_error_word, hipStream_t stream);
+
+/*
  * yrk_decode_workspace_size -- bytes of device workspace that
  * yrk_decode_attention needs for these sizes (the split partials: per
  * sequence, query head and split, head_dim fp32 plus one fp32 log-sum-exp).

@@ -156,6 +156,32 @@ def test_append_validation():
     assert f(ctypes.byref(i8), None, None, 0, 0x400, 4, None, None, None) == Y.OK
 
 
+def test_rope_append_validation():
+    L = _layer()
+    p = Y.YarnParams()
+    f = Y._lib.yrk_rope_append
+
+    def call(layer=L, params=p, q=0x8000, hq=24, qs=24 * 256, k=0x100, v=0x200, T=4, bt=0x400,
+             bt_len=4, pos=0x300):
+        lc, pc = layer, params.c()
+        return f(ctypes.byref(lc), ctypes.byref(pc), q, hq, qs, k, v, T, bt, bt_len, pos, None,
+                 None)
+
+    assert call(params=Y.YarnParams(factor=0.5)) == Y.EINVAL
+    assert call(params=Y.YarnParams(rotary_dim=32)) == Y.ENOTSUP   # fused pass: 64 of 256
+    assert call(params=Y.YarnParams(head_dim=128, rotary_dim=64)) == Y.ENOTSUP
+    assert call(qs=24 * 256 - 4) == Y.EINVAL                        # rows overlap
+    assert call(qs=24 * 256 + 2) == Y.EINVAL                        # stride not a multiple of 4
+    assert call(q=0x8004) == Y.EINVAL                               # q not 8-byte aligned
+    assert call(hq=0) == Y.EINVAL
+    assert call(k=0x108) == Y.EINVAL                                # k not 16-byte aligned
+    assert call(T=-1) == Y.EINVAL
+    assert call(bt=None) == Y.EINVAL
+    assert call(layer=_layer(dtype=Y.KV_INT8)) == Y.EINVAL          # scale planes missing
+    assert call(T=0) == Y.OK                                        # nothing enqueued
+    assert call(q=None, hq=0, qs=0, T=0) == Y.OK
+
+
 def test_prefill_validation():
     L = _layer()
     f = Y._lib.yrk_prefill_attention

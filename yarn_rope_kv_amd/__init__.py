@@ -69,6 +69,8 @@ _SIGS = {
     "yrk_nvfp4_tensor_scale": ([_P, _i64, _P, _P], ctypes.c_int),
     "yrk_kv_append_quantize": ([ctypes.POINTER(_KvLayerC), _P, _P, _i64, _P, _i64, _P, _P, _P],
                                ctypes.c_int),
+    "yrk_rope_append": ([ctypes.POINTER(_KvLayerC), ctypes.POINTER(_YarnParamsC), _P, _i32, _i64,
+                         _P, _P, _i64, _P, _i64, _P, _P, _P], ctypes.c_int),
     "yrk_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i64], ctypes.c_size_t),
     "yrk_decode_attention": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _P, _i64, _P, _i64, _f,
                               _P, _i32, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
@@ -202,6 +204,24 @@ def kv_append_quantize(layer: KVLayer, k, v, block_table, positions, err=None):
     _check(_lib.yrk_kv_append_quantize(ctypes.byref(lc), k.data_ptr(), v.data_ptr(), T,
                                        _ptr(block_table), bt_len, positions.data_ptr(),
                                        _ptr(err), _stream(k)), "yrk_kv_append_quantize")
+
+
+def rope_append(layer: KVLayer, params: YarnParams, q, k, v, block_table, positions, err=None):
+    """One pass: q (bf16 [T, Hq, 256] or a strided view of rows, or None) roped
+    in place at positions; k (not yet roped) and v (bf16 [T, Hkv, 256]) roped
+    and appended at the same positions."""
+    T = k.shape[0]
+    lc, pc = layer.c(), params.c()
+    if q is not None:
+        if q.stride(2) != 1 or q.stride(1) != HEAD_DIM:
+            raise YrkError(EINVAL, "rope_append: q heads must be contiguous rows")
+        q_ptr, hq, q_stride = q.data_ptr(), q.shape[1], q.stride(0)
+    else:
+        q_ptr, hq, q_stride = None, 0, 0
+    bt_len = block_table.numel() if block_table is not None else 0
+    _check(_lib.yrk_rope_append(ctypes.byref(lc), ctypes.byref(pc), q_ptr, hq, q_stride,
+                                k.data_ptr(), v.data_ptr(), T, _ptr(block_table), bt_len,
+                                positions.data_ptr(), _ptr(err), _stream(k)), "yrk_rope_append")
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, max_seq_len, head_dim=HEAD_DIM):

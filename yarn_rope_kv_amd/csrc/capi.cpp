@@ -173,6 +173,53 @@ int yrk_kv_append_quantize(const yrk_kv_layer* layer, const void* k_dev, const v
   return launch_status(yrk::launch_append(a, stream));
 }
 
+int yrk_rope_append(const yrk_kv_layer* layer, const yrk_yarn_params* params, void* q_dev,
+                    int32_t num_q_heads, int64_t q_token_stride, const void* k_dev,
+                    const void* v_dev, int64_t num_tokens, const int32_t* block_table_dev,
+                    int64_t block_table_len, const int32_t* positions_dev,
+                    uint32_t* dev_error_word, hipStream_t stream) {
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  yrk::RopeAppendArgs ra;
+  double inv_freq[yrk::kMaxRotaryHalf];
+  rc = yarn_table(params, inv_freq, &ra.mscale, nullptr, nullptr);
+  if (rc) return rc;
+  if (params->head_dim != yrk::kHeadDim || params->rotary_dim != 2 * yrk::kFusedRopePairs)
+    return YRK_ENOTSUP;
+  if (num_tokens < 0) return YRK_EINVAL;
+  if (layer->paged && (!block_table_dev || block_table_len <= 0)) return YRK_EINVAL;
+  if (q_dev) {
+    if (num_q_heads <= 0 || q_token_stride < (int64_t)num_q_heads * yrk::kHeadDim ||
+        q_token_stride % 4 != 0 || ((uintptr_t)q_dev & 7u) != 0)
+      return YRK_EINVAL;
+  }
+  if (num_tokens == 0) return YRK_OK;
+  if (!k_dev || !v_dev || !positions_dev) return YRK_EINVAL;
+  if (!aligned16(k_dev) || !aligned16(v_dev) || !aligned16(layer->k) || !aligned16(layer->v))
+    return YRK_EINVAL;
+  for (int i = 0; i < yrk::kFusedRopePairs; ++i) ra.inv_freq[i] = inv_freq[i];
+  ra.q = static_cast<uint16_t*>(q_dev);
+  ra.num_q_heads = q_dev ? num_q_heads : 0;
+  ra.q_token_stride = q_dev ? q_token_stride : 0;
+  yrk::AppendArgs& a = ra.ap;
+  a.geo = geometry(layer);
+  a.dtype = layer->dtype;
+  a.k_src = static_cast<const uint16_t*>(k_dev);
+  a.v_src = static_cast<const uint16_t*>(v_dev);
+  a.num_tokens = num_tokens;
+  a.block_table = layer->paged ? block_table_dev : nullptr;
+  a.block_table_len = layer->paged ? block_table_len : 0;
+  a.positions = positions_dev;
+  a.err = dev_error_word;
+  a.k_dst = layer->k;
+  a.v_dst = layer->v;
+  a.k_scale_dst = static_cast<uint8_t*>(layer->k_scale);
+  a.v_scale_dst = static_cast<uint8_t*>(layer->v_scale);
+  a.k_tensor_scale = layer->k_tensor_scale_dev;
+  a.v_tensor_scale = layer->v_tensor_scale_dev;
+  return launch_status(yrk::launch_rope_append(ra, stream));
+}
+
 size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int64_t max_seq_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != yrk::kHeadDim ||

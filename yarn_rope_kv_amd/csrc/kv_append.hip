@@ -11,7 +11,7 @@
 // the memory picture": groups of 64 with 2-byte scales, 16.5 KiB per token
 // per device; its rounding rules are readings (symmetric absmax groups,
 // binary16 scale RNE(amax / 127), codes clamp(RNE(x / s), +-127)).
-#include "device_common.h"
+#include "rope_common.h"
 #include "yrk_internal.h"
 
 namespace yrk {
@@ -101,6 +101,36 @@ __device__ __forceinline__ int e4m3_encode(double q) {
   return (int)keep;  // 0..8; 8 is the smallest normal, code 0x08
 }
 
+// The scale of one 16-element block from its largest magnitude (bf16 bits;
+// |x| orders like the low 15 bits): the e4m3 code and the effective scale
+// e4m3 * S (exact in fp64).
+struct Fp4Block {
+  int qs;
+  double eff;
+};
+__device__ __forceinline__ Fp4Block nvfp4_block(uint32_t bmax_bits, double S) {
+  const double b = (double)bf16_to_f32((uint16_t)bmax_bits);
+  Fp4Block B;
+  B.qs = e4m3_encode(b / (6.0 * S));
+  B.eff = e4m3_value(B.qs) * S;
+  return B;
+}
+
+// Code of one bf16 element: sign bit | nearest e2m1 magnitude of |x| / eff.
+// Decision points between neighbouring e2m1 magnitudes, scaled by eff: at a
+// point exactly between two codes the even code wins (>= where the upper
+// code is even, > where the lower one is).
+__device__ __forceinline__ uint32_t nvfp4_code(uint32_t bits, const Fp4Block& B) {
+  const double a = (double)bf16_to_f32((uint16_t)(bits & 0x7fffu));
+  const double e = B.eff;
+  uint32_t mag = 0;
+  if (e > 0.0)
+    mag = (uint32_t)(a > 0.25 * e) + (uint32_t)(a >= 0.75 * e) + (uint32_t)(a > 1.25 * e) +
+          (uint32_t)(a >= 1.75 * e) + (uint32_t)(a > 2.5 * e) + (uint32_t)(a >= 3.5 * e) +
+          (uint32_t)(a > 5.0 * e);
+  return (((bits >> 15) & 1u) << 3) | mag;
+}
+
 // Quantise 16 bf16 values: returns the scale code and writes 8 packed bytes
 // (element 2j in the low nibble of byte j).
 __device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, double S,
@@ -112,29 +142,16 @@ __device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, d
     bmax = max(bmax, w[i] & 0x7fffu);
     bmax = max(bmax, (w[i] >> 16) & 0x7fffu);
   }
-  const double b = (double)bf16_to_f32((uint16_t)bmax);   // |x| ordering == bit ordering
-  const int qs = e4m3_encode(b / (6.0 * S));
-  const double eff = e4m3_value(qs) * S;                  // exact in fp64
-  // Decision points between neighbouring e2m1 magnitudes, scaled by eff.  At
-  // a point exactly between two codes the even code wins: >= where the upper
-  // code is even, > where the lower one is.
-  const double t0 = 0.25 * eff, t1 = 0.75 * eff, t2 = 1.25 * eff, t3 = 1.75 * eff;
-  const double t4 = 2.5 * eff, t5 = 3.5 * eff, t6 = 5.0 * eff;
+  const Fp4Block B = nvfp4_block(bmax, S);
   uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
-    const double a = (double)bf16_to_f32((uint16_t)(bits & 0x7fffu));
-    uint32_t mag = 0;
-    if (eff > 0.0)
-      mag = (uint32_t)(a > t0) + (uint32_t)(a >= t1) + (uint32_t)(a > t2) + (uint32_t)(a >= t3) +
-            (uint32_t)(a > t4) + (uint32_t)(a >= t5) + (uint32_t)(a > t6);
-    const uint32_t code = ((bits >> 15) << 3) | mag;
-    out[i >> 3] |= code << (4 * (i & 7));
+    out[i >> 3] |= nvfp4_code(bits, B) << (4 * (i & 7));
   }
   packed->x = out[0];
   packed->y = out[1];
-  return (uint32_t)qs;
+  return (uint32_t)B.qs;
 }
 
 // One thread quantises one 16-element block of K and the matching block of V.
@@ -264,6 +281,121 @@ __global__ __launch_bounds__(256) void append_int8_kernel(AppendArgs a) {
   }
 }
 
+// ---- rope fused with append ------------------------------------------------
+//
+// One wave per new token.  Lane l owns elements 4 l .. 4 l + 3 of a head row;
+// the rotary span (elements 0 .. 63) is lanes 0 .. 15 of a row, and element
+// i < 32 pairs with i + 32, held by lane l ^ 8.  Every lane computes the cos
+// and sin of the pairs 4 (l & 7) .. +3 once per token (fp64); they serve the
+// token's query heads (4 heads at a time, one per 16 lanes) and its key
+// heads.  The rotation is the rope kernel's, through the same inline
+// functions, so the roped values are bit-identical to rope followed by
+// append; keys then take the format's own path (copy, NVFP4 or INT8 group-64
+// quantisation, with the quantisers of the plain append) and values are
+// stored or quantised unroped.
+
+// Rotates this lane's 4 elements given its partner's (lane ^ 8) 4 elements.
+__device__ __forceinline__ uint2 rotate4(uint2 own, uint2 partner, bool second_half,
+                                         const double (&c)[4], const double (&sn)[4]) {
+  const uint32_t o[4] = {own.x & 0xffffu, own.x >> 16, own.y & 0xffffu, own.y >> 16};
+  const uint32_t p[4] = {partner.x & 0xffffu, partner.x >> 16, partner.y & 0xffffu,
+                         partner.y >> 16};
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double x = (double)bf16_to_f32((uint16_t)o[j]);
+    const double y = (double)bf16_to_f32((uint16_t)p[j]);
+    r[j] = second_half ? rope_second(y, x, c[j], sn[j]) : rope_first(x, y, c[j], sn[j]);
+  }
+  return make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+}
+
+__device__ __forceinline__ uint2 shfl_xor8(uint2 w) {
+  return make_uint2((uint32_t)__shfl_xor((int)w.x, 8), (uint32_t)__shfl_xor((int)w.y, 8));
+}
+
+// Largest of x over the 4 lanes of a DPP quad (every lane gets it).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false));
+  return x;
+}
+
+// Stores this lane's 4 elements of one cache row in the layer's format.
+template <int FMT>
+__device__ __forceinline__ void store_row4(const AppendArgs& a, bool is_k, int64_t row, int lane,
+                                           uint2 w, double S) {
+  void* dst = is_k ? a.k_dst : a.v_dst;
+  if constexpr (FMT == 0) {
+    reinterpret_cast<uint2*>(dst)[row * (kHeadDim / 4) + lane] = w;
+  } else if constexpr (FMT == 2) {
+    uint32_t sb;
+    const uint32_t codes = quantize_i8x4(w, &sb);
+    reinterpret_cast<uint32_t*>(dst)[row * (kHeadDim / 4) + lane] = codes;
+    if ((lane & 15) == 0)
+      reinterpret_cast<uint16_t*>(is_k ? a.k_scale_dst : a.v_scale_dst)[row * kI8Groups +
+                                                                        (lane >> 4)] =
+          (uint16_t)sb;
+  } else {
+    // a 16-element block is the 4 lanes of a DPP quad
+    const uint32_t e[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, e[i] & 0x7fffu);
+    const Fp4Block B = nvfp4_block(quad_max_u32(m), S);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= nvfp4_code(e[i], B) << (4 * i);
+    reinterpret_cast<uint16_t*>(dst)[row * (kHeadDim / 4) + lane] = (uint16_t)packed;
+    if ((lane & 3) == 0)
+      (is_k ? a.k_scale_dst : a.v_scale_dst)[row * kQBlocks + (lane >> 2)] = (uint8_t)B.qs;
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
+  const AppendArgs& a = ra.ap;
+  const int H = a.geo.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const bool second = (lane & 8) != 0;
+  double kS = 1.0, vS = 1.0;
+  if constexpr (FMT == 1) {
+    kS = (double)*a.k_tensor_scale;
+    vS = (double)*a.v_tensor_scale;
+  }
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < a.num_tokens;
+       t += wstride) {
+    const int32_t pos = a.positions[t];
+    double c[4], sn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      rope_cos_sin(pos, ra.inv_freq[4 * (lane & 7) + j], ra.mscale, &c[j], &sn[j]);
+    if (ra.q) {
+      for (int h0 = 0; h0 < ra.num_q_heads; h0 += 4) {
+        const int h = h0 + (lane >> 4);
+        const int hl = h < ra.num_q_heads ? h : ra.num_q_heads - 1;   // every lane shuffles
+        uint2* p = reinterpret_cast<uint2*>(ra.q + t * ra.q_token_stride +
+                                            (int64_t)hl * kHeadDim) + (lane & 15);
+        const uint2 w = *p;
+        const uint2 r = rotate4(w, shfl_xor8(w), second, c, sn);
+        if (h < ra.num_q_heads) *p = r;
+      }
+    }
+    for (int h = 0; h < H; ++h) {
+      const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, pos, h, a.err,
+                                    lane == 0);
+      if (row < 0) continue;
+      const int64_t src = (t * H + h) * (kHeadDim / 4) + lane;
+      const uint2 kw = reinterpret_cast<const uint2*>(a.k_src)[src];
+      const uint2 vw = reinterpret_cast<const uint2*>(a.v_src)[src];
+      const uint2 kr = rotate4(kw, shfl_xor8(kw), second, c, sn);
+      store_row4<FMT>(a, true, row, lane, lane < 16 ? kr : kw, kS);
+      store_row4<FMT>(a, false, row, lane, vw, vS);
+    }
+  }
+}
+
 // ---- tensor scale ----------------------------------------------------------
 
 __global__ void store_word_kernel(uint32_t* p, uint32_t v) {
@@ -325,6 +457,14 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   }
   const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
   return launch(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+}
+
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
+  if (a.ap.num_tokens == 0) return hipSuccess;
+  const dim3 grid(grid_for(a.ap.num_tokens * 64, 1 << 18));   // one wave per token
+  if (a.ap.dtype == 0) return launch(rope_append_kernel<0>, grid, dim3(256), 0, s, a);
+  if (a.ap.dtype == 2) return launch(rope_append_kernel<2>, grid, dim3(256), 0, s, a);
+  return launch(rope_append_kernel<1>, grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s) {

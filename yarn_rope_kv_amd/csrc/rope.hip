@@ -16,7 +16,7 @@
 // (write); the pass-through dimensions are never read.  Lanes of a wave take
 // consecutive pairs of one token, so the two 64-byte halves of the rotary
 // slice are each read by 32 adjacent lanes.
-#include "device_common.h"
+#include "rope_common.h"
 #include "yrk_internal.h"
 
 namespace yrk {
@@ -39,20 +39,15 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeKernelArgs a) {
   for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < a.total; gid += stride) {
     const int64_t t = gid / a.half;
     const int i = (int)(gid - t * a.half);
-    const double angle = (double)a.positions[t] * a.inv_freq[i];
-    double sn, cs;
-    sincos(angle, &sn, &cs);
-    const double c = a.mscale * cs;
-    const double s = a.mscale * sn;
+    double c, s;
+    rope_cos_sin(a.positions[t], a.inv_freq[i], a.mscale, &c, &s);
     uint16_t* row = a.x + t * a.token_stride + i;
     for (int h = 0; h < a.num_heads; ++h) {
       uint16_t* p = row + (int64_t)h * a.head_dim;
       const double x1 = (double)bf16_to_f32(p[0]);
       const double x2 = (double)bf16_to_f32(p[a.half]);
-      const double y1 = x1 * c - x2 * s;
-      const double y2 = x2 * c + x1 * s;
-      p[0] = f64_to_bf16(y1);
-      p[a.half] = f64_to_bf16(y2);
+      p[0] = rope_first(x1, x2, c, s);
+      p[a.half] = rope_second(x1, x2, c, s);
     }
   }
 }

@@ -13,8 +13,9 @@
 // two products are dense enough for the matrix cores:
 //
 //   grid      (split, kv_head, seq), 4 waves; a split owns a contiguous token
-//             range and wave w takes its pages w, w + 4, ... (16 tokens each),
-//             with the next page's loads in flight while one is computed.
+//             range and wave w takes its pages w, w + 4, ... (16 tokens each);
+//             where registers allow, the next page's loads are in flight while
+//             one is computed.
 //   S^T       = K Q^T on v_mfma_f32_16x16x32_bf16, one 16-row column block of
 //             Q at a time (C = ceil(R / 16) blocks).  Lane (t, kg) loads 16
 //             bytes of key row t per step (head dims 32 j + 8 kg .. +7; every
@@ -70,6 +71,17 @@ __device__ __forceinline__ u32x4_t split_weights(const float (&p)[4]) {
   return u32x4_t{h01, h23, l01, l23};
 }
 
+// Per column-block count C: pages a wave keeps in flight beyond the one it
+// computes, and workgroups resident per CU (which the registers allow).  Two
+// waves per SIMD matter more than a deeper register ring (measured at 4
+// queries, 1M tokens: 0.755 ms with two workgroups per CU and no ring
+// against 0.815 ms with one workgroup and one page ahead); three column
+// blocks hold 192 accumulator registers and leave room for one workgroup.
+template <int C> struct VerifyTune;
+template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWgsPerCu = 2; };
+template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWgsPerCu = 2; };
+template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWgsPerCu = 1; };
+
 // One lane's share of one page: 16-byte chunks 4 j + kg of key and value
 // row t (head dims 32 j + 8 kg .. +7).
 struct VUnit {
@@ -77,9 +89,11 @@ struct VUnit {
   bool ok;                  // page present and inside the split
 };
 
-template <int C, int AHEAD>
-__global__ __launch_bounds__(kThreads, (C == 1 ? 2 : 1)) void verify_split_bf16(VerifyArgs va) {
-  static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 1, "verify kernel shape");
+template <int C>
+__global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_split_bf16(
+    VerifyArgs va) {
+  constexpr int AHEAD = VerifyTune<C>::kAhead;
+  static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
   const DecodeArgs& a = va.d;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -293,12 +307,19 @@ __global__ __launch_bounds__(kThreads, (C == 1 ? 2 : 1)) void verify_split_bf16(
 
 int column_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
+int wgs_per_cu(int rows) {
+  switch (column_blocks(rows)) {
+    case 1: return VerifyTune<1>::kWgsPerCu;
+    case 2: return VerifyTune<2>::kWgsPerCu;
+    default: return VerifyTune<3>::kWgsPerCu;
+  }
+}
+
 }  // namespace
 
-// One round of workgroups: two per CU where a column block's accumulators
-// leave room for a second workgroup, else one.
+// One round of workgroups over the 256 CUs.
 DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len) {
-  const int64_t target_wgs = column_blocks(rows) == 1 ? 512 : 256;
+  const int64_t target_wgs = 256 * wgs_per_cu(rows);
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   const int64_t chunks = (max_seq_len + unit - 1) / unit;
@@ -319,9 +340,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const dim3 grid(d.plan.num_splits, d.geo.num_kv_heads, d.num_seqs);
   hipError_t e;
   switch (column_blocks(rows)) {
-    case 1: e = launch(verify_split_bf16<1, 1>, grid, dim3(kThreads), 0, st, a); break;
-    case 2: e = launch(verify_split_bf16<2, 1>, grid, dim3(kThreads), 0, st, a); break;
-    case 3: e = launch(verify_split_bf16<3, 1>, grid, dim3(kThreads), 0, st, a); break;
+    case 1: e = launch(verify_split_bf16<1>, grid, dim3(kThreads), 0, st, a); break;
+    case 2: e = launch(verify_split_bf16<2>, grid, dim3(kThreads), 0, st, a); break;
+    case 3: e = launch(verify_split_bf16<3>, grid, dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

@@ -55,6 +55,19 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// Rope and append in one pass: the new tokens' queries are roped in place
+// and their keys roped on the way into the cache (rotary_dim 64 of 256).
+constexpr int kFusedRopePairs = 32;
+struct RopeAppendArgs {
+  AppendArgs ap;             // ap.k_src holds the keys before rope
+  uint16_t* q;               // nullable: [num_tokens] rows of num_q_heads heads, roped in place
+  int32_t num_q_heads;
+  int64_t q_token_stride;    // elements
+  double mscale;
+  double inv_freq[kFusedRopePairs];
+};
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
+
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s);
 
 struct DecodePlan {
