@@ -39,10 +39,11 @@ def measured_traffic(record):
     path = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+        sources = rec.get("kernel_sources") or [[rec["kernel_source"], rec["kernel_source_sha256"]]]
+        for src, sha in sources:
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+                return None
     except (OSError, ValueError, KeyError):
-        return None
-    if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
         return None
     return 1024.0 * (rec["fetch_kib_per_call"] * rec["fetch_scale"] +
                      rec["write_kib_per_call"] * rec["write_scale"])

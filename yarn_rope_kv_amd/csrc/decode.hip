@@ -862,15 +862,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
 
 // ---- merge ------------------------------------------------------------------
 
-// Grid (4 x q_head, seq), 256 threads: a workgroup owns 64 head dims of one
-// (sequence, query head); its 4 waves each walk every 4th split, and the 4
-// partial (max, sum, weighted output) triples are combined through LDS:
+// Grid (4 x q_head, seq), 1024 threads: a workgroup owns 64 head dims of one
+// (sequence, query head); its 16 waves each walk every 16th split (the walk
+// is serial within a wave, so more waves shorten it: measured 2% on a
+// whole decode call at 12 q / 2 KV heads, whose 256 splits made the merge
+// 15 us long), and the 16 partial (max, sum, weighted output) triples are
+// combined through LDS:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // Splits that saw no token carry lse = -inf and weigh nothing.
-constexpr int kMergeGroups = 4;
+constexpr int kMergeGroups = 16;
 constexpr int kMergeDims = kHeadDim / 4;
 
-__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMergeGroups) void decode_merge(DecodeArgs a) {
   __shared__ float sm_m[kMergeGroups], sm_l[kMergeGroups];
   __shared__ float sm_o[kMergeGroups][kMergeDims];
   const int qh = blockIdx.x >> 2, chunk = blockIdx.x & 3, s = blockIdx.y;
@@ -989,7 +992,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st) {
-  return launch(decode_merge, dim3(4 * a.num_q_heads, a.num_seqs), dim3(256), 0, st, a);
+  return launch(decode_merge, dim3(4 * a.num_q_heads, a.num_seqs), dim3(64 * kMergeGroups), 0,
+                st, a);
 }
 
 }  // namespace yrk
