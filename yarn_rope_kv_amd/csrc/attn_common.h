@@ -35,10 +35,15 @@ __device__ __forceinline__ uint32_t err_flag(uint32_t* err, uint32_t bit) {
 __device__ __forceinline__ bool page_base(const DecodeArgs& a, int s, int g, int64_t page,
                                           int64_t row_elems, int64_t* base, int64_t* tstride) {
   if (a.geo.paged) {
-    // one table entry for the whole wave: make that explicit, so the page
-    // test below is a scalar branch and not a per-lane one
+    // one table entry for the whole wave, read through the constant address
+    // space so that it is a scalar load: a vector load here would be waited
+    // for with the vector-load counter, which retires in order, so every K/V
+    // load still in flight (the pages prefetched for later steps) would be
+    // waited for too.  The table is not written while a kernel runs.
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const const_i32* table = (const const_i32*)(const void*)a.block_tables;
     const int64_t blk = __builtin_amdgcn_readfirstlane(
-        a.block_tables[(int64_t)s * a.block_table_stride + page]);
+        table[(int64_t)s * a.block_table_stride + page]);
     if (blk < 0 || blk >= a.geo.num_blocks) return false;
     *base = ((blk * a.geo.num_kv_heads + g) * kBlockSize) * row_elems;
     *tstride = row_elems;
