@@ -175,28 +175,41 @@ def time_steps(step, ev, steps, warmup, torch):
     return wall, sum(kern_ms) / len(kern_ms)
 
 
-def cpu_baseline(W, w):
-    """The oracle timed on one of the 16 layers (all 1,048,576 tokens, 24
-    query heads); inputs are prepared outside the timed call."""
+def cpu_baseline(W, w, min_seconds=10.0):
+    """The oracle timed on whole layers of the decode workload (all 1,048,576
+    tokens, 24 query heads, the planted needle), one layer after another
+    until at least min_seconds of oracle time; inputs are prepared outside
+    the timed calls."""
     import numpy as np
     import oracle as O
     import synth
 
     N = w.n_ctx
     t = O.yarn_table(original_max_position=w.orig)
-    q = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.Q), 0, 1, 24, 256), [N], t,
-               bf16_out=True)[0]
-    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, 4, 256),
-               np.arange(N), t, bf16_out=True)
-    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, 4, 256)
-    qf = O.bf16_to_f64(q)
-    t0 = time.perf_counter()
-    O.decode_attention(qf, k, v)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": N / dt, "unit": "KV token-layers/s", "cores": cores, "kind": "oracle",
-            "sample": f"1 of 16 layers of the long workload: {N} cached tokens x 24 q heads, "
-                      f"fp64, {dt:.2f} s"}
+    total, done = 0.0, 0
+    for u in range(w.layers):
+        q = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256), [N], t,
+                   bf16_out=True)[0]
+        k = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.K), 0, N, w.hkv, 256),
+                   np.arange(N), t, bf16_out=True)
+        v = synth.host_fill(w.seed, synth.stream_id(u, synth.V), 0, N, w.hkv, 256)
+        if w.needle:
+            p_star = synth.needle_position(w.seed, u, N)
+            for g in range(w.hkv):
+                k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
+        qf = O.bf16_to_f64(q)
+        t0 = time.perf_counter()
+        O.decode_attention(qf, k, v)
+        total += time.perf_counter() - t0
+        done += 1
+        del k, v
+        if total >= min_seconds:
+            break
+    cores = O.num_threads()
+    return {"value": done * N / total, "unit": "KV token-layers/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {w.layers} layers of the long workload: {N} cached tokens x "
+                      f"{w.hq} q heads each, fp64, {total:.2f} s"}
 
 
 def bench_prefill(W, Y, torch, dev, reps, name="prefill"):

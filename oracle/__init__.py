@@ -52,6 +52,7 @@ def lib():
                                   _p, _p], _i32),
         "orc_prefill_attention": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _f, _f,
                                    _d, _p], _i32),
+        "orc_num_threads": ([], _i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -250,6 +251,11 @@ def prefill_attention(q, positions, k, v, scale=None, nvfp4=None, int8=None):
     if rc:
         raise ValueError("bad prefill_attention arguments")
     return out
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(lib().orc_num_threads())
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_element, batch=1):

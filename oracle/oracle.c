@@ -24,6 +24,7 @@
  * Precision: fp64 throughout, compiled without fast-math or FMA contraction.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -604,3 +605,7 @@ int orc_prefill_attention(const double *q, const int64_t *pos, int64_t R, int Hq
     }
     return 0;
 }
+
+/* Threads an OpenMP loop of this library runs on (reported next to timings;
+ * no arithmetic depends on it). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
