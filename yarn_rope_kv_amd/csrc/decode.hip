@@ -648,7 +648,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
-constexpr int kAheadI8 = 1;                                        // steps in flight
+// Steps in flight beyond the one computed.  The kernel waits on memory far
+// more than it computes (a page is ~380 vector instructions and 25 MFMAs),
+// so the registers go to a deeper ring: the Q^T operands live in LDS (read
+// at every step) instead of 32 registers, and each lane loads only its own
+// row's group scales and fetches the 4 rows it needs from their lanes
+// (ds_bpermute) when it computes, 4 registers per step instead of 16.
+// Measured per 1M-token layer: 0.443 ms with one step ahead, 0.407 ms with
+// two (243 registers, no spills).
+constexpr int kAheadI8 = 2;
+constexpr bool kQOpLdsI8 = true;
+constexpr bool kScaleOwnRowI8 = true;
+constexpr int kScaleRowsI8 = kScaleOwnRowI8 ? 1 : 4;
+constexpr int kQOpBytesI8 = kQOpLdsI8 ? 8 * 64 * 16 : 0;
 
 __device__ __forceinline__ floatx4_t mfma_f16_k16(const uint2& a, const uint2& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
@@ -671,7 +683,8 @@ __device__ __forceinline__ uint4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
 struct I8Unit {
   u32x2_t kc[8];            // K: step j's 8 code bytes of row t (dims of group j / 2)
   u32x4_t vc[4];            // V: code bytes [64 kg, 64 kg + 64) of row t
-  u32x2_t ks[4], vs[4];     // binary16 scales (4 groups) of rows 4 kg .. 4 kg + 3
+  u32x2_t ks[kScaleRowsI8], vs[kScaleRowsI8];   // binary16 scales (4 groups) of rows
+                            // 4 kg .. 4 kg + 3, or of row t alone
   bool ok;                  // page present and inside the split
 };
 
@@ -680,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
   static_assert((kWaves * G * kHeadDim + 2 * kWaves * G) * 4 <= kStageBytesI8,
                 "split combine reuses the staging buffer");
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytesI8];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytesI8 + kQOpBytesI8];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -704,6 +717,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
   if (tok1 > tok0) {
     uint4 qop[8];   // step j = 2 g + j2: dims 64 g + 32 j2 + 8 hi .. +7 of head lo
     const float c = a.scale_log2 * load_q_f16<G>(a, s, g, lo, hi, qop, true);
+    uint4* qlds = reinterpret_cast<uint4*>(stage + kStageBytesI8);   // [step][lane]
+    if constexpr (kQOpLdsI8) {   // tok1 > tok0 is the same for the whole workgroup
+      if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qlds[j * 64 + lane] = qop[j];
+      }
+      __syncthreads();
+    }
 
     const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
     const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
@@ -723,12 +744,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       U.ok = ok;
       const u32x2_t z2 = {0u, 0u};
       const u32x4_t z4 = {0u, 0u, 0u, 0u};
-      u32x2_t kc[8], ks[4], vs[4];
+      u32x2_t kc[8], ks[kScaleRowsI8], vs[kScaleRowsI8];
       u32x4_t vc[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j) kc[j] = z2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { vc[i] = z4; ks[i] = z2; vs[i] = z2; }
+      for (int i = 0; i < 4; ++i) vc[i] = z4;
+#pragma unroll
+      for (int e = 0; e < kScaleRowsI8; ++e) { ks[e] = z2; vs[e] = z2; }
       if (ok) {
         const int64_t row = base + lo * ts;
         const uint8_t* kp = Kc + row * kHeadDim + 8 * hi;
@@ -739,8 +762,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) vc[i] = vp[i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t srow = base + (4 * hi + e) * ts;
+        for (int e = 0; e < kScaleRowsI8; ++e) {
+          const int64_t srow = kScaleOwnRowI8 ? row : base + (4 * hi + e) * ts;
           ks[e] = *reinterpret_cast<const u32x2_t*>(Ks + srow * (kHeadDim / 64));
           vs[e] = *reinterpret_cast<const u32x2_t*>(Vs + srow * (kHeadDim / 64));
         }
@@ -748,7 +771,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) U.kc[j] = kc[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { U.vc[i] = vc[i]; U.ks[i] = ks[i]; U.vs[i] = vs[i]; }
+      for (int i = 0; i < 4; ++i) U.vc[i] = vc[i];
+#pragma unroll
+      for (int e = 0; e < kScaleRowsI8; ++e) { U.ks[e] = ks[e]; U.vs[e] = vs[e]; }
     };
 
     const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
@@ -763,10 +788,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ke = 4 * hi + e < nv;
+        for (int e = 0; e < kScaleRowsI8; ++e) {
+          const bool ke = (kScaleOwnRowI8 ? lo : 4 * hi + e) < nv;
           U.vs[e] = ke ? U.vs[e] : u32x2_t{0u, 0u};
           U.ks[e] = ke ? U.ks[e] : u32x2_t{0u, 0u};
+        }
+      }
+      // the group scales of rows 4 hi .. 4 hi + 3 (row r's are in lane r)
+      u32x2_t ksr[4], vsr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kScaleOwnRowI8) {
+          const int src = 4 * (4 * hi + e);
+          ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks[0].x),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks[0].y)};
+          vsr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs[0].x),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs[0].y)};
+        } else {
+          ksr[e] = U.ks[e];
+          vsr[e] = U.vs[e];
         }
       }
       // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
@@ -783,14 +823,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        tg[j >> 1] = mfma_f16(i8x8_to_f16(U.kc[j][0], U.kc[j][1]), qop[j], tg[j >> 1]);
+        tg[j >> 1] = mfma_f16(i8x8_to_f16(U.kc[j][0], U.kc[j][1]),
+                              kQOpLdsI8 ? qlds[j * 64 + lane] : qop[j], tg[j >> 1]);
       float x[4];
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // copy the vector elements out first: a bit cast of a vector element
         // lvalue reads the vector's first element whatever the index
-        const uint32_t w01 = U.ks[e].x, w23 = U.ks[e].y;
+        const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;
         const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
         const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
         float v = tg[0][e] * (float)s01[0];
@@ -824,8 +865,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         for (int gg = 0; gg < 4; ++gg) {
           const int dw = gg >> 1;
           const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
-          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(U.vs[1][dw], U.vs[0][dw], sel));
-          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(U.vs[3][dw], U.vs[2][dw], sel));
+          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel));
+          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[3][dw], vsr[2][dw], sel));
           pg[gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
                               __builtin_bit_cast(uint32_t, p23 * s23));
         }
