@@ -240,6 +240,73 @@ def bench_prefill(W, Y, torch, dev, reps, name="prefill"):
                          "traffic": measured_traffic(record) if record else None}}
 
 
+def bench_append(W, Y, torch, dev, reps=3):
+    """Filling one 1,048,576-token layer (4 KV heads, paged over a seeded
+    permutation): the bf16 copy, the NVFP4 and INT8 quantisers (the NVFP4
+    tensor scale included), the plain rope of the keys, and the fused rope +
+    append.  Algorithmic bytes: the bf16 keys and values read (4 KiB per
+    token) plus what the cache format writes per token (the rope alone
+    reads and writes the 64 rotary dims of each key head)."""
+    w = W.WORKLOADS["long"]
+    N = w.n_ctx
+    k = torch.empty((N, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    W.gen_kv(w, 0, 1, N, k)
+    W.gen_kv(w, 0, 2, N, v)
+    pos = torch.arange(N, dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(W.page_table(w, 0)[0]).to(dev)
+    yp = w.yarn()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    read = 2 * w.hkv * 256 * 2 * N
+    for name, kv, written in (("bf16_copy", Y.KV_BF16, 2 * w.hkv * 512),
+                              ("nvfp4_quantize", Y.KV_NVFP4, 2 * w.hkv * 144),
+                              ("int8_quantize", Y.KV_INT8, 2 * w.hkv * 264)):
+        L = Y.KVLayer.allocate(kv, w.hkv, w.pages_per_seq, paged=True, device=dev)
+        if kv == Y.KV_NVFP4:
+            def fn():
+                Y.nvfp4_tensor_scale(k, L.k_tensor_scale)
+                Y.nvfp4_tensor_scale(v, L.v_tensor_scale)
+                Y.kv_append_quantize(L, k, v, bt, pos)
+            extra = read                      # the two amax passes read k and v again
+        else:
+            def fn():
+                Y.kv_append_quantize(L, k, v, bt, pos)
+            extra = 0
+        ms = timed(fn)
+        b = read + extra + written * N
+        out[name] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
+                     "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if kv == Y.KV_BF16:
+            ms = timed(lambda: Y.rope_append(L, yp, None, k, v, bt, pos))
+            b = read + written * N
+            out["bf16_rope_append_fused"] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
+                                             "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del L
+        torch.cuda.empty_cache()
+    kr = k.clone()
+    ms = timed(lambda: Y.yarn_rope_apply(yp, kr, pos))
+    b = 2 * w.hkv * 128 * N
+    out["rope_keys"] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
+                        "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["workload"] = ("one layer: 1,048,576 tokens x 4 KV heads x 256 (bf16 K and V in HBM), "
+                       "paged over a seeded permutation of 65,536 pages")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +317,7 @@ def main():
     ap.add_argument("--no-nvfp4", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-tp2", action="store_true",
                     help="skip one card's share of a two-way KV-head split (12 q / 2 KV heads)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,6 +412,10 @@ def main():
                          "traffic": measured_traffic("decode_split_int8_long_int8_1m.json"),
                          "bytes_per_launch": bpli}}
         del li, stepi, evi
+        torch.cuda.empty_cache()
+    if not args.no_append:
+        log("append and rope over one 1M-token layer")
+        result["append"] = bench_append(W, Y, torch, dev)
         torch.cuda.empty_cache()
     if not args.no_prefill:
         log("prefill")

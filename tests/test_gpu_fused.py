@@ -28,16 +28,16 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def _case(seed, T, paged):
-    """T tokens: raw q [T, 24, 256], k, v [T, 4, 256] (1% x20 outliers in k
+def _case(seed, T, paged, hq=24, hkv=4):
+    """T tokens: raw q [T, hq, 256], k, v [T, hkv, 256] (1% x20 outliers in k
     and v), distinct positions, and for the paged layout a block table that
     gives each token's page its own block (so positions can reach 2^20 with
     a pool of T blocks)."""
     rng = np.random.default_rng(seed)
-    q = synth.host_fill(seed, synth.Q, 0, T, 24, 256)
-    k = synth.host_fill(seed, synth.K, 0, T, 4, 256, outlier_stream=synth.K_OUTLIER,
+    q = synth.host_fill(seed, synth.Q, 0, T, hq, 256)
+    k = synth.host_fill(seed, synth.K, 0, T, hkv, 256, outlier_stream=synth.K_OUTLIER,
                         outlier_p=0.01, outlier_mul=20.0)
-    v = synth.host_fill(seed, synth.V, 0, T, 4, 256, outlier_stream=synth.V_OUTLIER,
+    v = synth.host_fill(seed, synth.V, 0, T, hkv, 256, outlier_stream=synth.V_OUTLIER,
                         outlier_p=0.01, outlier_mul=20.0)
     if paged:
         # the first and last positions of the original window and of 2^20,
@@ -57,18 +57,18 @@ def _case(seed, T, paged):
     return q, k, v, pos.astype(np.int64), table, blocks
 
 
-def _pool_rows(pool_bytes, table, pos, row_bytes, blocks):
-    """Rows [T, 4, row_bytes] of a cache plane at the tokens' positions."""
+def _pool_rows(pool_bytes, table, pos, row_bytes, blocks, hkv=4):
+    """Rows [T, hkv, row_bytes] of a cache plane at the tokens' positions."""
     a = pool_bytes.reshape(-1)
     if table is None:
-        return a.reshape(blocks * 16, 4, row_bytes)[pos]
+        return a.reshape(blocks * 16, hkv, row_bytes)[pos]
     blk = table[pos // 16]
     slot = pos % 16
-    return a.reshape(blocks, 4, 16, row_bytes)[blk, :, slot]
+    return a.reshape(blocks, hkv, 16, row_bytes)[blk, :, slot]
 
 
-def _layer(Y, kv, blocks, paged, kS=None, vS=None):
-    L = Y.KVLayer.allocate(kv, 4, blocks, paged=paged, device=DEV)
+def _layer(Y, kv, blocks, paged, kS=None, vS=None, hkv=4):
+    L = Y.KVLayer.allocate(kv, hkv, blocks, paged=paged, device=DEV)
     for t in (L.k, L.v) + ((L.k_scale, L.v_scale) if L.k_scale is not None else ()):
         t.zero_()
     if kv == Y.KV_NVFP4:
@@ -77,20 +77,23 @@ def _layer(Y, kv, blocks, paged, kS=None, vS=None):
     return L
 
 
-@pytest.mark.parametrize("paged", [True, False])
+@pytest.mark.parametrize("paged,hq,hkv", [(True, 24, 4), (False, 24, 4), (True, 12, 2),
+                                          (True, 6, 1)])
 @pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
-def test_rope_append_matches_oracle(Y, fmt, paged):
+def test_rope_append_matches_oracle(Y, fmt, paged, hq, hkv):
+    """Also one card's 12 q / 2 KV-head share and a single KV head, whose
+    rows put rotary and pass-through groups in the same pass."""
     kv = _FMT[fmt]
     T = 300
-    _say(f"rope_append {fmt} paged={paged}")
-    q, k, v, pos, table, blocks = _case(1200 + kv + 10 * paged, T, paged)
+    _say(f"rope_append {fmt} paged={paged} {hq}x{hkv}")
+    q, k, v, pos, table, blocks = _case(1200 + kv + 10 * paged + hkv, T, paged, hq, hkv)
     t = O.yarn_table()
     q_ref = O.rope(q, pos, t, bf16_out=True)
     k_ref = O.rope(k, pos, t, bf16_out=True)
     kS = vS = None
     if kv == Y.KV_NVFP4:
         kS, vS = O.nvfp4_tensor_scale(k_ref), O.nvfp4_tensor_scale(v)
-    L = _layer(Y, kv, blocks, paged, kS, vS)
+    L = _layer(Y, kv, blocks, paged, kS, vS, hkv)
     qd = _dev(q)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     Y.rope_append(L, Y.YarnParams(), qd, _dev(k), _dev(v),
@@ -104,8 +107,8 @@ def test_rope_append_matches_oracle(Y, fmt, paged):
     assert np.all(np.abs(got_q.astype(np.int32) - q_ref.astype(np.int32))[diff] <= 1)
     assert diff.sum() <= max(1, diff.size // 100000)
     if kv == Y.KV_BF16:
-        gk = _pool_rows(_bits(L.k).view(np.uint8), table, pos, 512, blocks).view(np.uint16)
-        gv = _pool_rows(_bits(L.v).view(np.uint8), table, pos, 512, blocks).view(np.uint16)
+        gk = _pool_rows(_bits(L.k).view(np.uint8), table, pos, 512, blocks, hkv).view(np.uint16)
+        gv = _pool_rows(_bits(L.v).view(np.uint8), table, pos, 512, blocks, hkv).view(np.uint16)
         assert np.array_equal(gk.reshape(k_ref.shape), k_ref)
         assert np.array_equal(gv.reshape(v.shape), v)
         return
@@ -114,14 +117,14 @@ def test_rope_append_matches_oracle(Y, fmt, paged):
         sb = scales_t.cpu().numpy().view(np.uint8)
         if kv == Y.KV_NVFP4:
             c_ref, s_ref = O.nvfp4_quantize(raw, S)
-            gc = _pool_rows(cb, table, pos, 128, blocks)
-            gs = _pool_rows(sb, table, pos, 16, blocks)
+            gc = _pool_rows(cb, table, pos, 128, blocks, hkv)
+            gs = _pool_rows(sb, table, pos, 16, blocks, hkv)
             assert np.array_equal(gs.reshape(s_ref.shape), s_ref)
             assert np.array_equal(gc.reshape(-1), O.nvfp4_pack(c_ref).reshape(-1))
         else:
             c_ref, s_ref = O.int8_quantize(raw)
-            gc = _pool_rows(cb, table, pos, 256, blocks)
-            gs = _pool_rows(sb, table, pos, 8, blocks)
+            gc = _pool_rows(cb, table, pos, 256, blocks, hkv)
+            gs = _pool_rows(sb, table, pos, 8, blocks, hkv)
             assert np.array_equal(gs.reshape(-1).view(np.uint16).reshape(s_ref.shape), s_ref)
             assert np.array_equal(gc.reshape(-1).view(np.int8).reshape(c_ref.shape), c_ref)
 

@@ -283,16 +283,20 @@ __global__ __launch_bounds__(256) void append_int8_kernel(AppendArgs a) {
 
 // ---- rope fused with append ------------------------------------------------
 //
-// One wave per new token.  Lane l owns elements 4 l .. 4 l + 3 of a head row;
-// the rotary span (elements 0 .. 63) is lanes 0 .. 15 of a row, and element
-// i < 32 pairs with i + 32, held by lane l ^ 8.  Every lane computes the cos
-// and sin of the pairs 4 (l & 7) .. +3 once per token (fp64); they serve the
-// token's query heads (4 heads at a time, one per 16 lanes) and its key
-// heads.  The rotation is the rope kernel's, through the same inline
-// functions, so the roped values are bit-identical to rope followed by
-// append; keys then take the format's own path (copy, NVFP4 or INT8 group-64
-// quantisation, with the quantisers of the plain append) and values are
-// stored or quantised unroped.
+// One wave per new token.  Work comes in 64-element groups of a head row,
+// one group per 16 lanes (lane l owns elements 4 (l % 16) .. +3 of it), so a
+// 16-lane DPP row is an INT8 scale group and a 4-lane quad an NVFP4 block.
+// The rotary span is group 0; its element i < 32 pairs with i + 32, held by
+// lane l ^ 8.  Groups are taken group-major (all heads' group 0 first), so a
+// pass of 4 groups is all rotary or all pass-through (with up to 4 heads)
+// and the fp64 rotation runs only where it is needed.  Lane l computes the
+// cos and sin of pair l % 32 once per token (fp64) and fetches those of its
+// pairs 4 (l & 7) .. +3 from their lanes; they serve the token's query heads
+// (4 heads at a time, all rotary) and its key heads.  The rotation is the
+// rope kernel's, through the same inline functions, so the roped values are
+// bit-identical to rope followed by append; keys then take the format's own
+// path (copy, NVFP4 or INT8 group-64 quantisation, with the quantisers of the
+// plain append) and values are stored or quantised unroped.
 
 // Rotates this lane's 4 elements given its partner's (lane ^ 8) 4 elements.
 __device__ __forceinline__ uint2 rotate4(uint2 own, uint2 partner, bool second_half,
@@ -310,6 +314,14 @@ __device__ __forceinline__ uint2 rotate4(uint2 own, uint2 partner, bool second_h
   return make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
 }
 
+// The double held by lane src (byte address 4 src) of the wave.
+__device__ __forceinline__ double bpermute_f64(int src, double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ uint2 shfl_xor8(uint2 w) {
   return make_uint2((uint32_t)__shfl_xor((int)w.x, 8), (uint32_t)__shfl_xor((int)w.y, 8));
 }
@@ -321,20 +333,22 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
   return x;
 }
 
-// Stores this lane's 4 elements of one cache row in the layer's format.
+// Stores this lane's 4 elements (elements 4 c .. 4 c + 3 of a cache row) in
+// the layer's format.  The 16 lanes that share a DPP row hold one 64-element
+// group, the 4 lanes of a quad one 16-element block.
 template <int FMT>
-__device__ __forceinline__ void store_row4(const AppendArgs& a, bool is_k, int64_t row, int lane,
+__device__ __forceinline__ void store_row4(const AppendArgs& a, bool is_k, int64_t row, int c,
                                            uint2 w, double S) {
   void* dst = is_k ? a.k_dst : a.v_dst;
   if constexpr (FMT == 0) {
-    reinterpret_cast<uint2*>(dst)[row * (kHeadDim / 4) + lane] = w;
+    reinterpret_cast<uint2*>(dst)[row * (kHeadDim / 4) + c] = w;
   } else if constexpr (FMT == 2) {
     uint32_t sb;
     const uint32_t codes = quantize_i8x4(w, &sb);
-    reinterpret_cast<uint32_t*>(dst)[row * (kHeadDim / 4) + lane] = codes;
-    if ((lane & 15) == 0)
+    reinterpret_cast<uint32_t*>(dst)[row * (kHeadDim / 4) + c] = codes;
+    if ((c & 15) == 0)
       reinterpret_cast<uint16_t*>(is_k ? a.k_scale_dst : a.v_scale_dst)[row * kI8Groups +
-                                                                        (lane >> 4)] =
+                                                                        (c >> 4)] =
           (uint16_t)sb;
   } else {
     // a 16-element block is the 4 lanes of a DPP quad
@@ -346,9 +360,9 @@ __device__ __forceinline__ void store_row4(const AppendArgs& a, bool is_k, int64
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed |= nvfp4_code(e[i], B) << (4 * i);
-    reinterpret_cast<uint16_t*>(dst)[row * (kHeadDim / 4) + lane] = (uint16_t)packed;
-    if ((lane & 3) == 0)
-      (is_k ? a.k_scale_dst : a.v_scale_dst)[row * kQBlocks + (lane >> 2)] = (uint8_t)B.qs;
+    reinterpret_cast<uint16_t*>(dst)[row * (kHeadDim / 4) + c] = (uint16_t)packed;
+    if ((c & 3) == 0)
+      (is_k ? a.k_scale_dst : a.v_scale_dst)[row * kQBlocks + (c >> 2)] = (uint8_t)B.qs;
   }
 }
 
@@ -367,10 +381,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
   for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < a.num_tokens;
        t += wstride) {
     const int32_t pos = a.positions[t];
+    double cl, sl;
+    rope_cos_sin(pos, ra.inv_freq[lane & 31], ra.mscale, &cl, &sl);
     double c[4], sn[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      rope_cos_sin(pos, ra.inv_freq[4 * (lane & 7) + j], ra.mscale, &c[j], &sn[j]);
+    for (int j = 0; j < 4; ++j) {
+      c[j] = bpermute_f64(4 * (lane & 7) + j, cl);
+      sn[j] = bpermute_f64(4 * (lane & 7) + j, sl);
+    }
     if (ra.q) {
       for (int h0 = 0; h0 < ra.num_q_heads; h0 += 4) {
         const int h = h0 + (lane >> 4);
@@ -382,16 +400,30 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
         if (h < ra.num_q_heads) *p = r;
       }
     }
-    for (int h = 0; h < H; ++h) {
-      const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, pos, h, a.err,
-                                    lane == 0);
-      if (row < 0) continue;
-      const int64_t src = (t * H + h) * (kHeadDim / 4) + lane;
+    // the token's row for head 0; head h's row follows at a fixed stride
+    const int64_t row0 = cache_row(a.geo, a.block_table, a.block_table_len, pos, 0, a.err,
+                                   lane == 0);
+    if (row0 < 0) continue;
+    const int64_t hstride = a.geo.paged ? kBlockSize : 1;
+    const int items = H * (kHeadDim / 64);          // (group, head), group-major
+    const int sub = lane >> 4, el = lane & 15;      // this lane's item in a pass, element quad
+    for (int i0 = 0; i0 < items; i0 += 4) {
+      const int it = i0 + sub < items ? i0 + sub : items - 1;   // every lane shuffles
+      const int grp = it / H, h = it % H;
+      const int e = grp * 16 + el;                  // uint2 index within the row
+      const int64_t src = (t * H + h) * (kHeadDim / 4) + e;
       const uint2 kw = reinterpret_cast<const uint2*>(a.k_src)[src];
       const uint2 vw = reinterpret_cast<const uint2*>(a.v_src)[src];
-      const uint2 kr = rotate4(kw, shfl_xor8(kw), second, c, sn);
-      store_row4<FMT>(a, true, row, lane, lane < 16 ? kr : kw, kS);
-      store_row4<FMT>(a, false, row, lane, vw, vS);
+      uint2 kr = kw;
+      if (i0 < H) {                                 // the pass holds group-0 (rotary) items
+        const uint2 r = rotate4(kw, shfl_xor8(kw), second, c, sn);
+        kr = grp == 0 ? r : kw;
+      }
+      if (i0 + sub < items) {
+        const int64_t row = row0 + h * hstride;
+        store_row4<FMT>(a, true, row, e, kr, kS);
+        store_row4<FMT>(a, false, row, e, vw, vS);
+      }
     }
   }
 }
