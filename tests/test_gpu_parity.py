@@ -533,7 +533,13 @@ def test_decode_paged_equals_contiguous_and_repeats_bitwise(Y, W):
 _LENS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1000, 4097]
 
 
-def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=None):
+def _scale_bf16(bits, mul):
+    """bf16 bit patterns times a power of two (exact while in range)."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(mul)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=None, v_mul=1.0):
     """One batched decode call over sequences of the given lengths.  Keys are
     roped on the host by the oracle and appended (and, for NVFP4, quantised)
     by the library, so the cache holds exactly what the oracle quantises.
@@ -550,6 +556,8 @@ def _decode_batch(Y, kv, lens, hq, hkv, seed, paged=True, q_mul=1.0, bad_page=No
         q_raw = synth.host_fill(seed, synth.stream_id(s, synth.Q), 0, 1, hq, 256)
         k_raw = synth.host_fill(seed, synth.stream_id(s, synth.K), 0, max(n, 1), hkv, 256)[:n]
         v_raw = synth.host_fill(seed, synth.stream_id(s, synth.V), 0, max(n, 1), hkv, 256)[:n]
+        if v_mul != 1.0:
+            v_raw = _scale_bf16(v_raw, v_mul)
         qs.append(O.rope(q_raw, [n], t, bf16_out=True)[0])
         ks.append(O.rope(k_raw, np.arange(n), t, bf16_out=True) if n else k_raw)
         vs.append(v_raw)
@@ -643,6 +651,22 @@ def test_decode_contiguous_equals_paged_bitwise(Y, fmt):
     b, _, _ = _decode_batch(Y, kv, [1234], 24, 4, seed=820, paged=False)
     assert np.array_equal(a, b)
     _compare_attention(f"contiguous/{fmt}", b[0], refs[0], bf16_out=False)
+
+
+@pytest.mark.parametrize("v_mul", [2.0 ** 10, 2.0 ** -20])
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
+def test_decode_value_magnitude(Y, fmt, v_mul):
+    """Values 2^10 larger (INT8 group scales up to ~30, so p times the scale
+    would leave binary16's range without the kernel's shift) and 2^20
+    smaller; outputs scale with them, so the bound is relative to |v|."""
+    kv = _FMT[fmt]
+    _say(f"decode v x {v_mul} {fmt}")
+    got, refs, err = _decode_batch(Y, kv, [500, 33, 4097], 24, 4, seed=835, v_mul=v_mul)
+    assert err == 0
+    for s in range(3):
+        assert np.all(np.isfinite(got[s]))
+        _compare_attention(f"v_mul/{fmt}/{v_mul:g}/{s}", got[s] / v_mul, refs[s] / v_mul,
+                           bf16_out=False)
 
 
 @pytest.mark.parametrize("q_mul", [2.0 ** 20, 2.0 ** -30])

@@ -640,8 +640,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 //             holds tokens 4r..4r+3, whose scale rows it reads).
 //   O^T      += V^T (P o s_g)^T: V is staged as exact fp16 codes; 16 output
 //             dims lie in one group, and the P^T operand of those products is
-//             P times the token's group scale (rounded to fp16 like P; the
-//             largest p is 2^14 and its product with s is exact).  The row
+//             P times the token's group scale, rounded to fp16 like P.  A page
+//             whose largest V scale is at least 1 counts as higher in the
+//             running maximum by the scale's binary exponent, so that every
+//             p * s stays below 2^15 (fp16's range ends at 65504).  The row
 //             sums use P itself.  K = 16 tokens: the S^T accumulator is the
 //             P^T operand, one transposing LDS read per 16 dims is V^T.
 
@@ -842,6 +844,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         mx = fmaxf(mx, x[e]);
       }
       mx = max_over_row_groups(mx);
+      // p is multiplied by the token's V group scale s in fp16 below, so p
+      // must stay under 2^15 / s: with s < 2^(b - 14) (b its binary16
+      // exponent field), the page counts as vshift = max(0, b - 14) log2
+      // units higher in the running maximum, which keeps every p * s below
+      // 2^15 (the softmax does not depend on the constant taken off a row)
+      {
+        uint32_t sb = 0;   // largest V scale of the page (non-negative binary16 bits)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w0 = vsr[e].x, w1 = vsr[e].y;
+          sb = max(sb, max(max(w0 & 0xffffu, w0 >> 16), max(w1 & 0xffffu, w1 >> 16)));
+        }
+        sb = (uint32_t)max_over_row_groups((float)sb);
+        mx += (float)max(0, (int)((sb >> 10) & 31u) - 14);
+      }
       const bool grow = mx > m + kRescaleF4;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float mn = grow ? mx : m;
