@@ -132,7 +132,8 @@ def build_verify_step(W, Y, w, layers, nq, torch, dev):
     return step, ev
 
 
-def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2, 4, 6)):
+def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2, 4, 6),
+                 per_token=KV_BYTES_PER_TOKEN_LAYER, fmt="bf16", record=None):
     """Verify steps at several query counts over the decode layers; the entry
     for main_nq (3 draft tokens) is the headline, the others are listed."""
     res = {}
@@ -140,7 +141,7 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
         step, ev = build_verify_step(W, Y, w, layers, nq, torch, dev)
         wall, kms = time_steps(step, ev, steps, warmup, torch)
         ctx = w.n_ctx + nq
-        bpl = decode_bytes_per_launch(ctx, KV_BYTES_PER_TOKEN_LAYER, w.hq * nq)
+        bpl = decode_bytes_per_launch(ctx, per_token, w.hq * nq)
         res[nq] = {"value": w.layers * ctx / (wall / steps), "avg_launch_ms": kms,
                    "ms_per_step": wall / steps * 1e3, "bytes_per_launch": bpl,
                    "frac": bpl / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -149,12 +150,12 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
     m = res[main_nq]
     return {
         "workload": f"speculative verify step, {w.layers} layers x 1,048,576 + {main_nq} cached "
-                    f"tokens (bf16), {main_nq} causal queries x 24 q / 4 KV heads",
+                    f"tokens ({fmt}), {main_nq} causal queries x 24 q / 4 KV heads",
         "value": m["value"], "unit": "KV token-layers/s", "ms_per_step": m["ms_per_step"],
         "avg_launch_ms": m["avg_launch_ms"],
         "roofline": {"bound": "hbm", "achieved": m["bytes_per_launch"] / (m["avg_launch_ms"] * 1e-3)
                      / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["frac"],
-                     "traffic": measured_traffic(f"verify_split_bf16_long_q{main_nq}_1m.json"),
+                     "traffic": measured_traffic(record) if record else None,
                      "bytes_per_launch": m["bytes_per_launch"]},
         "by_queries": {str(nq): {"avg_launch_ms": r["avg_launch_ms"], "frac": r["frac"]}
                        for nq, r in res.items()},
@@ -375,7 +376,8 @@ def main():
     if not args.no_verify:
         log("timing verify steps")
         result["verify"] = bench_verify(W, Y, w, layers, torch, dev, max(3, args.steps // 2),
-                                        args.warmup)
+                                        args.warmup,
+                                        record="verify_split_bf16_long_q4_1m.json")
     del layers
     torch.cuda.empty_cache()
     if not args.no_nvfp4:
@@ -411,7 +413,13 @@ def main():
                          "frac": bpli / (ki * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": measured_traffic("decode_split_int8_long_int8_1m.json"),
                          "bytes_per_launch": bpli}}
-        del li, stepi, evi
+        del stepi, evi
+        if not args.no_verify:
+            log("timing INT8 verify steps")
+            result["int8_verify"] = bench_verify(
+                W, Y, wi, li, torch, dev, si, args.warmup, per_token=INT8_BYTES_PER_TOKEN_LAYER,
+                fmt="INT8 group-64", record="verify_split_int8_long_int8_q4_1m.json")
+        del li
         torch.cuda.empty_cache()
     if not args.no_append:
         log("append and rope over one 1M-token layer")

@@ -299,9 +299,11 @@ size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t 
  * 0 .. seq_lens[s] - num_queries + i.  Query head h reads KV head
  * h / (num_q_heads / num_kv_heads); logits are softmax_scale * <q, k> (0
  * selects 1/sqrt(head_dim)).  The split-K plan and the log-sum-exp merge are
- * those of yrk_decode_attention.  Both products run on bf16 matrix cores
- * with fp32 accumulation; the attention weights enter the value product as
- * two bf16 terms (16 significant bits).
+ * those of yrk_decode_attention.  Over a bf16 cache both products run on
+ * bf16 matrix cores with fp32 accumulation, and the attention weights enter
+ * the value product as two bf16 terms (16 significant bits).  Over an INT8
+ * cache the codes enter fp16 matrix cores as exact integers and the group
+ * scales are applied as in yrk_decode_attention.
  *   q_dev            bf16 [num_seqs][num_queries][num_q_heads][head_dim]
  *                    (already roped at the queries' positions), 16-byte aligned
  *   block_tables_dev int32 [num_seqs][block_table_stride] (paged); NULL for
@@ -315,7 +317,7 @@ size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t 
  *   workspace_dev    >= yrk_verify_workspace_size(...) bytes, 16-byte aligned
  *   dev_error_word   nullable; see the conventions above
  * Errors: YRK_EINVAL, YRK_ERANGE (max_seq_len beyond table or capacity),
- * YRK_ENOTSUP (a cache other than bf16, head_dim != 256, group size not in
+ * YRK_ENOTSUP (an NVFP4 cache, head_dim != 256, group size not in
  * {1,2,3,4,6}, or more than 48 query rows per KV head:
  * num_queries * num_q_heads / num_kv_heads > 48), YRK_ENOSPC.
  */

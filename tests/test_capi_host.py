@@ -113,7 +113,11 @@ def _verify(layer, S=1, nq=4, Hq=24, bt=0x3000, stride=64, lens=0x4000, max_len=
 def test_verify_validation():
     L = _layer()
     assert _verify(_layer(head_dim=128)) == Y.ENOTSUP
-    assert _verify(_layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50000)) == Y.ENOTSUP
+    assert _verify(_layer(dtype=Y.KV_NVFP4, k_scale=0x40000, v_scale=0x50000,
+                          k_tensor_scale_dev=0x60000, v_tensor_scale_dev=0x70000)) == Y.ENOTSUP
+    # INT8 is accepted: the call gets as far as the workspace check
+    assert _verify(_layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50000),
+                   ws_bytes=16) == Y.ENOSPC
     assert _verify(_layer(dtype=Y.KV_NVFP4)) == Y.EINVAL     # scale planes missing
     assert _verify(L, nq=0) == Y.EINVAL
     assert _verify(L, nq=9) == Y.ENOTSUP                     # 9 x 6 = 54 rows > 48

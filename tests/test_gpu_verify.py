@@ -10,7 +10,7 @@ import pytest
 import oracle as O
 import synth
 
-from test_gpu_parity import DEV, _bits, _compare_attention, _f64, _host_case, _say
+from test_gpu_parity import DEV, _bits, _compare_attention, _f64, _host_case, _say, _scale_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def _verify_batch(Y, lens, nq, hq, hkv, seed, paged=True, bad_page=None, out_f32=True):
+def _verify_batch(Y, lens, nq, hq, hkv, seed, paged=True, bad_page=None, out_f32=True,
+                  kv=None, v_mul=1.0):
     """One batched verify call.  Keys are roped on the host by the oracle and
     appended by the library; queries are roped by the oracle at their
     positions (clipped at 0 for the queries a too-short sequence leaves at
@@ -49,10 +50,13 @@ def _verify_batch(Y, lens, nq, hq, hkv, seed, paged=True, bad_page=None, out_f32
         q_raw = synth.host_fill(seed, synth.stream_id(s, synth.Q), 0, nq, hq, 256)
         k_raw = synth.host_fill(seed, synth.stream_id(s, synth.K), 0, max(n, 1), hkv, 256)[:n]
         v_raw = synth.host_fill(seed, synth.stream_id(s, synth.V), 0, max(n, 1), hkv, 256)[:n]
+        if v_mul != 1.0:
+            v_raw = _scale_bf16(v_raw, v_mul)
         qs.append(O.rope(q_raw, np.maximum(np.arange(n - nq, n), 0), t, bf16_out=True))
         ks.append(O.rope(k_raw, np.arange(n), t, bf16_out=True) if n else k_raw)
         vs.append(v_raw)
-    L = Y.KVLayer.allocate(Y.KV_BF16, hkv, pool, paged=paged, device=DEV)
+    kv = Y.KV_BF16 if kv is None else kv
+    L = Y.KVLayer.allocate(kv, hkv, pool, paged=paged, device=DEV)
     if paged:
         table = synth.block_permutation(seed, pool).reshape(S, pages_per)
         bt = torch.from_numpy(table).to(DEV)
@@ -83,9 +87,16 @@ def _verify_batch(Y, lens, nq, hq, hkv, seed, paged=True, bad_page=None, out_f32
     for s, n in enumerate(lens):
         qf = O.bf16_to_f64(qs[s])
         r = np.zeros((nq, hq, 256))
+        if kv == Y.KV_INT8 and n:
+            kc, ksc = O.int8_quantize(ks[s])
+            vc, vsc = O.int8_quantize(vs[s])
         for i in range(nq):
             sel = keep[s][keep[s] <= n - nq + i]
-            if len(sel):
+            if not len(sel):
+                continue
+            if kv == Y.KV_INT8:
+                r[i] = O.decode_attention(qf[i], kc[sel], vc[sel], int8=(ksc[sel], vsc[sel]))
+            else:
                 r[i] = O.decode_attention(qf[i], ks[s][sel], vs[s][sel])
         refs.append(r)
     return _f64(out), refs, int(err.item())
@@ -107,6 +118,41 @@ def test_verify_ragged_shapes(Y, hq, hkv, nq):
     assert err == 0
     for s, n in enumerate(lens):
         _compare_attention(f"verify/{hq}x{hkv}/q{nq}/len{n}", got[s], refs[s], bf16_out=False)
+
+
+_SHAPES_I8 = [(24, 4, 1), (24, 4, 2), (24, 4, 4), (24, 4, 6), (4, 4, 6), (8, 4, 6), (12, 4, 5),
+              (16, 4, 12), (12, 2, 4)]
+
+
+@pytest.mark.parametrize("hq,hkv,nq", _SHAPES_I8)
+def test_verify_int8_ragged_shapes(Y, hq, hkv, nq):
+    """The verify round over the INT8 group-64 cache (the pages' 1M-token
+    format): every row against the oracle's dense softmax over the
+    dequantised keys and values it may see."""
+    lens = sorted({nq, nq + 1, 15, 16, 17, 33, 100, 1000, 4097} - set(range(nq)))
+    _say(f"verify int8 ragged hq={hq} hkv={hkv} nq={nq}")
+    got, refs, err = _verify_batch(Y, lens, nq, hq, hkv, seed=960 + 7 * hq + hkv + 31 * nq,
+                                   kv=Y.KV_INT8)
+    assert err == 0
+    for s, n in enumerate(lens):
+        _compare_attention(f"verify_int8/{hq}x{hkv}/q{nq}/len{n}", got[s], refs[s],
+                           bf16_out=False)
+
+
+@pytest.mark.parametrize("v_mul", [2.0 ** 10, 2.0 ** -20])
+def test_verify_int8_value_magnitude_bad_page_and_contiguous(Y, v_mul):
+    _say(f"verify int8 v x {v_mul}, bad page, contiguous")
+    got, refs, err = _verify_batch(Y, [300, 77], 4, 24, 4, seed=970, bad_page=(0, 5),
+                                   kv=Y.KV_INT8, v_mul=v_mul)
+    assert err == Y.DEVERR_BLOCK_ID
+    for s in range(2):
+        assert np.all(np.isfinite(got[s]))
+        _compare_attention(f"verify_int8/v_mul{v_mul:g}/bad_page/{s}", got[s] / v_mul,
+                           refs[s] / v_mul, bf16_out=False)
+    a, refs, _ = _verify_batch(Y, [1234], 6, 24, 4, seed=975, kv=Y.KV_INT8, v_mul=v_mul)
+    b, _, _ = _verify_batch(Y, [1234], 6, 24, 4, seed=975, paged=False, kv=Y.KV_INT8,
+                            v_mul=v_mul)
+    assert np.array_equal(a, b)
 
 
 def test_verify_masks_and_flags_a_bad_page(Y):

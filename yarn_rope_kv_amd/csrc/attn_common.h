@@ -84,6 +84,64 @@ __device__ __forceinline__ uint2 vt_operand(const uint8_t* page_stage, int i, in
   return __builtin_bit_cast(uint2, v);
 }
 
+// ---- fp16 matrix-core pieces of the quantised-cache kernels ----------------
+
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+// The running maximum m is raised only when a step's maximum exceeds it by
+// more than kRescaleF4, so s - m <= kRescaleF4 and p = 2^(s - m + kPShiftF4)
+// <= 2^15 fits fp16.  The shift keeps probabilities down to 2^-28 of m at
+// full fp16 precision (2^-38 as subnormals); it cancels in O / l and is taken
+// off the log-sum-exp.  (A threshold of 6 with a shift of 9 ran at the same
+// speed and lost 13x in accuracy on the 1M-token outlier workload.)
+constexpr float kRescaleF4 = 1.0f;
+constexpr float kPShiftF4 = 14.0f;
+
+__device__ __forceinline__ floatx4_t mfma_f16(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4_t mfma_f16_k16(const uint2& a, const uint2& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                               __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed fp16, rounded to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, f16x2_t));
+}
+
+// Eight int8 codes (two dwords, element i in byte i) -> eight fp16 integers:
+// a byte c becomes fp16 1152 + c exactly (0x64 placed above c ^ 0x80 by a
+// byte permute), and one packed subtraction gives c.
+__device__ __forceinline__ uint4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
+  auto two = [&](uint32_t t, uint32_t sel) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, t, sel));
+    return __builtin_bit_cast(uint32_t, h - off);
+  };
+  return make_uint4(two(t0, 0x04010400u), two(t0, 0x04030402u), two(t1, 0x04010400u),
+                    two(t1, 0x04030402u));
+}
+
+// The largest binary16 V group scale among the 4 token rows of u (two
+// scale dwords per row, 4 groups), maxed over the wave's row groups: the
+// extra log2 units a page counts as in the running maximum so that p times
+// any of its scales stays below 2^15 (s < 2^(b - 14) for exponent field b).
+__device__ __forceinline__ float vscale_shift(const u32x2_t (&rows)[4]) {
+  uint32_t sb = 0;   // non-negative binary16 bits order like their values
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w0 = rows[e].x, w1 = rows[e].y;
+    sb = max(sb, max(max(w0 & 0xffffu, w0 >> 16), max(w1 & 0xffffu, w1 >> 16)));
+  }
+  sb = (uint32_t)max_over_row_groups((float)sb);
+  return (float)max(0, (int)((sb >> 10) & 31u) - 14);
+}
+
 // Orders one wave's LDS writes before its later reads of the same buffer
 // (the staging buffers are private to a wave).
 __device__ __forceinline__ void wave_lds_sync() {

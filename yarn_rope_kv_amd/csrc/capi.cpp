@@ -300,8 +300,15 @@ size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t 
     return 0;
   const int64_t rows = (int64_t)num_queries * (num_q_heads / num_kv_heads);
   if (rows > yrk::kVerifyMaxRows) return 0;
-  const yrk::DecodePlan p = yrk::plan_verify(num_seqs, num_kv_heads, (int32_t)rows, max_seq_len);
-  return yrk::decode_workspace_bytes(num_seqs, num_queries * num_q_heads, p);
+  // the cache format is not an argument here: enough for either plan
+  size_t need = 0;
+  for (int32_t dtype : {YRK_KV_BF16, YRK_KV_INT8}) {
+    const yrk::DecodePlan p =
+        yrk::plan_verify(num_seqs, num_kv_heads, (int32_t)rows, max_seq_len, dtype);
+    const size_t b = yrk::decode_workspace_bytes(num_seqs, num_queries * num_q_heads, p);
+    need = b > need ? b : need;
+  }
+  return need;
 }
 
 int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
@@ -321,7 +328,7 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   if (!aligned16(q_dev) || !aligned16(workspace_dev) || !aligned16(layer->k) ||
       !aligned16(layer->v))
     return YRK_EINVAL;
-  if (layer->dtype != YRK_KV_BF16) return YRK_ENOTSUP;
+  if (layer->dtype == YRK_KV_NVFP4) return YRK_ENOTSUP;
   const int group = num_q_heads / layer->num_kv_heads;
   if (group != 1 && group != 2 && group != 3 && group != 4 && group != 6)
     return YRK_ENOTSUP;
@@ -337,7 +344,8 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   yrk::VerifyArgs va;
   yrk::DecodeArgs& a = va.d;
   va.num_queries = num_queries;
-  a.plan = yrk::plan_verify(num_seqs, layer->num_kv_heads, num_queries * group, max_seq_len);
+  a.plan = yrk::plan_verify(num_seqs, layer->num_kv_heads, num_queries * group, max_seq_len,
+                            layer->dtype);
   const int32_t rows_per_seq = num_queries * num_q_heads;
   const size_t need = yrk::decode_workspace_bytes(num_seqs, rows_per_seq, a.plan);
   if (workspace_bytes < need) return YRK_ENOSPC;
@@ -350,8 +358,8 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   a.q = static_cast<const uint16_t*>(q_dev);
   a.k = layer->k;
   a.v = layer->v;
-  a.k_scale = nullptr;
-  a.v_scale = nullptr;
+  a.k_scale = static_cast<const uint8_t*>(layer->k_scale);   // INT8 group scales, else unused
+  a.v_scale = static_cast<const uint8_t*>(layer->v_scale);
   a.k_tensor_scale = nullptr;
   a.v_tensor_scale = nullptr;
   a.block_tables = layer->paged ? block_tables_dev : nullptr;

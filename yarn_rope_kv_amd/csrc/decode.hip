@@ -289,26 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
 constexpr int kUnitPages = 2;                            // pages per wave step
 constexpr int kStageBytes = kWaves * kUnitPages * kBlockSize * kRowBytesF16;   // 64 KiB
 constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
-// The running maximum m is raised only when a step's maximum exceeds it by
-// more than kRescaleF4, so s - m <= kRescaleF4 and p = 2^(s - m + kPShiftF4)
-// <= 2^15 fits fp16.  The shift keeps probabilities down to 2^-28 of m at
-// full fp16 precision (2^-38 as subnormals); it cancels in O / l and is taken
-// off the log-sum-exp.  (A threshold of 6 with a shift of 9 ran at the same
-// speed and lost 13x in accuracy on the 1M-token outlier workload.)
-constexpr float kRescaleF4 = 1.0f;
 constexpr int kVtAhead = 4;                              // V^T operands in flight ahead of their products
-constexpr float kPShiftF4 = 14.0f;
-
-__device__ __forceinline__ floatx4_t mfma_f16(const uint4& a, const uint4& b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-// Two floats -> packed fp16, rounded to nearest even (v_cvt_pk_f16_f32).
-__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, f16x2_t));
-}
 
 // Block scale (e4m3 byte SEL of w) as a packed fp16 pair.  The hardware fp8
 // conversion decodes OCP E4M3FN exactly, and every e4m3 value (0 and
@@ -647,7 +628,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 //             sums use P itself.  K = 16 tokens: the S^T accumulator is the
 //             P^T operand, one transposing LDS read per 16 dims is V^T.
 
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
 // Steps in flight beyond the one computed.  The kernel waits on memory far
@@ -664,22 +644,6 @@ constexpr bool kScaleOwnRowI8 = true;
 constexpr int kScaleRowsI8 = kScaleOwnRowI8 ? 1 : 4;
 constexpr int kQOpBytesI8 = kQOpLdsI8 ? 8 * 64 * 16 : 0;
 
-__device__ __forceinline__ floatx4_t mfma_f16_k16(const uint2& a, const uint2& b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                               __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
-}
-
-// Eight int8 codes (two dwords, element i in byte i) -> eight fp16 integers.
-__device__ __forceinline__ uint4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
-  const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
-  auto two = [&](uint32_t t, uint32_t sel) {
-    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, t, sel));
-    return __builtin_bit_cast(uint32_t, h - off);
-  };
-  return make_uint4(two(t0, 0x04010400u), two(t0, 0x04030402u), two(t1, 0x04010400u),
-                    two(t1, 0x04030402u));
-}
 
 // One lane's share of one page.
 struct I8Unit {
@@ -844,21 +808,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         mx = fmaxf(mx, x[e]);
       }
       mx = max_over_row_groups(mx);
-      // p is multiplied by the token's V group scale s in fp16 below, so p
-      // must stay under 2^15 / s: with s < 2^(b - 14) (b its binary16
-      // exponent field), the page counts as vshift = max(0, b - 14) log2
-      // units higher in the running maximum, which keeps every p * s below
-      // 2^15 (the softmax does not depend on the constant taken off a row)
-      {
-        uint32_t sb = 0;   // largest V scale of the page (non-negative binary16 bits)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w0 = vsr[e].x, w1 = vsr[e].y;
-          sb = max(sb, max(max(w0 & 0xffffu, w0 >> 16), max(w1 & 0xffffu, w1 >> 16)));
-        }
-        sb = (uint32_t)max_over_row_groups((float)sb);
-        mx += (float)max(0, (int)((sb >> 10) & 31u) - 14);
-      }
+      // p is multiplied by the token's V group scale in fp16 below: the page
+      // counts as higher in the running maximum by the scales' exponent, so
+      // every p * s stays below 2^15 (the softmax does not depend on the
+      // constant taken off a row)
+      mx += vscale_shift(vsr);
       const bool grow = mx > m + kRescaleF4;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float mn = grow ? mx : m;

@@ -305,21 +305,340 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
   }
 }
 
+// ---- INT8 group-64 cache -----------------------------------------------------
+//
+// The same rows, column blocks, masks and combine over an INT8 group-64
+// cache, with the INT8 decode kernel's exact integer path: the codes enter
+// the matrix cores as fp16 integers (v_mfma_f32_16x16x32_f16 for the scores,
+// 16x16x16 for the values), each key step covers 32 dims of one scale group
+// so that a group's partial products T_g are scaled by the token's key group
+// scale in fp32, and the value group scales ride on the fp16 weights
+// (p = 2^(s - m + 14), the page counted higher in the running maximum by its
+// largest V scale's exponent so that p * s stays below 2^15).  The Q^T
+// operands are fp16 after one power-of-two prescale shared by the R rows,
+// which puts the largest |q| in [2^14, 2^15) (bf16 values are exact there).
+
+// Measured per 1M-token layer (2, 4, 6 queries at GQA 6): C = 1 0.427 ms
+// with one page ahead (0.443 with two); C = 2 0.464 ms without a ring;
+// C = 3, one workgroup per CU, 0.941 / 0.897 / 0.819 ms with 0 / 1 / 2
+// pages ahead (one wave per SIMD leaves latency exposed).
+template <int C> struct VerifyTuneI8;
+template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWgsPerCu = 2; };
+template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWgsPerCu = 2; };
+template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWgsPerCu = 1; };
+
+// One lane's share of one page.
+struct I8VUnit {
+  u32x2_t kc[8];   // K: step j's 8 code bytes of row t (dims 64 (j/2) + 32 (j%2) + 8 kg .. +7)
+  u32x4_t vc[4];   // V: code bytes [64 kg, 64 kg + 64) of row t
+  u32x2_t ks, vs;  // row t's four binary16 group scales
+  bool ok;         // page present and inside the split
+};
+
+template <int C>
+__global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_split_int8(
+    VerifyArgs va) {
+  constexpr int AHEAD = VerifyTuneI8<C>::kAhead;
+  static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
+  static_assert(kStageBytesV + 3 * kQOpBytes <= kFinishBytes, "V staging and Q^T fit the buffer");
+  const DecodeArgs& a = va.d;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFinishBytes];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int lo = lane & 15, hi = lane >> 4;
+  const int G = a.group, nq = va.num_queries, R = nq * G;
+
+  int64_t len = a.seq_lens[s];
+  if (len > a.max_seq_len) {
+    if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+    len = a.max_seq_len;
+  }
+  if (len < nq && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+  if (len < 0) len = 0;
+  const int64_t qpos0 = len - nq;
+  const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
+  const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
+
+  // Q^T operands: block c, step j, lane l at ((c * 8 + j) * 64 + l) * 16
+  // bytes: row 16 c + l % 16, head dims 64 (j / 2) + 32 (j % 2) + 8 (l / 16)
+  // .. +7, as fp16 after the shared prescale (zero rows beyond R)
+  auto q_chunk = [&](int idx) {
+    const int l = idx & 63, j = (idx >> 6) & 7, c = idx >> 9;
+    const int r = kColRows * c + (l & 15);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      const int64_t h = (int64_t)g * G + r % G;
+      const uint16_t* qrow = a.q + (((int64_t)s * nq + r / G) * a.num_q_heads + h) * kHeadDim;
+      v = *reinterpret_cast<const u32x4_t*>(qrow + 64 * (j >> 1) + 32 * (j & 1) + 8 * (l >> 4));
+    }
+    return v;
+  };
+  float* red = reinterpret_cast<float*>(lds + kStageBytesV + C * kQOpBytes);   // [kWaves]
+  float qmax = 0.f;
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+    const u32x4_t v = q_chunk(idx);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
+  }
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
+  if (lane == 0) red[wave] = qmax;
+  __syncthreads();
+  qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // 2^(14 - e): the largest |q| lands in [2^14, 2^15)
+  const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
+  const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
+  const float qpre = __uint_as_float((uint32_t)pe << 23);
+  const float cl2 = a.scale_log2 * __uint_as_float((uint32_t)(254 - pe) << 23);
+  uint4* qop = reinterpret_cast<uint4*>(lds + kStageBytesV);
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+    const u32x4_t v = q_chunk(idx);
+    uint32_t h4[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) h4[w] = pk_f16(bf16_lo(v[w]) * qpre, bf16_hi(v[w]) * qpre);
+    qop[idx] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+  }
+  int64_t last[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int r = kColRows * c + lo;
+    last[c] = qpos0 + (r < R ? r / G : nq - 1);
+  }
+  __syncthreads();
+
+  floatx4_t o[C][16], lsum[C];
+  float m[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[c][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m[c] = kNegBig;
+  }
+
+  if (tok1 > tok0) {
+    const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
+    const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(a.k_scale);
+    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(a.v_scale);
+    const int64_t page0 = tok0 / kBlockSize;
+    const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+    uint8_t* my_stage = lds + wave * (kBlockSize * kRowBytesF16);
+    const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
+
+    auto load_unit = [&](int64_t pi, I8VUnit& U) {
+      int64_t base = 0, ts = 0;   // in rows
+      bool ok = false;
+      if (pi < npages) {
+        ok = page_base(a, s, g, page0 + pi, 1, &base, &ts);
+        if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
+      }
+      U.ok = ok;
+      const u32x2_t z2 = {0u, 0u};
+      const u32x4_t z4 = {0u, 0u, 0u, 0u};
+      u32x2_t kc[8], ks = z2, vs = z2;
+      u32x4_t vc[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kc[j] = z2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vc[i] = z4;
+      if (ok) {
+        const int64_t row = base + lo * ts;
+        const uint8_t* kp = Kc + row * kHeadDim + 8 * hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          kc[j] = *reinterpret_cast<const u32x2_t*>(kp + 64 * (j >> 1) + 32 * (j & 1));
+        const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(Vc + row * kHeadDim + 64 * hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vc[i] = vp[i];
+        ks = *reinterpret_cast<const u32x2_t*>(Ks + row * (kHeadDim / 64));
+        vs = *reinterpret_cast<const u32x2_t*>(Vs + row * (kHeadDim / 64));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) U.kc[j] = kc[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U.vc[i] = vc[i];
+      U.ks = ks;
+      U.vs = vs;
+    };
+
+    auto compute_unit = [&](int64_t pi, I8VUnit& U) {
+      const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
+      const int nv = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
+      // every row sees every token of the page (the same for all lanes)
+      const bool full = nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
+      if (nv < kBlockSize) {
+        // rows outside the split or the sequence, or of a masked page, get
+        // weight 0; their stale codes and scales become zeros (0 * NaN is not 0)
+        const bool keep = lo < nv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
+        U.ks = keep ? U.ks : u32x2_t{0u, 0u};
+        U.vs = keep ? U.vs : u32x2_t{0u, 0u};
+      }
+      // the group scales of rows 4 hi .. 4 hi + 3 (row r's are in lane r)
+      u32x2_t ksr[4], vsr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int src = 4 * (4 * hi + e);
+        ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.x),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.y)};
+        vsr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.x),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.y)};
+      }
+      // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
+      {
+        uint8_t* row = my_stage + lo * kRowBytesF16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) =
+              i8x8_to_f16(U.vc[j >> 1][2 * (j & 1)], U.vc[j >> 1][2 * (j & 1) + 1]);
+      }
+      // T_g = K_g Q_g^T per scale group and column block (each key step's
+      // codes are converted once for all blocks)
+      floatx4_t tg[C][4];
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) tg[c][gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint4 kf = i8x8_to_f16(U.kc[j][0], U.kc[j][1]);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          tg[c][j >> 1] = mfma_f16(kf, qop[(c * 8 + j) * 64 + lane], tg[c][j >> 1]);
+      }
+      const float vsh = vscale_shift(vsr);
+      uint2 pg[C][4];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;   // copies: see the INT8 decode kernel
+          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
+          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
+          float v = tg[c][0][e] * (float)s01[0];
+          v = fmaf(tg[c][1][e], (float)s01[1], v);
+          v = fmaf(tg[c][2][e], (float)s23[0], v);
+          v = fmaf(tg[c][3][e], (float)s23[1], v);
+          const bool vis = full || (4 * hi + e < nv && pt0 + 4 * hi + e <= last[c]);
+          x[e] = vis ? v * cl2 : -INFINITY;
+          mx = fmaxf(mx, x[e]);
+        }
+        mx = max_over_row_groups(mx) + vsh;
+        const bool grow = mx > m[c] + kRescaleF4;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mn = grow ? mx : m[c];
+          const float alpha = fast_exp2(m[c] - mn);
+          m[c] = mn;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
+          lsum[c] *= alpha;
+        }
+        const float mp = m[c] - kPShiftF4;
+        uint2 pop;
+        pop.x = pk_f16(fast_exp2(x[0] - mp), fast_exp2(x[1] - mp));
+        pop.y = pk_f16(fast_exp2(x[2] - mp), fast_exp2(x[3] - mp));
+        lsum[c] = mfma_f16_k16(ones, pop, lsum[c]);
+        // P^T operands with the V group scales of tokens 4 hi .. 4 hi + 3
+        const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop.x);
+        const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop.y);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int dw = gg >> 1;
+          const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
+          const f16x2_t s01 =
+              __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel));
+          const f16x2_t s23 =
+              __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[3][dw], vsr[2][dw], sel));
+          pg[c][gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
+                                 __builtin_bit_cast(uint32_t, p23 * s23));
+        }
+      }
+      // O^T += V^T (P o s_g)^T; 16 output dims lie in one scale group
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint2 vt = vt_operand(my_stage, i, lo, hi);
+#pragma unroll
+        for (int c = 0; c < C; ++c) o[c][i] = mfma_f16_k16(vt, pg[c][i >> 2], o[c][i]);
+      }
+      wave_lds_sync();
+    };
+
+    I8VUnit U[AHEAD + 1];
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * kWaves, U[k]);
+    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * kWaves) {
+#pragma unroll
+      for (int b = 0; b <= AHEAD; ++b) {
+        const int64_t uu = u + b * kWaves;
+        load_unit(uu + AHEAD * kWaves, U[(b + AHEAD) % (AHEAD + 1)]);
+        if (uu < npages) compute_unit(uu, U[b]);
+      }
+    }
+  }
+
+  // combine the 4 waves, one column block at a time (l and O carry 2^kPShiftF4)
+  float* sm_o = reinterpret_cast<float*>(lds);     // [kWaves][16][256]
+  float* sm_m = sm_o + kWaves * kColRows * kHeadDim;
+  float* sm_l = sm_m + kWaves * kColRows;
+  const int nsp = a.plan.num_splits;
+  const int64_t rows_per_seq = (int64_t)nq * a.num_q_heads;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<floatx4_t*>(sm_o + (wave * kColRows + lo) * kHeadDim + 16 * i + 4 * hi) =
+          o[c][i];
+    if (hi == 0) {
+      sm_m[wave * kColRows + lo] = m[c] - kPShiftF4;
+      sm_l[wave * kColRows + lo] = lsum[c][0];
+    }
+    __syncthreads();
+    for (int row = 0; row < kColRows; ++row) {
+      const int r = kColRows * c + row;
+      if (r >= R) break;
+      const int d = threadIdx.x;
+      float M = kNegBig;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
+      float L = 0.f, Ov = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(sm_m[w * kColRows + row] - M);
+        L += sm_l[w * kColRows + row] * sc;
+        Ov += sm_o[(w * kColRows + row) * kHeadDim + d] * sc;
+      }
+      const int64_t hh = (int64_t)(r / G) * a.num_q_heads + (int64_t)g * G + r % G;
+      const int64_t slot = ((int64_t)s * rows_per_seq + hh) * nsp + split;
+      a.ws_o[slot * kHeadDim + d] = L > 0.f ? Ov / L : 0.f;
+      if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
 int column_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
-int wgs_per_cu(int rows) {
-  switch (column_blocks(rows)) {
-    case 1: return VerifyTune<1>::kWgsPerCu;
-    case 2: return VerifyTune<2>::kWgsPerCu;
-    default: return VerifyTune<3>::kWgsPerCu;
-  }
+int wgs_per_cu(int rows, int32_t dtype) {
+  const int c = column_blocks(rows);
+  if (dtype == 2)
+    return c == 1 ? VerifyTuneI8<1>::kWgsPerCu
+                  : (c == 2 ? VerifyTuneI8<2>::kWgsPerCu : VerifyTuneI8<3>::kWgsPerCu);
+  return c == 1 ? VerifyTune<1>::kWgsPerCu
+                : (c == 2 ? VerifyTune<2>::kWgsPerCu : VerifyTune<3>::kWgsPerCu);
 }
 
 }  // namespace
 
 // One round of workgroups over the 256 CUs.
-DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len) {
-  const int64_t target_wgs = 256 * wgs_per_cu(rows);
+DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len,
+                       int32_t dtype) {
+  const int64_t target_wgs = 256 * wgs_per_cu(rows, dtype);
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   const int64_t chunks = (max_seq_len + unit - 1) / unit;
@@ -339,10 +658,14 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const int rows = a.num_queries * d.group;
   const dim3 grid(d.plan.num_splits, d.geo.num_kv_heads, d.num_seqs);
   hipError_t e;
+  const bool i8 = d.dtype == 2;
   switch (column_blocks(rows)) {
-    case 1: e = launch(verify_split_bf16<1>, grid, dim3(kThreads), 0, st, a); break;
-    case 2: e = launch(verify_split_bf16<2>, grid, dim3(kThreads), 0, st, a); break;
-    case 3: e = launch(verify_split_bf16<3>, grid, dim3(kThreads), 0, st, a); break;
+    case 1: e = i8 ? launch(verify_split_int8<1>, grid, dim3(kThreads), 0, st, a)
+                   : launch(verify_split_bf16<1>, grid, dim3(kThreads), 0, st, a); break;
+    case 2: e = i8 ? launch(verify_split_int8<2>, grid, dim3(kThreads), 0, st, a)
+                   : launch(verify_split_bf16<2>, grid, dim3(kThreads), 0, st, a); break;
+    case 3: e = i8 ? launch(verify_split_int8<3>, grid, dim3(kThreads), 0, st, a)
+                   : launch(verify_split_bf16<3>, grid, dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

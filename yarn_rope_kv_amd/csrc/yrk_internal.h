@@ -116,7 +116,8 @@ struct VerifyArgs {
   DecodeArgs d;           // d.num_q_heads: query heads per token
   int32_t num_queries;
 };
-DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len);
+DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len,
+                       int32_t dtype);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 
 struct PrefillArgs {
