@@ -1,4 +1,5 @@
-// Split-K decode attention over a paged bf16 or NVFP4 KV cache (gfx950).
+// Split-K decode attention over a paged bf16, NVFP4 or INT8 group-64 KV cache
+// (gfx950).
 //
 // One query per sequence, GQA: the G query heads of one KV head share every
 // key and value they read ([P5] "Why NVFP4 KV changes the math": 4 KV heads x
@@ -24,12 +25,12 @@
 //   merge phase   grid (q_head, seq): log-sum-exp combination of the splits
 //                 ([P3] "Limitations": the decode split policy).
 //
-// NVFP4 pages ([P5] "Why NVFP4 KV changes the math") are read as packed
-// e2m1 codes and e4m3 scales: lane (r, c) reads, per token, the 8 code bytes
-// of head dims [16c, 16c+16) and that block's scale byte, and dequantises in
-// registers (the hardware fp4 -> bf16 conversion, then a bf16 dot with q and
-// one scale multiply per 16 elements; the tensor scales are folded into the
-// softmax scale and the output).
+// The quantised caches take the matrix cores instead (the sections further
+// down): NVFP4 pages ([P5] "Why NVFP4 KV changes the math": packed e2m1
+// codes, an e4m3 scale per 16 elements and a per-tensor fp32 scale) and INT8
+// group-64 pages are turned into fp16 in registers, exactly, and both
+// products run on v_mfma with fp32 accumulation; the tensor scales are folded
+// into the softmax scale and the output.
 #include "attn_common.h"
 
 namespace yrk {
@@ -623,8 +624,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 //             dims lie in one group, and the P^T operand of those products is
 //             P times the token's group scale, rounded to fp16 like P.  A page
 //             whose largest V scale is at least 1 counts as higher in the
-//             running maximum by the scale's binary exponent, so that every
-//             p * s stays below 2^15 (fp16's range ends at 65504).  The row
+//             running maximum by one more than that scale's binary exponent,
+//             so every p * s stays below 2^15 (fp16 ends at 65504).  The row
 //             sums use P itself.  K = 16 tokens: the S^T accumulator is the
 //             P^T operand, one transposing LDS read per 16 dims is V^T.
 
@@ -637,20 +638,15 @@ constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
 // row's group scales and fetches the 4 rows it needs from their lanes
 // (ds_bpermute) when it computes, 4 registers per step instead of 16.
 // Measured per 1M-token layer: 0.443 ms with one step ahead, 0.407 ms with
-// two (243 registers, no spills).
+// two (about 240 registers, no spills).
 constexpr int kAheadI8 = 2;
-constexpr bool kQOpLdsI8 = true;
-constexpr bool kScaleOwnRowI8 = true;
-constexpr int kScaleRowsI8 = kScaleOwnRowI8 ? 1 : 4;
-constexpr int kQOpBytesI8 = kQOpLdsI8 ? 8 * 64 * 16 : 0;
-
+constexpr int kQOpBytesI8 = 8 * 64 * 16;                            // Q^T operands in LDS
 
 // One lane's share of one page.
 struct I8Unit {
   u32x2_t kc[8];            // K: step j's 8 code bytes of row t (dims of group j / 2)
   u32x4_t vc[4];            // V: code bytes [64 kg, 64 kg + 64) of row t
-  u32x2_t ks[kScaleRowsI8], vs[kScaleRowsI8];   // binary16 scales (4 groups) of rows
-                            // 4 kg .. 4 kg + 3, or of row t alone
+  u32x2_t ks, vs;           // row t's four binary16 group scales
   bool ok;                  // page present and inside the split
 };
 
@@ -684,13 +680,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
     uint4 qop[8];   // step j = 2 g + j2: dims 64 g + 32 j2 + 8 hi .. +7 of head lo
     const float c = a.scale_log2 * load_q_f16<G>(a, s, g, lo, hi, qop, true);
     uint4* qlds = reinterpret_cast<uint4*>(stage + kStageBytesI8);   // [step][lane]
-    if constexpr (kQOpLdsI8) {   // tok1 > tok0 is the same for the whole workgroup
-      if (wave == 0) {
+    if (wave == 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qlds[j * 64 + lane] = qop[j];
-      }
-      __syncthreads();
+      for (int j = 0; j < 8; ++j) qlds[j * 64 + lane] = qop[j];
     }
+    __syncthreads();   // tok1 > tok0 is the same for the whole workgroup
 
     const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
     const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
@@ -710,14 +704,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       U.ok = ok;
       const u32x2_t z2 = {0u, 0u};
       const u32x4_t z4 = {0u, 0u, 0u, 0u};
-      u32x2_t kc[8], ks[kScaleRowsI8], vs[kScaleRowsI8];
+      u32x2_t kc[8], ks = z2, vs = z2;
       u32x4_t vc[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j) kc[j] = z2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) vc[i] = z4;
-#pragma unroll
-      for (int e = 0; e < kScaleRowsI8; ++e) { ks[e] = z2; vs[e] = z2; }
       if (ok) {
         const int64_t row = base + lo * ts;
         const uint8_t* kp = Kc + row * kHeadDim + 8 * hi;
@@ -727,19 +719,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(Vc + row * kHeadDim + 64 * hi);
 #pragma unroll
         for (int i = 0; i < 4; ++i) vc[i] = vp[i];
-#pragma unroll
-        for (int e = 0; e < kScaleRowsI8; ++e) {
-          const int64_t srow = kScaleOwnRowI8 ? row : base + (4 * hi + e) * ts;
-          ks[e] = *reinterpret_cast<const u32x2_t*>(Ks + srow * (kHeadDim / 64));
-          vs[e] = *reinterpret_cast<const u32x2_t*>(Vs + srow * (kHeadDim / 64));
-        }
+        ks = *reinterpret_cast<const u32x2_t*>(Ks + row * (kHeadDim / 64));
+        vs = *reinterpret_cast<const u32x2_t*>(Vs + row * (kHeadDim / 64));
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) U.kc[j] = kc[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) U.vc[i] = vc[i];
-#pragma unroll
-      for (int e = 0; e < kScaleRowsI8; ++e) { U.ks[e] = ks[e]; U.vs[e] = vs[e]; }
+      U.ks = ks;
+      U.vs = vs;
     };
 
     const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
@@ -753,27 +741,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
         const bool keep = lo < nv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < kScaleRowsI8; ++e) {
-          const bool ke = (kScaleOwnRowI8 ? lo : 4 * hi + e) < nv;
-          U.vs[e] = ke ? U.vs[e] : u32x2_t{0u, 0u};
-          U.ks[e] = ke ? U.ks[e] : u32x2_t{0u, 0u};
-        }
+        U.vs = keep ? U.vs : u32x2_t{0u, 0u};
+        U.ks = keep ? U.ks : u32x2_t{0u, 0u};
       }
       // the group scales of rows 4 hi .. 4 hi + 3 (row r's are in lane r)
       u32x2_t ksr[4], vsr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if constexpr (kScaleOwnRowI8) {
-          const int src = 4 * (4 * hi + e);
-          ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks[0].x),
-                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks[0].y)};
-          vsr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs[0].x),
-                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs[0].y)};
-        } else {
-          ksr[e] = U.ks[e];
-          vsr[e] = U.vs[e];
-        }
+        const int src = 4 * (4 * hi + e);
+        ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.x),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.y)};
+        vsr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.x),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.y)};
       }
       // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
       {
@@ -789,8 +768,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        tg[j >> 1] = mfma_f16(i8x8_to_f16(U.kc[j][0], U.kc[j][1]),
-                              kQOpLdsI8 ? qlds[j * 64 + lane] : qop[j], tg[j >> 1]);
+        tg[j >> 1] = mfma_f16(i8x8_to_f16(U.kc[j][0], U.kc[j][1]), qlds[j * 64 + lane],
+                              tg[j >> 1]);
       float x[4];
       float mx = -INFINITY;
 #pragma unroll
@@ -809,9 +788,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       }
       mx = max_over_row_groups(mx);
       // p is multiplied by the token's V group scale in fp16 below: the page
-      // counts as higher in the running maximum by the scales' exponent, so
-      // every p * s stays below 2^15 (the softmax does not depend on the
-      // constant taken off a row)
+      // counts as higher in the running maximum by 1 + the largest scale's
+      // binary exponent (0 if it is below 1), so every p * s stays below
+      // 2^15 (the softmax does not depend on the constant taken off a row)
       mx += vscale_shift(vsr);
       const bool grow = mx > m + kRescaleF4;
       if (__builtin_amdgcn_ballot_w64(grow)) {

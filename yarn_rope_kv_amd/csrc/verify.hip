@@ -1,4 +1,5 @@
-// Multi-query split-K decode attention over a paged bf16 KV cache (gfx950):
+// Multi-query split-K decode attention over a paged bf16 or INT8 group-64 KV
+// cache (gfx950):
 // the verify step of speculative decoding, where num_queries consecutive
 // tokens of a sequence (the last accepted one and the drafted ones) attend
 // to the cache at once ([P1] "Things that bit me" and [P3] "Limitations":
@@ -313,8 +314,8 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
 // 16x16x16 for the values), each key step covers 32 dims of one scale group
 // so that a group's partial products T_g are scaled by the token's key group
 // scale in fp32, and the value group scales ride on the fp16 weights
-// (p = 2^(s - m + 14), the page counted higher in the running maximum by its
-// largest V scale's exponent so that p * s stays below 2^15).  The Q^T
+// (p = 2^(s - m + 14), the page counted higher in the running maximum by 1 +
+// its largest V scale's exponent so that p * s stays below 2^15).  The Q^T
 // operands are fp16 after one power-of-two prescale shared by the R rows,
 // which puts the largest |q| in [2^14, 2^15) (bf16 values are exact there).
 
