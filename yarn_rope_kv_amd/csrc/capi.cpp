@@ -344,6 +344,7 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   yrk::VerifyArgs va;
   yrk::DecodeArgs& a = va.d;
   va.num_queries = num_queries;
+  va.min_len = num_queries;
   a.plan = yrk::plan_verify(num_seqs, layer->num_kv_heads, num_queries * group, max_seq_len,
                             layer->dtype);
   const int32_t rows_per_seq = num_queries * num_q_heads;

@@ -5,254 +5,32 @@
 // key and value they read ([P5] "Why NVFP4 KV changes the math": 4 KV heads x
 // 256; 24 query heads).  Decode time is dominated by streaming the cache
 // ([P1] "Two cards are faster than one, not just bigger": each card reading
-// half the KV is what made TP2 faster), so the kernel is organised around
+// half the KV is what made TP2 faster), so the kernels are organised around
 // HBM streaming:
 //
 //   split phase   grid (split, kv_head, seq), 4 waves per workgroup.  A
 //                 split owns a contiguous range of pages; wave w of the
-//                 workgroup takes pages w, w+4, ...  For each 16-token page
-//                 the wave issues all of its K and V loads at once (16 KiB
-//                 for bf16: 16 x 16-byte loads per lane) and then computes.
-//                 Lane l = 16 r + c handles tokens 4j + r (j < 4) of the page
-//                 and head dims [8c, 8c+8) and [128+8c, 128+8c+8): every load
-//                 instruction reads 4 tokens x 256 contiguous bytes.
-//                 Scores: v_dot2_f32_bf16 partial dots, summed over the 16
-//                 lanes of a DPP row.  Each row keeps its own online softmax
-//                 (max, sum, acc[G][16] in fp32 registers); rows, then waves,
-//                 are merged at the end of the split and one partial
-//                 (normalised output + log-sum-exp) per query head goes to
-//                 the workspace.
+//                 workgroup takes pages w, w+4, ...  Both products run on
+//                 the matrix cores with the G heads padded to a 16-column
+//                 block, the loads of the wave's next pages in flight while
+//                 one is computed.  Each wave keeps its own online softmax;
+//                 the waves are combined at the end of the split and one
+//                 partial (normalised output + log2-sum-exp) per query head
+//                 goes to the workspace.
 //   merge phase   grid (q_head, seq): log-sum-exp combination of the splits
 //                 ([P3] "Limitations": the decode split policy).
 //
-// The quantised caches take the matrix cores instead (the sections further
-// down): NVFP4 pages ([P5] "Why NVFP4 KV changes the math": packed e2m1
-// codes, an e4m3 scale per 16 elements and a per-tensor fp32 scale) and INT8
-// group-64 pages are turned into fp16 in registers, exactly, and both
-// products run on v_mfma with fp32 accumulation; the tensor scales are folded
+// A bf16 cache is served by the multi-query kernels of the verify step run
+// with one query (same partials, same merge).  This file holds the kernels of
+// the quantised caches, NVFP4 pages ([P5] "Why NVFP4 KV changes the math":
+// packed e2m1 codes, an e4m3 scale per 16 elements and a per-tensor fp32
+// scale) and INT8 group-64 pages, whose codes are turned into fp16 in
+// registers, exactly, with fp32 accumulation; the tensor scales are folded
 // into the softmax scale and the output.
 #include "attn_common.h"
 
 namespace yrk {
 namespace {
-
-// Per-row online softmax update for one page: scores sc[j][h] already in the
-// log2 domain (masked tokens at -inf).  Returns the probabilities in sc.
-template <int G>
-__device__ __forceinline__ void softmax_update(float (&sc)[4][G], float (&m)[G], float (&l)[G],
-                                               float (&acc)[G][16]) {
-  bool grow = false;
-  float mnew[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
-    mnew[h] = fmaxf(m[h], mx);
-    grow |= mnew[h] > m[h];
-  }
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float alpha = fast_exp2(m[h] - mnew[h]);
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
-      m[h] = mnew[h];
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j][h] = fast_exp2(sc[j][h] - m[h]);
-      l[h] += sc[j][h];
-    }
-  }
-}
-
-// End of a split: merge the 4 rows of each wave, then the 4 waves through
-// LDS, and write one normalised partial + log2-sum-exp per query head.
-// dim_of(e) maps accumulator slot e of lane c to its head dimension.
-template <int G, typename DimOf>
-__device__ __forceinline__ void finish_split(const DecodeArgs& a, int s, int g, int split,
-                                             float (&m)[G], float (&l)[G], float (&acc)[G][16],
-                                             DimOf dim_of) {
-  __shared__ float sm_acc[kWaves][G][kHeadDim];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-  const int c = lane & 15;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = fmaxf(m[h], __shfl_xor(m[h], 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
-    const float alpha = fast_exp2(m[h] - M);
-    float lh = l[h] * alpha;
-    lh += __shfl_xor(lh, 16);
-    lh += __shfl_xor(lh, 32);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = acc[h][e] * alpha;
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[h][e] = v;
-    }
-    m[h] = M;
-    l[h] = lh;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sm_acc[wave][h][dim_of(c, e)] = acc[h][e];
-      if (c == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-  const int nsp = a.plan.num_splits;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
-    const int h = idx / kHeadDim;
-    const int d = idx % kHeadDim;
-    float M = kNegBig;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = fast_exp2(sm_m[w][h] - M);
-      L += sm_l[w][h] * sc;
-      O += sm_acc[w][h][d] * sc;
-    }
-    const int qh = g * G + h;
-    const int64_t slot = ((int64_t)s * a.num_q_heads + qh) * nsp + split;
-    a.ws_o[slot * kHeadDim + d] = L > 0.f ? O / L : 0.f;
-    if (d == 0) a.ws_lse[slot] = L > 0.f ? M + __log2f(L) : -INFINITY;
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_bf16(DecodeArgs a) {
-  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-  const int r = lane >> 4, c = lane & 15;
-
-  int64_t len = a.seq_lens[s];
-  if (len > a.max_seq_len) {
-    if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
-    len = a.max_seq_len;
-  }
-  if (len < 0) len = 0;
-  const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
-  const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
-
-  float m[G], l[G], acc[G][16];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
-  }
-
-  if (tok1 > tok0) {
-    // q slices of this lane: dims [8c, 8c+8) and [128+8c, 128+8c+8) of each head
-    uint4 qa[G][2];
-    const uint16_t* qbase = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * kHeadDim;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qa[h][0] = *reinterpret_cast<const uint4*>(qbase + h * kHeadDim + 8 * c);
-      qa[h][1] = *reinterpret_cast<const uint4*>(qbase + h * kHeadDim + 128 + 8 * c);
-    }
-    const uint16_t* K = static_cast<const uint16_t*>(a.k);
-    const uint16_t* V = static_cast<const uint16_t*>(a.v);
-    const int64_t page0 = tok0 / kBlockSize;
-    const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-    for (int64_t pi = wave; pi < npages; pi += kWaves) {
-      const int64_t page = page0 + pi;
-      int64_t base = 0, ts = 0;
-      const bool ok = page_base(a, s, g, page, kHeadDim, &base, &ts);
-      if (!ok && lane == 0) err_flag(a.err, kErrBlockId);
-      uint4 kr[4][2], vr[4][2];
-      if (ok) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint16_t* kp = K + base + (4 * j + r) * ts + 8 * c;
-          kr[j][0] = *reinterpret_cast<const uint4*>(kp);
-          kr[j][1] = *reinterpret_cast<const uint4*>(kp + 128);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint16_t* vp = V + base + (4 * j + r) * ts + 8 * c;
-          vr[j][0] = *reinterpret_cast<const uint4*>(vp);
-          vr[j][1] = *reinterpret_cast<const uint4*>(vp + 128);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          kr[j][0] = kr[j][1] = vr[j][0] = vr[j][1] = make_uint4(0, 0, 0, 0);
-      }
-      float sc[4][G];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float d = 0.f;
-          d = dot2_bf16(qa[h][0].x, kr[j][0].x, d);
-          d = dot2_bf16(qa[h][0].y, kr[j][0].y, d);
-          d = dot2_bf16(qa[h][0].z, kr[j][0].z, d);
-          d = dot2_bf16(qa[h][0].w, kr[j][0].w, d);
-          d = dot2_bf16(qa[h][1].x, kr[j][1].x, d);
-          d = dot2_bf16(qa[h][1].y, kr[j][1].y, d);
-          d = dot2_bf16(qa[h][1].z, kr[j][1].z, d);
-          d = dot2_bf16(qa[h][1].w, kr[j][1].w, d);
-          sc[j][h] = d;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t tok = page * kBlockSize + 4 * j + r;
-        const bool valid = ok && tok < tok1;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float d = row16_sum(sc[j][h]);
-          sc[j][h] = valid ? d * a.scale_log2 : -INFINITY;
-        }
-      }
-      softmax_update<G>(sc, m, l, acc);
-      // Rows past the end of the sequence (or of a masked page) hold whatever
-      // the pool holds; their weight is 0, but 0 * NaN is not, so clear them.
-      if (!ok || (page + 1) * kBlockSize > tok1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (!(ok && page * kBlockSize + 4 * j + r < tok1))
-            vr[j][0] = vr[j][1] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float vf[16];
-        const uint32_t w[8] = {vr[j][0].x, vr[j][0].y, vr[j][0].z, vr[j][0].w,
-                               vr[j][1].x, vr[j][1].y, vr[j][1].z, vr[j][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          vf[2 * e] = bf16_lo(w[e]);
-          vf[2 * e + 1] = bf16_hi(w[e]);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = sc[j][h];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-        }
-      }
-    }
-  }
-  finish_split<G>(a, s, g, split, m, l, acc,
-                  [](int cc, int e) { return e < 8 ? 8 * cc + e : 128 + 8 * cc + (e - 8); });
-}
 
 // ---- NVFP4 on the matrix cores ----------------------------------------------
 //
@@ -930,35 +708,42 @@ __global__ __launch_bounds__(64 * kMergeGroups) void decode_merge(DecodeArgs a) 
 template <int G>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.plan.num_splits, a.geo.num_kv_heads, a.num_seqs);
-  if (a.dtype == 0) return launch(decode_split_bf16<G>, grid, dim3(kThreads), 0, st, a);
   if (a.dtype == 2) return launch(decode_split_int8<G>, grid, dim3(kThreads), 0, st, a);
   return launch(decode_split_nvfp4<G>, grid, dim3(kThreads), 0, st, a);
 }
 
 }  // namespace
 
-// Workgroups a decode launch aims for: both split kernels keep two resident
+// Workgroups a decode launch aims for: the split kernels keep two resident
 // per CU and get a single round of them (measured: 1,024 bf16 workgroups, two
 // rounds, were 1.5% slower at 24 q / 4 KV heads and 10% slower at 12 q / 2
-// KV heads, where each split then holds only 2,048 tokens).
+// KV heads, where each split then holds only 2,048 tokens; 768, 1,024 and
+// 2,048 NVFP4 workgroups were 22%, 5% and 11% slower than 512).  The bf16
+// cache runs the one-query verify kernel, which is planned the same way.
 constexpr int64_t kTargetWgsBf16 = 512;
 constexpr int64_t kTargetWgsF4 = 512;
 constexpr int64_t kTargetWgsI8 = 512;
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len, int32_t dtype) {
-  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : (dtype == 1 ? kTargetWgsF4 : kTargetWgsI8);
+DecodePlan split_plan(int64_t units, int64_t max_seq_len, int64_t target_wgs) {
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
   const int64_t chunks = (max_seq_len + unit - 1) / unit;      // 64-token chunks
-  int64_t splits = (target_wgs + units - 1) / units;
+  // as many splits as keep units x splits within the target: workgroups
+  // beyond one round would run after it, few of them and alone (15
+  // sequences x 4 KV heads: 8 splits, 480 workgroups, rather than 540)
+  int64_t splits = target_wgs / units;
   if (splits > chunks) splits = chunks;
   if (splits < 1) splits = 1;
-  int64_t per = (chunks + splits - 1) / splits;                // chunks per split
+  const int64_t per = (chunks + splits - 1) / splits;          // chunks per split
   DecodePlan p;
   p.tokens_per_split = per * unit;
   p.num_splits = (int32_t)((chunks + per - 1) / per);
   if (p.num_splits < 1) p.num_splits = 1;
   return p;
+}
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len, int32_t dtype) {
+  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : (dtype == 1 ? kTargetWgsF4 : kTargetWgsI8);
+  return split_plan((int64_t)num_seqs * num_kv_heads, max_seq_len, target_wgs);
 }
 
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const DecodePlan& p) {
@@ -969,6 +754,15 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const Decod
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.dtype == 0) {
+    // bf16: the verify kernels with one query at position len - 1, which sees
+    // every cached token; an empty sequence gives zeros and is no error
+    VerifyArgs v;
+    v.d = a;
+    v.num_queries = 1;
+    v.min_len = 0;
+    return launch_verify(v, st);
+  }
   hipError_t e;
   switch (a.group) {
     case 1: e = launch_split<1>(a, st); break;

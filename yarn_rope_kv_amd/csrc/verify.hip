@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
     if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
     len = a.max_seq_len;
   }
-  if (len < nq && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+  if (len < va.min_len && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
   if (len < 0) len = 0;
   const int64_t qpos0 = len - nq;   // position of query 0 (negative only when flagged)
   const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
     if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
     len = a.max_seq_len;
   }
-  if (len < nq && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+  if (len < va.min_len && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
   if (len < 0) len = 0;
   const int64_t qpos0 = len - nq;
   const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
@@ -639,19 +639,7 @@ int wgs_per_cu(int rows, int32_t dtype) {
 // One round of workgroups over the 256 CUs.
 DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len,
                        int32_t dtype) {
-  const int64_t target_wgs = 256 * wgs_per_cu(rows, dtype);
-  const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  const int64_t chunks = (max_seq_len + unit - 1) / unit;
-  int64_t splits = (target_wgs + units - 1) / units;
-  if (splits > chunks) splits = chunks;
-  if (splits < 1) splits = 1;
-  const int64_t per = (chunks + splits - 1) / splits;
-  DecodePlan p;
-  p.tokens_per_split = per * unit;
-  p.num_splits = (int32_t)((chunks + per - 1) / per);
-  if (p.num_splits < 1) p.num_splits = 1;
-  return p;
+  return split_plan((int64_t)num_seqs * num_kv_heads, max_seq_len, 256 * wgs_per_cu(rows, dtype));
 }
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {

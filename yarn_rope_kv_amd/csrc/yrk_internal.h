@@ -74,6 +74,9 @@ struct DecodePlan {
   int32_t num_splits;
   int64_t tokens_per_split;  // multiple of 4 * kBlockSize
 };
+// Splits of units (sequence, KV head) x max_seq_len tokens into at most
+// target_wgs workgroups when units allow (64-token granularity).
+DecodePlan split_plan(int64_t units, int64_t max_seq_len, int64_t target_wgs);
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len,
                        int32_t dtype);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const DecodePlan& p);
@@ -115,6 +118,8 @@ constexpr int kVerifyMaxRows = 48;
 struct VerifyArgs {
   DecodeArgs d;           // d.num_q_heads: query heads per token
   int32_t num_queries;
+  int32_t min_len;        // shorter sequences are flagged: num_queries for verify,
+                          // 0 when single-query decode runs on these kernels
 };
 DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len,
                        int32_t dtype);
