@@ -73,6 +73,15 @@ constexpr float kMaxRowSum = 0x1p64f;     // main kernel: largest row sum it acc
 constexpr float kNegBig = -1.0e30f;       // finite start for the running maximum
 constexpr int kNK = 32;                   // keys per tile
 constexpr int kNST = 4;                   // tiles in the LDS ring
+// 32-dim score steps (0..7) after which the two load groups of a full page
+// go out.  A direct load holds the issuing wave for tens of cycles; issued
+// among the score products, that time overlaps the products already in the
+// matrix core.  Measured per 8,192-token chunk: 188 ms with groups after
+// steps 0 and 3 (188-190 ms for other pairs), 200 ms with all 8 loads ahead
+// of the products, 194-200 ms with four groups of two (one more M0 write
+// each), 195-198 ms with one group among the PV products.
+constexpr int kLoadStep0 = 0;
+constexpr int kLoadStep1 = 3;
 
 template <int NK>
 struct Tile {
@@ -264,13 +273,21 @@ __device__ __forceinline__ void load_rows(const PrefillArgs& a, const PageLoad& 
   }
 }
 
-// The 8 direct loads of a planned page.  `voffq` holds the per-lane offsets
-// of a full page less the instruction offset each load carries.
+// Half h (rows 0-7 or 8-15) of a page with all 16 rows visible: 4 direct
+// loads behind one M0 write.  `voffq` holds the per-lane offsets of a full
+// page less the instruction offset each load carries.
+__device__ __forceinline__ void load_full_half(const PageLoad& pl, const uint32_t (&voffq)[8],
+                                               int h) {
+  if (h == 0) dma16x4(pl.src, voffq[0], voffq[1], voffq[2], voffq[3], pl.lds0);
+  else dma16x4(pl.src, voffq[4], voffq[5], voffq[6], voffq[7], pl.lds0 + 4096u);
+}
+
+// The 8 direct loads of a planned page.
 __device__ __forceinline__ void load_page(const PrefillArgs& a, const PageLoad& pl,
                                           const uint32_t (&voffq)[8], uint32_t stride_b) {
   if (pl.full) {
-    dma16x4(pl.src, voffq[0], voffq[1], voffq[2], voffq[3], pl.lds0);
-    dma16x4(pl.src, voffq[4], voffq[5], voffq[6], voffq[7], pl.lds0 + 4096u);
+    load_full_half(pl, voffq, 0);
+    load_full_half(pl, voffq, 1);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) load_rows(a, pl, i, stride_b);
@@ -614,20 +631,21 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
                      islot = (uint32_t)(it + NST - 1) & (NST - 1);
       wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
       wg_barrier();
-      // plan tile it+NST-1 into the slot tile it-1 used; its 8 loads go out
-      // one per 32-dim step of the products below
+      // plan tile it+NST-1 into the slot tile it-1 used; a full page's 8
+      // loads go out in two groups of four among the score products below
       const bool load = it + NST - 1 < ntiles;
       PageLoad pl;
       if (load) {
         const uint32_t m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
                                             ring[islot], pl);
         missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
-        load_page(a, pl, voff, stride_b);
+        if (!pl.full) load_page(a, pl, voff, stride_b);
       }
       const uint32_t miss = (missing >> (2 * nslot)) & 3u;
       any_missing |= miss;
       scores.template operator()<true>(ring[nslot], (it + 1) * NK, miss, ring[cslot], [&](int ks) {
-
+        if (load && pl.full && (ks == kLoadStep0 || ks == kLoadStep1))
+          load_full_half(pl, voff, ks == kLoadStep0 ? 0 : 1);
       });
       pv.template operator()<true>(ring[cslot], pcur, pnext);
       ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
@@ -662,20 +680,21 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
                      islot = (uint32_t)(it + NST - 1) & (NST - 1);
       wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
       wg_barrier();
-      // plan tile it+NST-1 into the slot tile it-1 used; its 8 loads go out
-      // one per 32-dim step of the products below
+      // plan tile it+NST-1 into the slot tile it-1 used; a full page's 8
+      // loads go out in two groups of four among the score products below
       const bool load = it + NST - 1 < ntiles;
       PageLoad pl;
       if (load) {
         const uint32_t m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
                                             ring[islot], pl);
         missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
-        load_page(a, pl, voff, stride_b);
+        if (!pl.full) load_page(a, pl, voff, stride_b);
       }
       const uint32_t miss = (missing >> (2 * nslot)) & 3u;
       any_missing |= miss;
       scores.template operator()<true>(ring[nslot], (it + 1) * NK, miss, ring[cslot], [&](int ks) {
-
+        if (load && pl.full && (ks == kLoadStep0 || ks == kLoadStep1))
+          load_full_half(pl, voff, ks == kLoadStep0 ? 0 : 1);
       });
       pv.template operator()<true>(ring[cslot], pcur, pnext);
       ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
