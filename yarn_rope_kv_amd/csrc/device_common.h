@@ -19,8 +19,6 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -46,23 +44,7 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Sum over the 16 lanes of a DPP row: rotate by 8 and 4 inside the row, then
-// swap pairs and neighbours inside each quad.  Every lane of the row ends
-// with the row total.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));
-  return x;
-}
 
 __device__ __forceinline__ void set_error(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);
