@@ -102,6 +102,8 @@ def test_decode_workspace_size_is_stable():
     assert Y.decode_workspace_size(1, 24, 4, 1048576, head_dim=128) == 0
     # partial outputs grow with the number of sequences, never below one split each
     assert Y.decode_workspace_size(15, 24, 4, 131072) >= 15 * 24 * 257 * 4
+    # an empty longest sequence still plans one split (this once divided by zero)
+    assert Y.decode_workspace_size(2, 24, 4, 0) >= 2 * 24 * 257 * 4
 
 
 def _verify(layer, S=1, nq=4, Hq=24, bt=0x3000, stride=64, lens=0x4000, max_len=1024,
@@ -142,6 +144,7 @@ def test_verify_workspace_size():
     assert Y.verify_workspace_size(1, 2, 24, 5, 1048576) == 0     # 24 heads over 5 KV heads
     # one partial (256 + 1 floats) per (sequence, query, head, split), at least one split
     assert Y.verify_workspace_size(3, 6, 24, 4, 64) >= 3 * 6 * 24 * 257 * 4
+    assert Y.verify_workspace_size(1, 2, 24, 4, 0) >= 2 * 24 * 257 * 4
 
 
 def test_append_validation():

@@ -634,6 +634,28 @@ def test_decode_ragged_shapes(Y, fmt, hq, hkv):
                            bf16_out=False)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
+def test_decode_max_len_zero(Y, fmt):
+    """A batch whose longest sequence is empty (max_seq_len 0): zeros and no
+    flag, in every cache format."""
+    kv = _FMT[fmt]
+    _say(f"decode max_seq_len 0 {fmt}")
+    L = Y.KVLayer.allocate(kv, 4, 2, paged=True, device=DEV)
+    if kv == Y.KV_NVFP4:
+        L.k_tensor_scale.fill_(1.0)
+        L.v_tensor_scale.fill_(1.0)
+    q = torch.ones((2, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bt = torch.zeros((2, 1), dtype=torch.int32, device=DEV)
+    out = torch.full((2, 24, 256), 7.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(Y.decode_workspace_size(2, 24, 4, 0), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.decode_attention(L, q, bt, torch.zeros(2, dtype=torch.int32, device=DEV), 0, out, ws,
+                       err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.all(out == 0)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "int8"])
 def test_decode_quantised_masks_and_flags_a_bad_page(Y, fmt):
     _say(f"decode {fmt} bad page")

@@ -726,7 +726,9 @@ constexpr int64_t kTargetWgsI8 = 512;
 
 DecodePlan split_plan(int64_t units, int64_t max_seq_len, int64_t target_wgs) {
   const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
-  const int64_t chunks = (max_seq_len + unit - 1) / unit;      // 64-token chunks
+  // 64-token chunks; at least one, so that an empty range still gets a
+  // split (its workgroups find no page and write empty partials)
+  const int64_t chunks = max((max_seq_len + unit - 1) / unit, (int64_t)1);
   // as many splits as keep units x splits within the target: workgroups
   // beyond one round would run after it, few of them and alone (15
   // sequences x 4 KV heads: 8 splits, 480 workgroups, rather than 540)
