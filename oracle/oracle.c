@@ -23,6 +23,7 @@
  *
  * Precision: fp64 throughout, compiled without fast-math or FMA contraction.
  */
+#include <limits.h>
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
@@ -112,11 +113,13 @@ int orc_yarn_table(double base, int rot_dim, double factor, int64_t orig_max_pos
 
     double corr_fast = d * log(L / (two_pi * beta_fast)) / (2.0 * log(base));
     double corr_slow = d * log(L / (two_pi * beta_slow)) / (2.0 * log(base));
-    int low = (int)floor(corr_fast);
-    int high = (int)ceil(corr_slow);
-    if (low < 0) low = 0;
-    if (high > rot_dim - 1) high = rot_dim - 1;
-    double lo = (double)low, hi = (double)high;
+    /* the clamps in double, as written: the unclamped ends can lie far outside
+       the int range (a base just above 1), where a conversion is undefined */
+    double lo = floor(corr_fast), hi = ceil(corr_slow);
+    if (lo < 0.0) lo = 0.0;
+    if (hi > d - 1.0) hi = d - 1.0;
+    const int low = lo > (double)INT_MAX ? INT_MAX : (int)lo;
+    const int high = hi < (double)INT_MIN ? INT_MIN : (int)hi;
     if (hi == lo) hi += 0.001;
 
     for (int i = 0; i < half; ++i) {

@@ -37,6 +37,15 @@ def test_library_table_matches_oracle(orig, corr, factor):
     assert np.allclose(inv, t.inv_freq, rtol=4e-16, atol=0)
 
 
+@pytest.mark.parametrize("base", [1.0000001, 1.001])
+def test_library_table_matches_oracle_near_base_one(base):
+    """Correction-range ends far outside the int range: the same table."""
+    inv, _, lo, hi = Y.yarn_table(Y.YarnParams(rope_theta=base))
+    t = O.yarn_table(rope_theta=base)
+    assert np.allclose(inv, t.inv_freq, rtol=4e-16, atol=0)
+    assert hi == t.high
+
+
 def _rope(p, x=0x1000, T=1, H=24, stride=24 * 256, pos=0x2000):
     cp = p.c()
     return Y._lib.yrk_yarn_rope_apply(ctypes.byref(cp), x, T, H, stride, pos, None)

@@ -70,6 +70,18 @@ def test_factor_one_is_plain_rope_table():
     assert t.mscale == 1.0
 
 
+@pytest.mark.parametrize("base", [1.0000001, 1.001])
+def test_base_near_one_interpolates_every_pair(base):
+    """A base just above 1 puts the fast end of the correction range far
+    past the last pair (beyond the int range for 1 + 1e-7): the ramp is 1
+    for every pair, so every frequency is theta_i / s."""
+    d = GOLD["rotary_dim"]
+    t = _table(rope_theta=base)
+    theta = base ** (-2.0 * np.arange(d // 2) / d)
+    assert np.allclose(t.inv_freq, theta / GOLD["factor"], rtol=1e-15, atol=0)
+    assert t.low >= d and t.high == d - 1
+
+
 def test_domain_errors():
     with pytest.raises(ValueError):
         _table(factor=0.5)

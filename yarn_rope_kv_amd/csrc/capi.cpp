@@ -42,10 +42,15 @@ int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32
   auto pair_at_turns = [&](double turns) {
     return (double)d * log(L / (turns * 2.0 * M_PI)) / (2.0 * ln_base);
   };
-  int32_t lo = (int32_t)floor(pair_at_turns(p->beta_fast));
-  int32_t hi = (int32_t)ceil(pair_at_turns(p->beta_slow));
-  lo = lo < 0 ? 0 : lo;
-  hi = hi > d - 1 ? d - 1 : hi;
+  // low is clamped below at 0 and high above at d - 1.  Their other ends are
+  // limited too, low to d and high to -1, in double before the conversion to
+  // int32 (undefined out of range, which a base just above 1 reaches); no
+  // weight changes, since the ramp is already 1 (low > d) or 0 (high < -1)
+  // for every pair there.
+  const double lo_d = floor(pair_at_turns(p->beta_fast));
+  const double hi_d = ceil(pair_at_turns(p->beta_slow));
+  const int32_t lo = lo_d < 0.0 ? 0 : (lo_d > (double)d ? d : (int32_t)lo_d);
+  const int32_t hi = hi_d > (double)(d - 1) ? d - 1 : (hi_d < -1.0 ? -1 : (int32_t)hi_d);
   const double span = hi == lo ? 0.001 : (double)(hi - lo);
   if (inv_freq) {
     for (int i = 0; i < d / 2; ++i) {
