@@ -254,8 +254,11 @@ size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * "YaRN, and matching what vLLM actually does").  The cache is split into
  * token ranges processed in parallel across compute units and merged by
  * log-sum-exp ([P3] "Limitations": the decode split policy).
- * seq_lens[s] == 0 gives a zero output row.  Over an NVFP4 cache the keys
- * and values are dequantised to fp16 exactly for the matrix cores.  Over an
+ * seq_lens[s] == 0 gives a zero output row (max_seq_len 0 is allowed).
+ * Over a bf16 cache both products run on the matrix cores (the verify
+ * kernels with one query, whose P keeps 16 significant bits).  Over an
+ * NVFP4 cache the keys and values are dequantised to fp16 exactly for the
+ * matrix cores.  Over an
  * INT8 cache the codes enter the matrix cores as exact fp16 integers: each
  * scale group's partial key products are scaled in fp32, and the value
  * scales multiply the (fp16) attention weights, so no dequantised value is
