@@ -55,13 +55,17 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
     const int rem = (int)(gid - t * H * kChunksPerRow);
     const int h = rem / kChunksPerRow;
     const int c = rem % kChunksPerRow;
+    // the source loads go out before the destination lookup (position, then
+    // page table), whose latency they then overlap
+    const int64_t src = (t * H + h) * kChunksPerRow + c;
+    const uint4 kx = reinterpret_cast<const uint4*>(a.k_src)[src];
+    const uint4 vx = reinterpret_cast<const uint4*>(a.v_src)[src];
     const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
                                   a.err, c == 0);
     if (row < 0) continue;
-    const int64_t src = (t * H + h) * kChunksPerRow + c;
     const int64_t dst = row * kChunksPerRow + c;
-    reinterpret_cast<uint4*>(a.k_dst)[dst] = reinterpret_cast<const uint4*>(a.k_src)[src];
-    reinterpret_cast<uint4*>(a.v_dst)[dst] = reinterpret_cast<const uint4*>(a.v_src)[src];
+    reinterpret_cast<uint4*>(a.k_dst)[dst] = kx;
+    reinterpret_cast<uint4*>(a.v_dst)[dst] = vx;
   }
 }
 
@@ -166,15 +170,17 @@ __global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
     const int rem = (int)(gid - t * H * kQBlocks);
     const int h = rem / kQBlocks;
     const int qb = rem % kQBlocks;
-    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
-                                  a.err, qb == 0);
-    if (row < 0) continue;
+    // source loads first: they overlap the destination lookup
     const int64_t src = ((t * H + h) * kHeadDim + qb * 16) / 8;  // in uint4 units
     const uint4* ks = reinterpret_cast<const uint4*>(a.k_src) + src;
     const uint4* vs = reinterpret_cast<const uint4*>(a.v_src) + src;
+    const uint4 k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
+    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
+                                  a.err, qb == 0);
+    if (row < 0) continue;
     uint2 kp, vp;
-    const uint32_t kq = quantize16(ks[0], ks[1], kS, &kp);
-    const uint32_t vq = quantize16(vs[0], vs[1], vS, &vp);
+    const uint32_t kq = quantize16(k0, k1, kS, &kp);
+    const uint32_t vq = quantize16(v0, v1, vS, &vp);
     reinterpret_cast<uint2*>(a.k_dst)[row * kQBlocks + qb] = kp;
     reinterpret_cast<uint2*>(a.v_dst)[row * kQBlocks + qb] = vp;
     a.k_scale_dst[row * kQBlocks + qb] = (uint8_t)kq;
@@ -228,8 +234,14 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
 
 // Four bf16 values (one lane's share of a group) -> four packed int8 codes
 // and, in every lane, the group's binary16 scale bits.  The lanes of one DPP
-// row (16 lanes x 4 = 64 elements) hold one group.  Both quotients are fp64
-// divisions (correctly rounded) followed by one rounding to nearest even.
+// row (16 lanes x 4 = 64 elements) hold one group.  The scale is max / 127 in
+// fp64 (correctly rounded), then one rounding to binary16.  Each code is the
+// correctly rounded fp32 quotient x / s, then one rounding to nearest even:
+// with x = a 2^i (a < 2^8) and s = b 2^j (b < 2^11), x / s is either a
+// half-integer exactly (which fp32 holds) or at least 2^-12 away from every
+// half-integer up to 127.5, while the fp32 quotient is within 2^-18 of it, so
+// the code is the one the exact quotient gives.  (Subnormal x only meet
+// scales that make the quotient round to 0 either way.)
 __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits) {
   const uint32_t e[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
   uint32_t m = 0;
@@ -238,14 +250,14 @@ __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits)
   m = row16_max_u32(m);
   const uint32_t sb = f16_encode_sat((double)bf16_to_f32((uint16_t)m) / 127.0);
   *scale_bits = sb;
-  const double sv = f16_decode(sb);
+  const float sv = (float)f16_decode(sb);   // a binary16 value, exact in fp32
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int c = 0;
-    if (sv > 0.0) {
-      double q = rint((double)bf16_to_f32((uint16_t)e[i]) / sv);
-      q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+    if (sv > 0.0f) {
+      float q = rintf(bf16_to_f32((uint16_t)e[i]) / sv);
+      q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
       c = (int)q;
     }
     packed |= ((uint32_t)c & 0xffu) << (8 * i);
@@ -254,29 +266,46 @@ __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits)
 }
 
 // One wave per (token, head) row: lane l quantises elements 4l .. 4l+3 of K
-// and of V; group l / 16.
+// and of V; group l / 16.  A wave takes kI8RowsInFlight rows of its
+// grid-stride sequence at a time and issues all their source loads before the
+// destination lookups (position, then page table) and the quantisation.
+constexpr int kI8RowsInFlight = 4;
+
 __global__ __launch_bounds__(256) void append_int8_kernel(AppendArgs a) {
   const int H = a.geo.num_kv_heads;
   const int lane = threadIdx.x & 63;
   const int64_t rows = a.num_tokens * H;
   const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows;
-       r += wstride) {
-    const int64_t t = r / H;
-    const int h = (int)(r - t * H);
-    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
-                                  a.err, lane == 0);
-    if (row < 0) continue;
-    const uint2 kw = reinterpret_cast<const uint2*>(a.k_src)[r * (kHeadDim / 4) + lane];
-    const uint2 vw = reinterpret_cast<const uint2*>(a.v_src)[r * (kHeadDim / 4) + lane];
-    uint32_t ksb, vsb;
-    const uint32_t kc = quantize_i8x4(kw, &ksb);
-    const uint32_t vc = quantize_i8x4(vw, &vsb);
-    reinterpret_cast<uint32_t*>(a.k_dst)[row * (kHeadDim / 4) + lane] = kc;
-    reinterpret_cast<uint32_t*>(a.v_dst)[row * (kHeadDim / 4) + lane] = vc;
-    if ((lane & 15) == 0) {
-      reinterpret_cast<uint16_t*>(a.k_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)ksb;
-      reinterpret_cast<uint16_t*>(a.v_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)vsb;
+  for (int64_t r0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r0 < rows;
+       r0 += kI8RowsInFlight * wstride) {
+    uint2 kw[kI8RowsInFlight], vw[kI8RowsInFlight];
+#pragma unroll
+    for (int i = 0; i < kI8RowsInFlight; ++i) {
+      const int64_t r = r0 + i * wstride;
+      kw[i] = vw[i] = make_uint2(0u, 0u);
+      if (r < rows) {
+        kw[i] = reinterpret_cast<const uint2*>(a.k_src)[r * (kHeadDim / 4) + lane];
+        vw[i] = reinterpret_cast<const uint2*>(a.v_src)[r * (kHeadDim / 4) + lane];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kI8RowsInFlight; ++i) {
+      const int64_t r = r0 + i * wstride;
+      if (r >= rows) break;
+      const int64_t t = r / H;
+      const int h = (int)(r - t * H);
+      const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
+                                    a.err, lane == 0);
+      if (row < 0) continue;
+      uint32_t ksb, vsb;
+      const uint32_t kc = quantize_i8x4(kw[i], &ksb);
+      const uint32_t vc = quantize_i8x4(vw[i], &vsb);
+      reinterpret_cast<uint32_t*>(a.k_dst)[row * (kHeadDim / 4) + lane] = kc;
+      reinterpret_cast<uint32_t*>(a.v_dst)[row * (kHeadDim / 4) + lane] = vc;
+      if ((lane & 15) == 0) {
+        reinterpret_cast<uint16_t*>(a.k_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)ksb;
+        reinterpret_cast<uint16_t*>(a.v_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)vsb;
+      }
     }
   }
 }
@@ -484,7 +513,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     return launch(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
   }
   if (a.dtype == 2) {
-    const int64_t waves = a.num_tokens * a.geo.num_kv_heads;   // one wave per row
+    // one wave per kI8RowsInFlight rows
+    const int64_t waves = (a.num_tokens * a.geo.num_kv_heads + kI8RowsInFlight - 1) /
+                          kI8RowsInFlight;
     return launch(append_int8_kernel, dim3(grid_for(waves * 64, 1 << 18)), dim3(256), 0, s, a);
   }
   const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
