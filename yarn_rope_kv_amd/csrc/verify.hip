@@ -1,12 +1,13 @@
 // Multi-query split-K decode attention over a paged bf16 or INT8 group-64 KV
-// cache (gfx950):
-// the verify step of speculative decoding, where num_queries consecutive
-// tokens of a sequence (the last accepted one and the drafted ones) attend
-// to the cache at once ([P1] "Things that bit me" and [P3] "Limitations":
-// a verify round evaluates K + 1 query columns; [P3] "Usage": 1 to 5 draft
-// tokens, so 2 to 6 queries).  Their keys and values are in
-// the cache already; query i of a sequence of len cached tokens sits at
-// position len - num_queries + i and sees keys 0 .. len - num_queries + i.
+// cache (gfx950): the verify step of speculative decoding, where num_queries
+// consecutive tokens of a sequence (the last accepted one and the drafted
+// ones) attend to the cache at once ([P1] "Things that bit me" and [P3]
+// "Limitations": a verify round evaluates K + 1 query columns; [P3] "Usage":
+// 1 to 5 draft tokens, so 2 to 6 queries).  Their keys and values are in the
+// cache already; query i of a sequence of len cached tokens sits at position
+// len - num_queries + i and sees keys 0 .. len - num_queries + i.  With one
+// query (at len - 1, seeing every cached token) the bf16 kernel is also the
+// single-query decode kernel of a bf16 cache.
 //
 // With G query heads per KV head, one KV head serves R = num_queries x G
 // query rows (row r = query r / G, head r % G of the group).  Every key is
