@@ -116,7 +116,9 @@ typedef struct yrk_yarn_params {
  * the dequantised value is code * s.  The rounding rules are this library's
  * reading.  The tensor-scale pointers are not used.
  *
- * This build supports head_dim 256 and block_size 16.
+ * This build supports head_dim 256 and block_size 16.  k, v and (NVFP4,
+ * INT8) k_scale, v_scale must be 16-byte aligned, the tensor-scale pointers
+ * 4-byte aligned (YRK_EINVAL otherwise, from every entry point).
  */
 typedef struct yrk_kv_layer {
   int32_t dtype;          /* YRK_KV_BF16, YRK_KV_NVFP4 or YRK_KV_INT8 */
@@ -159,13 +161,15 @@ int yrk_yarn_table(const yrk_yarn_params* params, double* inv_freq_out, double* 
  *   x_dev          bf16, token t head h at x + t*token_stride + h*head_dim
  *   num_tokens     >= 0 (0 is a no-op)
  *   num_heads      > 0, num_heads*head_dim <= token_stride
- *   positions_dev  int32 [num_tokens], each >= 0 (negative positions are
- *                  reported through nothing: they rotate the other way)
- * Errors: YRK_EINVAL (null, bad params/shape), YRK_ENOTSUP (rotary_dim > 256).
+ *   positions_dev  int32 [num_tokens], each >= 0; a token with a negative
+ *                  position is left unchanged and sets YRK_DEVERR_POSITION
+ *   dev_error_word nullable device uint32 (see the conventions above)
+ * Errors: YRK_EINVAL (null, bad params/shape), YRK_ENOTSUP (rotary_dim > 256;
+ * refused before the table is built, whatever head_dim allows).
  */
 int yrk_yarn_rope_apply(const yrk_yarn_params* params, void* x_dev, int64_t num_tokens,
                         int32_t num_heads, int64_t token_stride, const int32_t* positions_dev,
-                        hipStream_t stream);
+                        uint32_t* dev_error_word, hipStream_t stream);
 
 /*
  * yrk_nvfp4_tensor_scale -- S = fl32(amax / (6 * 448)) of n bf16 values,
@@ -219,7 +223,8 @@ int yrk_kv_append_quantize(const yrk_kv_layer* layer, const void* k_dev, const v
  *   q_dev            nullable: bf16 [num_tokens] rows of num_q_heads heads
  *                    of head_dim, q_token_stride elements apart (a multiple
  *                    of 4, at least num_q_heads * head_dim), 8-byte aligned;
- *                    roped in place whatever the table says
+ *                    roped in place whatever the table says, except for a
+ *                    negative position (left unchanged, flagged)
  *   k_dev, v_dev     bf16 [num_tokens][num_kv_heads][head_dim], contiguous,
  *                    16-byte aligned, keys not yet roped; not modified
  *   block_table_dev  int32 [block_table_len] (paged); NULL for contiguous
@@ -362,7 +367,8 @@ size_t yrk_prefill_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int
  *                workgroup with a rescaling running maximum.  Calls that
  *                share a workspace must not overlap.
  * Errors: YRK_EINVAL (also a null or misaligned workspace), YRK_ERANGE
- * (positions beyond table or capacity), YRK_ENOTSUP (dtype other than bf16,
+ * (positions beyond table or capacity, or a chunk ending past 2^31 - 65),
+ * YRK_ENOTSUP (dtype other than bf16,
  * head_dim != 256, group size other than 6), YRK_ENOSPC (workspace smaller
  * than yrk_prefill_workspace_size()).
  */

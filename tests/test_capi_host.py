@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(Y.exported_symbols())
     for name in declared:
         assert hasattr(Y._lib, name)
-    assert Y._lib.yrk_abi_version() == 1
+    assert Y._lib.yrk_abi_version() == 2
 
 
 @pytest.mark.parametrize("orig,corr,factor", [(262144, 0, 4.0), (262144, 1048576, 4.0),
@@ -46,9 +46,9 @@ def test_library_table_matches_oracle_near_base_one(base):
     assert hi == t.high
 
 
-def _rope(p, x=0x1000, T=1, H=24, stride=24 * 256, pos=0x2000):
+def _rope(p, x=0x1000, T=1, H=24, stride=24 * 256, pos=0x2000, err=None):
     cp = p.c()
-    return Y._lib.yrk_yarn_rope_apply(ctypes.byref(cp), x, T, H, stride, pos, None)
+    return Y._lib.yrk_yarn_rope_apply(ctypes.byref(cp), x, T, H, stride, pos, err, None)
 
 
 @pytest.mark.parametrize("kw", [dict(factor=0.5), dict(factor=65.0), dict(factor=float("nan")),
@@ -57,6 +57,19 @@ def _rope(p, x=0x1000, T=1, H=24, stride=24 * 256, pos=0x2000):
                                 dict(mscale=float("inf"))])
 def test_rope_rejects_bad_params(kw):
     assert _rope(Y.YarnParams(**kw)) == Y.EINVAL
+
+
+@pytest.mark.parametrize("d", [258, 512, 8192])
+def test_rotary_tables_beyond_the_library_are_refused(d):
+    """head_dim = rotary_dim past the 128-pair table (and, for the fused pass,
+    past 64 dims): ENOTSUP, returned before the table is built, with the
+    process alive (these once overran a stack array)."""
+    p = Y.YarnParams(head_dim=d, rotary_dim=d)
+    assert _rope(p, stride=24 * d) == Y.ENOTSUP
+    L = _layer()
+    pc = p.c()
+    assert Y._lib.yrk_rope_append(ctypes.byref(L), ctypes.byref(pc), 0x8000, 24, 24 * 256,
+                                  0x100, 0x200, 4, 0x400, 4, 0x300, None, None) == Y.ENOTSUP
 
 
 def test_rope_rejects_bad_shapes_and_nulls():
@@ -102,6 +115,20 @@ def test_decode_validation():
     assert _decode(L, ws_bytes=16) == Y.ENOSPC
     assert _decode(_layer(paged=0), S=2, bt=None) == Y.EINVAL   # contiguous needs one sequence
     assert _decode(_layer(paged=0), bt=None, max_len=64 * 16 + 1) == Y.ERANGE
+    # every plane the kernels read with wide loads must be aligned
+    assert _decode(_layer(k=0x10008)) == Y.EINVAL
+    assert _decode(_layer(v=0x20004)) == Y.EINVAL
+    nv = dict(dtype=Y.KV_NVFP4, k_scale=0x40000, v_scale=0x50000, k_tensor_scale_dev=0x60000,
+              v_tensor_scale_dev=0x70000)
+    assert _decode(_layer(**nv), ws_bytes=16) == Y.ENOSPC            # aligned: reaches the end
+    assert _decode(_layer(**dict(nv, k_scale=0x40004))) == Y.EINVAL
+    assert _decode(_layer(**dict(nv, v_tensor_scale_dev=0x70002))) == Y.EINVAL
+    assert _decode(_layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50008)) == Y.EINVAL
+    # shapes beyond the launch grid, and pools whose block ids do not fit int32
+    assert _decode(L, S=70000, stride=64) == Y.ENOTSUP
+    assert _decode(_layer(num_blocks=1 << 31)) == Y.ERANGE
+    # a table stride whose token count overflows int64 is no error by itself
+    assert _decode(L, stride=(1 << 63) - 1, ws_bytes=16) == Y.ENOSPC
 
 
 def test_decode_workspace_size_is_stable():
@@ -211,12 +238,19 @@ def test_prefill_validation():
                  None, None)
 
     assert call(start=64 * 16 - 63) == Y.ERANGE
+    # chunks ending within two 32-key tiles of 2^31 are refused (int32 key bounds)
+    # (the accepted call stops at its workspace size, before any launch)
+    big = (1 << 31) // 16
+    short = Y.prefill_workspace_size(64, 24) - 1
+    assert call(start=(1 << 31) - 65 - 64, bt_len=big, ws_bytes=short) == Y.ENOSPC
+    assert call(start=(1 << 31) - 64 - 64, bt_len=big, ws_bytes=short) == Y.ERANGE
+    assert call(start=(1 << 63) - 1) == Y.ERANGE
     assert call(bt=None) == Y.EINVAL
     assert call(Hq=8) == Y.ENOTSUP
     assert call(T=-1) == Y.EINVAL
-    assert call(layer=_layer(dtype=Y.KV_NVFP4, k_scale=0x1, v_scale=0x1,
+    assert call(layer=_layer(dtype=Y.KV_NVFP4, k_scale=0x40000, v_scale=0x50000,
                              k_tensor_scale_dev=0x10, v_tensor_scale_dev=0x10)) == Y.ENOTSUP
-    assert call(layer=_layer(dtype=Y.KV_INT8, k_scale=0x1, v_scale=0x1)) == Y.ENOTSUP
+    assert call(layer=_layer(dtype=Y.KV_INT8, k_scale=0x40000, v_scale=0x50000)) == Y.ENOTSUP
     assert call(T=0, q=None, out=None) == Y.OK
     # the workspace holds one flag word per wave of the launch grid
     assert call(ws=None) == Y.EINVAL

@@ -174,3 +174,28 @@ def test_rope_append_keys_only_and_bad_position(Y):
     keep = np.arange(40) != 7
     assert np.array_equal(gk[keep], k_ref[keep])
     assert np.all(gk[7] == 0)                       # token 7's own block was never written
+
+
+def test_rope_append_negative_position_leaves_query_and_cache(Y):
+    """A negative position: that token's query is not roped, its key and
+    value are not written, and the position bit is set; the other tokens'
+    queries and keys are the oracle's."""
+    _say("rope_append negative position")
+    q, k, v, pos, table, blocks = _case(1401, 12, False)
+    pos_bad = pos.copy()
+    pos_bad[5] = -3
+    L = _layer(Y, Y.KV_BF16, blocks, False)
+    qd = _dev(q)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.rope_append(L, Y.YarnParams(), qd, _dev(k), _dev(v), None,
+                  torch.from_numpy(pos_bad.astype(np.int32)).to(DEV), err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == Y.DEVERR_POSITION
+    keep = np.arange(12) != 5
+    got_q = _bits(qd)
+    assert np.array_equal(got_q[5], q[5])
+    assert np.array_equal(got_q[keep], O.rope(q[keep], pos[keep], O.yarn_table(), bf16_out=True))
+    gk = _pool_rows(_bits(L.k).view(np.uint8), None, pos[keep], 512, blocks).view(np.uint16)
+    k_ref = O.rope(k[keep], pos[keep], O.yarn_table(), bf16_out=True)
+    assert np.array_equal(gk.reshape(k_ref.shape), k_ref)
+    assert np.all(_bits(L.k).reshape(blocks * 16, 4, 256)[pos[5]] == 0)   # never written

@@ -127,6 +127,27 @@ def test_rope_matches_oracle(Y, orig, corr, factor):
         assert np.array_equal(got[..., 64:], raw[..., 64:])
 
 
+def test_rope_negative_positions_are_flagged_and_left_unchanged(Y):
+    """A negative position is an error only the device sees: that token is
+    left as it is and the position bit is set; the others are roped."""
+    pos = np.array([5, -1, 262144, -(1 << 31), 1048575, -7], dtype=np.int64)
+    raw = synth.host_fill(79, synth.Q, 0, len(pos), 24, 256)
+    x = torch.from_numpy(raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Y.yarn_rope_apply(Y.YarnParams(), x, torch.from_numpy(pos.astype(np.int32)).to(DEV), err=err)
+    got = _bits(x)
+    bad = pos < 0
+    assert int(err.item()) == Y.DEVERR_POSITION
+    assert np.array_equal(got[bad], raw[bad])
+    ref = O.rope(raw[~bad], pos[~bad], O.yarn_table(), bf16_out=True)
+    assert np.array_equal(got[~bad], ref)
+    # no negative position: the word stays clear
+    err.zero_()
+    Y.yarn_rope_apply(Y.YarnParams(), x[:1], torch.tensor([3], dtype=torch.int32, device=DEV),
+                      err=err)
+    assert int(err.item()) == 0
+
+
 def test_rope_on_strided_rows(Y):
     """q heads inside a wider per-token row (a fused projection output)."""
     T, H = 9, 24

@@ -172,3 +172,65 @@ def test_bf16_rounding_is_nearest_even():
     assert tie.sum() >= 3
     exact = _rand_bits(rng, (1000,))
     assert np.array_equal(O.round_bf16(O.bf16_to_f64(exact)), exact)
+
+
+_PARAM_SETS = [dict(original_max_position=262144), dict(original_max_position=1024),
+               dict(original_max_position=262144, correction_max_position=1048576),
+               dict(original_max_position=4096, factor=1.0)]
+
+
+@pytest.mark.parametrize("kw", _PARAM_SETS)
+@pytest.mark.parametrize("rotary_dim", [64, 2, 256])
+def test_rope_bf16_is_one_rounding_of_the_fp64_rotation(kw, rotary_dim):
+    """The bf16 rope the GPU results are compared with is, bit for bit, the
+    pinned fp64 rotation rounded once to bf16 on the rotary dims, and a copy
+    of the input bits on the others (-0 and bf16 subnormals included)."""
+    rng = np.random.default_rng(11 + rotary_dim)
+    pos = np.concatenate([[0, 1, 262143, 262144, 1048575, 1048576],
+                          rng.integers(0, 1 << 21, 58)]).astype(np.int64)
+    T, H, D = len(pos), 5, 256
+    x = _rand_bits(rng, (T, H, D))
+    x[0, 0, :8] = [0x8000, 0x0000, 0x0001, 0x8001, 0x007F, 0x7F7F, 0xFF7F, 0x3F80]
+    x[1, 1, rotary_dim - 1] = 0x8000
+    x[2, 2, D - 1] = 0x8001
+    t = _table(rotary_dim=rotary_dim, **kw)
+    y16 = O.rope(x, pos, t, rotary_dim=rotary_dim, bf16_out=True)
+    y64 = O.rope(x, pos, t, rotary_dim=rotary_dim)
+    assert np.array_equal(y16[..., :rotary_dim], O.round_bf16(y64[..., :rotary_dim]))
+    assert np.array_equal(y16[..., rotary_dim:], x[..., rotary_dim:])
+
+
+def test_rope_bf16_at_position_zero_without_stretch_is_the_identity():
+    """Position 0 turns by nothing and factor 1 scales by nothing: every
+    element comes back bit for bit."""
+    rng = np.random.default_rng(12)
+    x = _rand_bits(rng, (16, 24, 256))
+    t = _table(factor=1.0)
+    assert t.mscale == 1.0
+    assert np.array_equal(O.rope(x, np.zeros(16, dtype=np.int64), t, bf16_out=True), x)
+
+
+def test_rope_bf16_single_pair_matches_numpy_rotation():
+    """With factor 1 and rotary_dim 2 the single pair turns by p radians; at
+    p = 0 nothing moves and the bf16 result of a turn by p is the correctly
+    rounded (x cos p - y sin p, y cos p + x sin p), checked here from numpy's
+    cos and sin, independently of the library's rotation loop."""
+    rng = np.random.default_rng(13)
+    x = _rand_bits(rng, (40, 3, 8))
+    pos = rng.integers(0, 1 << 20, 40).astype(np.int64)
+    t = _table(factor=1.0, rotary_dim=2)
+    assert t.inv_freq[0] == 1.0
+    y = O.rope(x, pos, t, rotary_dim=2, bf16_out=True)
+    a, b = O.bf16_to_f64(x[..., 0]), O.bf16_to_f64(x[..., 1])
+    c, s = np.cos(pos.astype(np.float64))[:, None], np.sin(pos.astype(np.float64))[:, None]
+    e0, e1 = a * c - b * s, b * c + a * s
+    # numpy's cos/sin may differ from libm's in the last bit: compare against
+    # the correctly rounded value with one bf16 step of slack only where the
+    # fp64 value lies within 1e-12 (relative) of a rounding boundary
+    for got, exact in ((y[..., 0], e0), (y[..., 1], e1)):
+        ref = O.round_bf16(exact)
+        near = np.abs(O.bf16_to_f64(O.round_bf16(exact * (1 + 1e-12))) -
+                      O.bf16_to_f64(O.round_bf16(exact * (1 - 1e-12)))) > 0
+        assert np.array_equal(got[~near], ref[~near])
+        assert np.all(np.abs(got[near].astype(np.int64) - ref[near].astype(np.int64)) <= 1)
+    assert np.array_equal(y[..., 2:], x[..., 2:])

@@ -64,7 +64,7 @@ _SIGS = {
     "yrk_abi_version": ([], ctypes.c_int),
     "yrk_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "yrk_yarn_table": ([ctypes.POINTER(_YarnParamsC), _P, _P, _P, _P], ctypes.c_int),
-    "yrk_yarn_rope_apply": ([ctypes.POINTER(_YarnParamsC), _P, _i64, _i32, _i64, _P, _P],
+    "yrk_yarn_rope_apply": ([ctypes.POINTER(_YarnParamsC), _P, _i64, _i32, _i64, _P, _P, _P],
                             ctypes.c_int),
     "yrk_nvfp4_tensor_scale": ([_P, _i64, _P, _P], ctypes.c_int),
     "yrk_kv_append_quantize": ([ctypes.POINTER(_KvLayerC), _P, _P, _i64, _P, _i64, _P, _P, _P],
@@ -137,14 +137,15 @@ def yarn_table(params: YarnParams):
     return inv, ms.value, lo.value, hi.value
 
 
-def yarn_rope_apply(params: YarnParams, x, positions):
+def yarn_rope_apply(params: YarnParams, x, positions, err=None):
     """Rotate x in place.  x: bf16 [T, H, head_dim] (token stride x.stride(0)),
-    positions: int32 [T] on the same device."""
+    positions: int32 [T] on the same device; err: optional uint32 device word."""
     T, H, D = x.shape
     assert x.stride(2) == 1 and x.stride(1) == D, "heads must be contiguous rows"
     cp = params.c()
     _check(_lib.yrk_yarn_rope_apply(ctypes.byref(cp), x.data_ptr(), T, H, x.stride(0),
-                                    positions.data_ptr(), _stream(x)), "yrk_yarn_rope_apply")
+                                    positions.data_ptr(), _ptr(err), _stream(x)),
+           "yrk_yarn_rope_apply")
     return x
 
 

@@ -10,7 +10,7 @@
 namespace yrk {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kAttnWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 constexpr int kRowBytesF16 = kHeadDim * 2;   // one staged 16-bit V row
@@ -115,7 +115,13 @@ __device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
 
 // Eight int8 codes (two dwords, element i in byte i) -> eight fp16 integers:
 // a byte c becomes fp16 1152 + c exactly (0x64 placed above c ^ 0x80 by a
-// byte permute), and one packed subtraction gives c.
+// byte permute), and one packed subtraction gives c.  This is the published
+// exponent-bias conversion (an integer written into the mantissa of a float
+// whose exponent makes one mantissa unit equal 1, then the bias subtracted),
+// used for int8 weights by Kim et al., "Who Says Elephants Can't Run:
+// Bringing Large Scale MoE Models into Cloud Scale Production", 2022; the
+// unsigned offset 0x80 keeps the whole int8 range on one exponent (1024 +
+// 128 + c).
 __device__ __forceinline__ uint4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
   const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
   const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;

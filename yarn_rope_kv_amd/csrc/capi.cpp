@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool is_finite(double x) { return __builtin_isfinite(x); }
 
@@ -20,9 +20,10 @@ bool is_finite(double x) { return __builtin_isfinite(x); }
 // high] holds the pairs whose number of full turns over the correction
 // length L lies between beta_slow and beta_fast; below it frequencies are
 // kept, from `high` up they are divided by the factor, in between a linear
-// ramp blends the two.
-int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32_t* lo_out,
-               int32_t* hi_out) {
+// ramp blends the two.  inv_freq holds `capacity` doubles: a table of more
+// pairs is refused (YRK_ENOTSUP) before anything is written.
+int yarn_table(const yrk_yarn_params* p, double* inv_freq, int capacity, double* mscale,
+               int32_t* lo_out, int32_t* hi_out) {
   if (!p) return YRK_EINVAL;
   const double base = p->rope_theta, s = p->factor;
   const int d = p->rotary_dim;
@@ -34,6 +35,7 @@ int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32
       p->beta_slow <= 0.0 || p->beta_slow > p->beta_fast)
     return YRK_EINVAL;
   if (!is_finite(p->mscale)) return YRK_EINVAL;
+  if (inv_freq && d / 2 > capacity) return YRK_ENOTSUP;
 
   const double L = (double)(p->correction_max_position > 0 ? p->correction_max_position
                                                            : p->original_max_position);
@@ -66,6 +68,8 @@ int yarn_table(const yrk_yarn_params* p, double* inv_freq, double* mscale, int32
   return YRK_OK;
 }
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 int check_layer(const yrk_kv_layer* L) {
   if (!L) return YRK_EINVAL;
   if (L->dtype != YRK_KV_BF16 && L->dtype != YRK_KV_NVFP4 && L->dtype != YRK_KV_INT8)
@@ -74,11 +78,21 @@ int check_layer(const yrk_kv_layer* L) {
     return YRK_EINVAL;
   if (L->paged != 0 && L->paged != 1) return YRK_EINVAL;
   if (L->reserved != 0) return YRK_EINVAL;
+  if (L->num_blocks > INT32_MAX) return YRK_ERANGE;   // block ids are int32
   if (!L->k || !L->v) return YRK_EINVAL;
   if (L->dtype == YRK_KV_NVFP4 &&
       (!L->k_scale || !L->v_scale || !L->k_tensor_scale_dev || !L->v_tensor_scale_dev))
     return YRK_EINVAL;
   if (L->dtype == YRK_KV_INT8 && (!L->k_scale || !L->v_scale)) return YRK_EINVAL;
+  // the kernels read code and value rows with 16-byte loads and the scale
+  // planes as whole rows (16 e4m3 bytes, or 4 binary16 words), the tensor
+  // scales as single floats
+  if (!aligned16(L->k) || !aligned16(L->v)) return YRK_EINVAL;
+  if (L->dtype != YRK_KV_BF16 && (!aligned16(L->k_scale) || !aligned16(L->v_scale)))
+    return YRK_EINVAL;
+  if (L->dtype == YRK_KV_NVFP4 && ((((uintptr_t)L->k_tensor_scale_dev) & 3u) != 0 ||
+                                   (((uintptr_t)L->v_tensor_scale_dev) & 3u) != 0))
+    return YRK_EINVAL;
   if (L->head_dim != yrk::kHeadDim || L->block_size != yrk::kBlockSize) return YRK_ENOTSUP;
   return YRK_OK;
 }
@@ -91,7 +105,17 @@ yrk::KvGeometry geometry(const yrk_kv_layer* L) {
   return g;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// Whether `pages` 16-token pages hold `tokens` tokens (0 <= tokens; no overflow).
+bool pages_hold(int64_t pages, int64_t tokens) {
+  return pages >= (tokens + yrk::kBlockSize - 1) / yrk::kBlockSize;
+}
+
+// Launch-grid limits of the split-K attention kernels: sequences and KV heads
+// are grid dimensions (at most 65,535), query heads index the merge grid.
+constexpr int32_t kMaxSeqs = 65535, kMaxKvHeads = 256, kMaxQHeads = 4096;
+bool shape_fits_grid(int64_t num_seqs, int64_t num_kv_heads, int64_t num_q_heads) {
+  return num_seqs <= kMaxSeqs && num_kv_heads <= kMaxKvHeads && num_q_heads <= kMaxQHeads;
+}
 
 int launch_status(hipError_t e) { return e == hipSuccess ? YRK_OK : YRK_EDEVICE; }
 
@@ -115,16 +139,16 @@ const char* yrk_status_string(int status) {
 
 int yrk_yarn_table(const yrk_yarn_params* params, double* inv_freq_out, double* mscale_out,
                    int32_t* corr_low_out, int32_t* corr_high_out) {
-  return yarn_table(params, inv_freq_out, mscale_out, corr_low_out, corr_high_out);
+  // the caller provides rotary_dim / 2 doubles
+  return yarn_table(params, inv_freq_out, INT32_MAX, mscale_out, corr_low_out, corr_high_out);
 }
 
 int yrk_yarn_rope_apply(const yrk_yarn_params* params, void* x_dev, int64_t num_tokens,
                         int32_t num_heads, int64_t token_stride, const int32_t* positions_dev,
-                        hipStream_t stream) {
+                        uint32_t* dev_error_word, hipStream_t stream) {
   yrk::RopeArgs a;
-  int rc = yarn_table(params, a.inv_freq, &a.mscale, nullptr, nullptr);
+  int rc = yarn_table(params, a.inv_freq, yrk::kMaxRotaryHalf, &a.mscale, nullptr, nullptr);
   if (rc) return rc;
-  if (params->rotary_dim / 2 > yrk::kMaxRotaryHalf) return YRK_ENOTSUP;
   if (num_tokens < 0 || num_heads <= 0) return YRK_EINVAL;
   if (token_stride < (int64_t)num_heads * params->head_dim) return YRK_EINVAL;
   if (num_tokens == 0) return YRK_OK;
@@ -136,6 +160,7 @@ int yrk_yarn_rope_apply(const yrk_yarn_params* params, void* x_dev, int64_t num_
   a.token_stride = token_stride;
   a.half = params->rotary_dim / 2;
   a.positions = positions_dev;
+  a.err = dev_error_word;
   return launch_status(yrk::launch_rope(a, stream));
 }
 
@@ -186,8 +211,7 @@ int yrk_rope_append(const yrk_kv_layer* layer, const yrk_yarn_params* params, vo
   int rc = check_layer(layer);
   if (rc) return rc;
   yrk::RopeAppendArgs ra;
-  double inv_freq[yrk::kMaxRotaryHalf];
-  rc = yarn_table(params, inv_freq, &ra.mscale, nullptr, nullptr);
+  rc = yarn_table(params, ra.inv_freq, yrk::kFusedRopePairs, &ra.mscale, nullptr, nullptr);
   if (rc) return rc;
   if (params->head_dim != yrk::kHeadDim || params->rotary_dim != 2 * yrk::kFusedRopePairs)
     return YRK_ENOTSUP;
@@ -202,7 +226,6 @@ int yrk_rope_append(const yrk_kv_layer* layer, const yrk_yarn_params* params, vo
   if (!k_dev || !v_dev || !positions_dev) return YRK_EINVAL;
   if (!aligned16(k_dev) || !aligned16(v_dev) || !aligned16(layer->k) || !aligned16(layer->v))
     return YRK_EINVAL;
-  for (int i = 0; i < yrk::kFusedRopePairs; ++i) ra.inv_freq[i] = inv_freq[i];
   ra.q = static_cast<uint16_t*>(q_dev);
   ra.num_q_heads = q_dev ? num_q_heads : 0;
   ra.q_token_stride = q_dev ? q_token_stride : 0;
@@ -228,7 +251,8 @@ int yrk_rope_append(const yrk_kv_layer* layer, const yrk_yarn_params* params, vo
 size_t yrk_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int64_t max_seq_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != yrk::kHeadDim ||
-      max_seq_len < 0)
+      max_seq_len < 0 || max_seq_len > INT32_MAX ||
+      !shape_fits_grid(num_seqs, num_kv_heads, num_q_heads))
     return 0;
   // the cache format is not an argument here: enough for either plan
   const size_t b16 = yrk::decode_workspace_bytes(
@@ -251,6 +275,7 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   if (rc) return rc;
   if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len < 0) return YRK_EINVAL;
   if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (!shape_fits_grid(num_seqs, layer->num_kv_heads, num_q_heads)) return YRK_ENOTSUP;
   if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
   if (!q_dev || !seq_lens_dev || !out_dev || !workspace_dev) return YRK_EINVAL;
   if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
@@ -260,12 +285,12 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
     return YRK_ENOTSUP;
   if (layer->paged) {
     if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
-    if (max_seq_len > block_table_stride * yrk::kBlockSize) return YRK_ERANGE;
-  } else {
-    if (num_seqs != 1) return YRK_EINVAL;
-    if (max_seq_len > layer->num_blocks * yrk::kBlockSize) return YRK_ERANGE;
+  } else if (num_seqs != 1) {
+    return YRK_EINVAL;
   }
   if (max_seq_len > INT32_MAX) return YRK_ERANGE;
+  if (!pages_hold(layer->paged ? block_table_stride : layer->num_blocks, max_seq_len))
+    return YRK_ERANGE;
   yrk::DecodeArgs a;
   a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len, layer->dtype);
   const size_t need = yrk::decode_workspace_bytes(num_seqs, num_q_heads, a.plan);
@@ -301,7 +326,9 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
 size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int64_t max_seq_len) {
   if (num_seqs <= 0 || num_queries <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      head_dim != yrk::kHeadDim || max_seq_len < 0 || num_q_heads % num_kv_heads)
+      head_dim != yrk::kHeadDim || max_seq_len < 0 || max_seq_len > INT32_MAX ||
+      num_q_heads % num_kv_heads ||
+      !shape_fits_grid(num_seqs, num_kv_heads, num_q_heads) || num_queries > yrk::kVerifyMaxRows)
     return 0;
   const int64_t rows = (int64_t)num_queries * (num_q_heads / num_kv_heads);
   if (rows > yrk::kVerifyMaxRows) return 0;
@@ -327,6 +354,9 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   if (num_seqs <= 0 || num_queries <= 0 || num_q_heads <= 0 || max_seq_len < 0)
     return YRK_EINVAL;
   if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (!shape_fits_grid(num_seqs, layer->num_kv_heads, num_q_heads) ||
+      num_queries > yrk::kVerifyMaxRows)
+    return YRK_ENOTSUP;
   if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
   if (!q_dev || !seq_lens_dev || !out_dev || !workspace_dev) return YRK_EINVAL;
   if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
@@ -340,12 +370,12 @@ int yrk_verify_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
   if ((int64_t)num_queries * group > yrk::kVerifyMaxRows) return YRK_ENOTSUP;
   if (layer->paged) {
     if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
-    if (max_seq_len > block_table_stride * yrk::kBlockSize) return YRK_ERANGE;
-  } else {
-    if (num_seqs != 1) return YRK_EINVAL;
-    if (max_seq_len > layer->num_blocks * yrk::kBlockSize) return YRK_ERANGE;
+  } else if (num_seqs != 1) {
+    return YRK_EINVAL;
   }
   if (max_seq_len > INT32_MAX) return YRK_ERANGE;
+  if (!pages_hold(layer->paged ? block_table_stride : layer->num_blocks, max_seq_len))
+    return YRK_ERANGE;
   yrk::VerifyArgs va;
   yrk::DecodeArgs& a = va.d;
   va.num_queries = num_queries;
@@ -399,11 +429,11 @@ int yrk_prefill_attention(const yrk_kv_layer* layer, const void* q_dev, int64_t 
   if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
   if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
   if (layer->paged && (!block_table_dev || block_table_len <= 0)) return YRK_EINVAL;
+  // the kernel forms key bounds up to two 32-key tiles past the chunk's end in int32
+  if (q_start_position > INT32_MAX || num_q_tokens > INT32_MAX) return YRK_ERANGE;
   const int64_t end = q_start_position + num_q_tokens;
-  if (end > INT32_MAX) return YRK_ERANGE;
-  if (layer->paged ? end > block_table_len * yrk::kBlockSize
-                   : end > layer->num_blocks * yrk::kBlockSize)
-    return YRK_ERANGE;
+  if (end > (int64_t)INT32_MAX - 64) return YRK_ERANGE;
+  if (!pages_hold(layer->paged ? block_table_len : layer->num_blocks, end)) return YRK_ERANGE;
   if (num_q_tokens == 0) return YRK_OK;
   if (!q_dev || !out_dev) return YRK_EINVAL;
   if (!aligned16(q_dev) || !aligned16(out_dev)) return YRK_EINVAL;

@@ -714,47 +714,6 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Workgroups a decode launch aims for: the split kernels keep two resident
-// per CU and get a single round of them (measured: 1,024 bf16 workgroups, two
-// rounds, were 1.5% slower at 24 q / 4 KV heads and 10% slower at 12 q / 2
-// KV heads, where each split then holds only 2,048 tokens; 768, 1,024 and
-// 2,048 NVFP4 workgroups were 22%, 5% and 11% slower than 512).  The bf16
-// cache runs the one-query verify kernel, which is planned the same way.
-constexpr int64_t kTargetWgsBf16 = 512;
-constexpr int64_t kTargetWgsF4 = 512;
-constexpr int64_t kTargetWgsI8 = 512;
-
-DecodePlan split_plan(int64_t units, int64_t max_seq_len, int64_t target_wgs) {
-  const int64_t unit = (int64_t)kWaves * kBlockSize;           // 64 tokens
-  // 64-token chunks; at least one, so that an empty range still gets a
-  // split (its workgroups find no page and write empty partials)
-  const int64_t chunks = max((max_seq_len + unit - 1) / unit, (int64_t)1);
-  // as many splits as keep units x splits within the target: workgroups
-  // beyond one round would run after it, few of them and alone (15
-  // sequences x 4 KV heads: 8 splits, 480 workgroups, rather than 540)
-  int64_t splits = target_wgs / units;
-  if (splits > chunks) splits = chunks;
-  if (splits < 1) splits = 1;
-  const int64_t per = (chunks + splits - 1) / splits;          // chunks per split
-  DecodePlan p;
-  p.tokens_per_split = per * unit;
-  p.num_splits = (int32_t)((chunks + per - 1) / per);
-  if (p.num_splits < 1) p.num_splits = 1;
-  return p;
-}
-
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int64_t max_seq_len, int32_t dtype) {
-  const int64_t target_wgs = dtype == 0 ? kTargetWgsBf16 : (dtype == 1 ? kTargetWgsF4 : kTargetWgsI8);
-  return split_plan((int64_t)num_seqs * num_kv_heads, max_seq_len, target_wgs);
-}
-
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const DecodePlan& p) {
-  const size_t slots = (size_t)num_seqs * num_q_heads * p.num_splits;
-  const size_t o = slots * kHeadDim * sizeof(float);
-  const size_t lse = slots * sizeof(float);
-  return ((o + 255) / 256) * 256 + ((lse + 255) / 256) * 256;
-}
-
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.dtype == 0) {
     // bf16: the verify kernels with one query at position len - 1, which sees

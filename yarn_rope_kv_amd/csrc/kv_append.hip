@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
       c[j] = bpermute_f64(4 * (lane & 7) + j, cl);
       sn[j] = bpermute_f64(4 * (lane & 7) + j, sl);
     }
-    if (ra.q) {
+    if (ra.q && pos >= 0) {         // a negative position is flagged below, q left as it is
       for (int h0 = 0; h0 < ra.num_q_heads; h0 += 4) {
         const int h = h0 + (lane >> 4);
         const int hl = h < ra.num_q_heads ? h : ra.num_q_heads - 1;   // every lane shuffles

@@ -7,15 +7,16 @@
 //
 // Work decomposition
 //   rows       a (token, query head) pair is one row, R = 6 x token + head
-//              within the GQA group of KV head g.  A workgroup owns 128
-//              consecutive rows (about 21 tokens x the 6 heads that share g),
-//              so every K/V tile in LDS serves the whole group.
+//              within the GQA group of KV head g.  A workgroup owns 192
+//              consecutive rows (32 tokens x the 6 heads that share g), so
+//              every K/V tile in LDS serves the whole group.
 //   workgroup  4 waves, one per SIMD (a wave may hold 512 registers; Q and O
-//              for 32 rows of head dim 256 take 192).
-//   wave       32 rows as 2 blocks of 16.  Per 32 keys, with
+//              for 48 rows of head dim 256 take 288).
+//   wave       48 rows as 3 blocks of 16.  Per 32 keys, with
 //              v_mfma_f32_16x16x32_bf16:
-//                S^T[32 keys x 32 rows]  = K . Q^T        32 MFMA
-//                O^T[256 x 32 rows]     += V^T . P^T      32 MFMA
+//                S^T[32 keys x 48 rows]  = K . Q^T        48 MFMA
+//                O^T[256 x 48 rows]     += V^T . P^T      48 MFMA
+//                row sums                 = P . ones        3 MFMA
 //              The S^T accumulator gives lane l (row l%16 of a block, quad q =
 //              l/16) keys 16kb + 4q + i (i < 4).  The P^T operand of a 32-key
 //              PV step needs, in lane l, operand slots 8q .. 8q+7; mapping
@@ -36,10 +37,18 @@
 //              L at key 4q + L/4, dims 16d + 4(L%4) .. +3 gives lane j the
 //              values of dim 16d + j at keys 4q .. 4q+3 -- the V^T operand
 //              in the key order of P^T.
-//   softmax    online, per row, log2 domain.  The running maximum is raised
-//              (and O rescaled) only when a tile's maximum exceeds it by more
-//              than 8, so p <= 2^8 and O is rarely touched.  P is rounded to
-//              bf16 for the MFMA and the row sum adds the same rounded values.
+//   softmax    log2 domain, with a fixed maximum per row: each row takes off
+//              the maximum of its first key tile (keys 0..31, which every
+//              causal row sees) and keeps it for every later tile, so the
+//              tile loop carries no running maximum and never rescales O.
+//              The first tile adds exactly 1 to the row sum l and every p is
+//              at most l; a wave whose rows end with l > 2^64 or a
+//              non-finite O sets its flag word in the workspace, and a
+//              second launch on the same grid recomputes those workgroups
+//              with a running maximum raised lazily (by more than 8, so
+//              p <= 2^8) and O rescaled; its other workgroups return at once.
+//              P is rounded to bf16 for the MFMA and the row sum adds the
+//              same rounded values.
 //   masking    a row at position p sees keys <= p; only tiles that reach past
 //              the smallest row position of the workgroup test it per key.
 //              Rows that are never attended (past the chunk, or in a page
@@ -61,11 +70,12 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-constexpr int kGroup = 6;                 // query heads per KV head
-constexpr int kWavesP = 4;
+constexpr int kGroup = kPrefillGroup;     // query heads per KV head
+constexpr int kWavesP = kPrefillWaves;
 constexpr int kPThreads = 64 * kWavesP;   // 256
 constexpr int kRowsPerWave = 48;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;   // 192 (token, head) rows = 32 tokens
+static_assert(kRowsPerWG == kPrefillRowsPerWG, "the planner's workgroup rows");
 constexpr int kRB = kRowsPerWave / 16;    // 3 row blocks per wave
 constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per row
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
   const int r16 = lane & 15, q4 = lane >> 4;
   const int64_t row0 = (int64_t)tile * kRowsPerWG;   // first (token, head) row
 
-  // rows of this lane: row block rb -> R = row0 + 32 wave + 16 rb + r16 = 6 token + head
+  // rows of this lane: row block rb -> R = row0 + 48 wave + 16 rb + r16 = 6 token + head
   int64_t tok[kRB];
   int32_t pos[kRB];                                   // positions fit in 32 bits
   int head[kRB];
@@ -757,31 +767,6 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 }
 
 }  // namespace
-
-namespace {
-// Launch grid: workgroups numbered so that each XCD (block id mod 8) serves
-// one KV head when the head count divides 8.
-struct PrefillGrid {
-  int32_t tiles, share;
-  int64_t blocks;
-};
-PrefillGrid prefill_grid(int64_t num_q_tokens, int32_t num_kv_heads) {
-  PrefillGrid gr;
-  gr.tiles = (int32_t)((num_q_tokens * kGroup + kRowsPerWG - 1) / kRowsPerWG);
-  gr.share = 0;
-  gr.blocks = (int64_t)gr.tiles * num_kv_heads;
-  if (num_kv_heads <= 8 && 8 % num_kv_heads == 0) {
-    gr.share = 8 / num_kv_heads;   // XCDs per KV head
-    gr.blocks = 8 * (((int64_t)gr.tiles + gr.share - 1) / gr.share);
-  }
-  return gr;
-}
-}  // namespace
-
-size_t prefill_workspace_bytes(int64_t num_q_tokens, int32_t num_q_heads) {
-  if (num_q_tokens <= 0 || num_q_heads % kGroup) return 0;
-  return (size_t)prefill_grid(num_q_tokens, num_q_heads / kGroup).blocks * kWavesP * sizeof(uint32_t);
-}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.group != kGroup) return hipErrorInvalidValue;

@@ -30,6 +30,7 @@ struct RopeKernelArgs {
   int32_t head_dim;
   int32_t half;
   const int32_t* positions;
+  uint32_t* err;
   double mscale;
   double inv_freq[kMaxRotaryHalf];
 };
@@ -39,8 +40,13 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeKernelArgs a) {
   for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < a.total; gid += stride) {
     const int64_t t = gid / a.half;
     const int i = (int)(gid - t * a.half);
+    const int32_t pos = a.positions[t];
+    if (pos < 0) {                  // the token is left as it is and reported
+      if (i == 0) set_error(a.err, kErrPosition);
+      continue;
+    }
     double c, s;
-    rope_cos_sin(a.positions[t], a.inv_freq[i], a.mscale, &c, &s);
+    rope_cos_sin(pos, a.inv_freq[i], a.mscale, &c, &s);
     uint16_t* row = a.x + t * a.token_stride + i;
     for (int h = 0; h < a.num_heads; ++h) {
       uint16_t* p = row + (int64_t)h * a.head_dim;
@@ -63,6 +69,7 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
   k.head_dim = a.head_dim;
   k.half = a.half;
   k.positions = a.positions;
+  k.err = a.err;
   k.mscale = a.mscale;
   for (int i = 0; i < kMaxRotaryHalf; ++i) k.inv_freq[i] = i < a.half ? a.inv_freq[i] : 0.0;
   if (k.total == 0) return hipSuccess;

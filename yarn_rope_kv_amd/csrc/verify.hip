@@ -45,7 +45,7 @@
 namespace yrk {
 namespace {
 
-constexpr int kColRows = 16;                                        // rows per MFMA column block
+constexpr int kColRows = kVerifyColRows;                            // rows per MFMA column block
 constexpr int kStageBytesV = kWaves * kBlockSize * kRowBytesF16;    // 32 KiB: one V page per wave
 constexpr int kQOpBytes = 8 * 64 * 16;                              // Q^T operands of a block: 8 KiB
 constexpr int kFinishBytes = (kWaves * kColRows * kHeadDim + 2 * kWaves * kColRows) * 4;
@@ -80,9 +80,9 @@ __device__ __forceinline__ u32x4_t split_weights(const float (&p)[4]) {
 // against 0.815 ms with one workgroup and one page ahead); three column
 // blocks hold 192 accumulator registers and leave room for one workgroup.
 template <int C> struct VerifyTune;
-template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWgsPerCu = 2; };
-template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWgsPerCu = 2; };
-template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWgsPerCu = 1; };
+template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(1, 0); };
+template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWgsPerCu = verify_wgs_per_cu(2, 0); };
+template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(3, 0); };
 
 // One lane's share of one page: 16-byte chunks 4 j + kg of key and value
 // row t (head dims 32 j + 8 kg .. +7).
@@ -325,9 +325,9 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
 // C = 3, one workgroup per CU, 0.941 / 0.897 / 0.819 ms with 0 / 1 / 2
 // pages ahead (one wave per SIMD leaves latency exposed).
 template <int C> struct VerifyTuneI8;
-template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWgsPerCu = 2; };
-template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWgsPerCu = 2; };
-template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWgsPerCu = 1; };
+template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(1, 2); };
+template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWgsPerCu = verify_wgs_per_cu(2, 2); };
+template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWgsPerCu = verify_wgs_per_cu(3, 2); };
 
 // One lane's share of one page.
 struct I8VUnit {
@@ -626,22 +626,7 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
 
 int column_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
-int wgs_per_cu(int rows, int32_t dtype) {
-  const int c = column_blocks(rows);
-  if (dtype == 2)
-    return c == 1 ? VerifyTuneI8<1>::kWgsPerCu
-                  : (c == 2 ? VerifyTuneI8<2>::kWgsPerCu : VerifyTuneI8<3>::kWgsPerCu);
-  return c == 1 ? VerifyTune<1>::kWgsPerCu
-                : (c == 2 ? VerifyTune<2>::kWgsPerCu : VerifyTune<3>::kWgsPerCu);
-}
-
 }  // namespace
-
-// One round of workgroups over the 256 CUs.
-DecodePlan plan_verify(int32_t num_seqs, int32_t num_kv_heads, int32_t rows, int64_t max_seq_len,
-                       int32_t dtype) {
-  return split_plan((int64_t)num_seqs * num_kv_heads, max_seq_len, 256 * wgs_per_cu(rows, dtype));
-}
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const DecodeArgs& d = a.d;

@@ -13,6 +13,21 @@ namespace yrk {
 constexpr int kHeadDim = 256;   // elements per head this build supports
 constexpr int kBlockSize = 16;  // tokens per KV page
 constexpr int kMaxRotaryHalf = 128;
+
+// Launch shapes that the host planners (plan.cpp) and the kernels share.
+constexpr int kAttnWaves = 4;          // waves per split-K attention workgroup
+constexpr int kVerifyColRows = 16;     // query rows per MFMA column block of the verify kernels
+// Workgroups per CU of the verify kernels by column blocks (1..3) and cache
+// format (YRK_KV_INT8 = 2, else bf16): two waves per SIMD where the
+// registers allow; three column blocks hold 192 accumulator registers and
+// leave room for one workgroup.
+constexpr int verify_wgs_per_cu(int column_blocks, int32_t dtype) {
+  (void)dtype;
+  return column_blocks <= 2 ? 2 : 1;
+}
+constexpr int kPrefillGroup = 6;       // query heads per KV head of the prefill kernel
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowsPerWG = 192; // (token, head) rows per prefill workgroup: 32 tokens
 constexpr uint32_t kErrBlockId = 1u;   // same bits as YRK_DEVERR_BLOCK_ID
 constexpr uint32_t kErrPosition = 2u;  // same bits as YRK_DEVERR_POSITION
 
@@ -24,6 +39,7 @@ struct RopeArgs {
   int64_t token_stride;
   int32_t half;                    // rotary_dim / 2
   const int32_t* positions;
+  uint32_t* err;                   // nullable; negative positions set kErrPosition
   double mscale;
   double inv_freq[kMaxRotaryHalf];
 };
@@ -141,6 +157,14 @@ struct PrefillArgs {
   uint32_t* err;
   uint32_t* flags;           // one word per wave of the main kernel (workspace)
 };
+// Prefill launch grid: `tiles` workgroup row tiles of kPrefillRowsPerWG rows
+// per KV head; with `share` > 0 the workgroups are numbered so that each XCD
+// (block id mod 8) serves one KV head, `share` XCDs per head.
+struct PrefillGrid {
+  int32_t tiles, share;
+  int64_t blocks;
+};
+PrefillGrid prefill_grid(int64_t num_q_tokens, int32_t num_kv_heads);
 // Bytes of prefill workspace: one flag word per wave of the launch grid
 // (0 when the shape is not supported; the call then fails on its own).
 size_t prefill_workspace_bytes(int64_t num_q_tokens, int32_t num_q_heads);
