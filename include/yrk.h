@@ -288,6 +288,31 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
                          uint32_t* dev_error_word, hipStream_t stream);
 
 /*
+ * yrk_decode_attention_noalloc -- yrk_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split partials go to a device array inside the library of
+ * YRK_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends; the call allocates nothing.  The array's
+ * address on a device is looked up on the first call made with that device
+ * current, and every later call on that device uses it; the caller's stream
+ * must belong to the current device.  Calls that overlap on one GPU (other
+ * streams, other threads) share the array and race: serialise them.
+ * Arguments, results and errors are those of yrk_decode_attention, plus
+ * YRK_ENOSPC when the shapes need more than YRK_NOALLOC_SCRATCH_BYTES of
+ * partials (yrk_decode_workspace_size() > the scratch size; 16 MiB covers,
+ * e.g., one sequence of any length at 24 q / 4 KV heads, or 15 sequences),
+ * and YRK_EDEVICE when the array's address cannot be looked up.
+ */
+#define YRK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int yrk_decode_attention_noalloc(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                                 int32_t num_q_heads, const int32_t* block_tables_dev,
+                                 int64_t block_table_stride, const int32_t* seq_lens_dev,
+                                 int64_t max_seq_len, float softmax_scale, void* out_dev,
+                                 int32_t out_dtype, uint32_t* dev_error_word,
+                                 hipStream_t stream);
+
+/*
  * yrk_verify_workspace_size -- bytes of device workspace that
  * yrk_verify_attention needs for these shapes (the split partials of every
  * (sequence, query, query head)); 0 for invalid sizes.

@@ -152,7 +152,7 @@ int main(int argc, char** argv) {
   for (long it = 0; it < iters; ++it) {
     const yrk_yarn_params P = random_params();
     const yrk_kv_layer L = random_layer();
-    const int which = pick(8);
+    const int which = pick(9);
     const long before = yrk::g_launches;
     int s = 0;
     const char* name = "";
@@ -208,6 +208,24 @@ int main(int argc, char** argv) {
                                  bytes, (uint32_t*)any_ptr(0x5000), nullptr);
         if (need && bytes == need)
           check(s != YRK_ENOSPC, "decode refused the workspace its size query gave", it);
+        break;
+      }
+      case 8: {
+        name = "yrk_decode_attention_noalloc";
+        const int32_t S = chance(70) ? 1 + pick(64) : any_i32(1);
+        const int32_t Hq = any_i32(24);
+        const int64_t N = chance(70) ? (int64_t)pick(1 << 21) : any_i64(1 << 20);
+        const int64_t stride = any_i64(N < 0 || N > INT64_MAX - 16 ? 1 : (N + 15) / 16 + 1);
+        const size_t need = yrk_decode_workspace_size(S, Hq, L.num_kv_heads, L.head_dim, N);
+        s = yrk_decode_attention_noalloc(&L, any_ptr(0x1000), S, Hq,
+                                         (const int32_t*)any_ptr(0x2000), stride,
+                                         (const int32_t*)any_ptr(0x3000), N, (float)any_f64(0.0),
+                                         any_ptr(0x4000), any_i32(pick(2)),
+                                         (uint32_t*)any_ptr(0x5000), nullptr);
+        if (need && need <= YRK_NOALLOC_SCRATCH_BYTES)
+          check(s != YRK_ENOSPC, "noalloc decode refused shapes that fit its scratch", it);
+        if (need > YRK_NOALLOC_SCRATCH_BYTES)
+          check(s != YRK_OK, "noalloc decode accepted shapes beyond its scratch", it);
         break;
       }
       case 6: {

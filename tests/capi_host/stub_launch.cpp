@@ -85,6 +85,13 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t device_scratch(void** ptr) {
+  // a host stand-in of the library's device scratch, of the same size
+  static unsigned char* buf = static_cast<unsigned char*>(malloc(kNoAllocScratchBytes));
+  *ptr = buf;
+  return hipSuccess;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t) {
   if (a.group != kPrefillGroup || a.num_q_tokens <= 0) fail("prefill shape");
   if (a.q_start + a.num_q_tokens > (int64_t)INT32_MAX - 64) fail("prefill positions");

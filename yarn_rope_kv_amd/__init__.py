@@ -74,6 +74,8 @@ _SIGS = {
     "yrk_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i64], ctypes.c_size_t),
     "yrk_decode_attention": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _P, _i64, _P, _i64, _f,
                               _P, _i32, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "yrk_decode_attention_noalloc": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _P, _i64, _P,
+                                      _i64, _f, _P, _i32, _P, _P], ctypes.c_int),
     "yrk_verify_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i64], ctypes.c_size_t),
     "yrk_verify_attention": ([ctypes.POINTER(_KvLayerC), _P, _i32, _i32, _i32, _P, _i64, _P, _i64,
                               _f, _P, _i32, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
@@ -244,6 +246,26 @@ def decode_attention(layer: KVLayer, q, block_tables, seq_lens, max_seq_len, out
                                      softmax_scale, out.data_ptr(), out_dtype,
                                      workspace.data_ptr(), _nbytes(workspace), _ptr(err),
                                      _stream(q)), "yrk_decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_attention_noalloc(layer: KVLayer, q, block_tables, seq_lens, max_seq_len, out,
+                             softmax_scale=0.0, err=None):
+    """decode_attention with the partials in the library's device scratch
+    (no workspace, no allocation); calls on one GPU must not overlap."""
+    import torch
+    S, Hq, _ = q.shape
+    lc = layer.c()
+    bt_stride = block_tables.shape[1] if block_tables is not None else 0
+    out_dtype = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(_lib.yrk_decode_attention_noalloc(ctypes.byref(lc), q.data_ptr(), S, Hq,
+                                             _ptr(block_tables), bt_stride, seq_lens.data_ptr(),
+                                             max_seq_len, softmax_scale, out.data_ptr(),
+                                             out_dtype, _ptr(err), _stream(q)),
+           "yrk_decode_attention_noalloc")
     return out
 
 

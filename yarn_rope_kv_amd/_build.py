@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "yrk")
 LIB = os.path.join(HERE, "libyrk.so")
-SOURCES = ["capi.cpp", "plan.cpp", "rope.hip", "kv_append.hip", "decode.hip", "verify.hip", "prefill.hip"]
+SOURCES = ["capi.cpp", "plan.cpp", "rope.hip", "kv_append.hip", "decode.hip", "verify.hip",
+           "prefill.hip", "noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -8,6 +8,8 @@
 
 #include "yrk_internal.h"
 
+static_assert(YRK_NOALLOC_SCRATCH_BYTES == yrk::kNoAllocScratchBytes, "one scratch size");
+
 namespace {
 
 constexpr int kAbiVersion = 2;
@@ -118,6 +120,71 @@ bool shape_fits_grid(int64_t num_seqs, int64_t num_kv_heads, int64_t num_q_heads
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? YRK_OK : YRK_EDEVICE; }
+
+// Decode attention behind both entry points.  workspace_dev == nullptr
+// selects the library's device scratch (yrk_decode_attention_noalloc), taken
+// only after every host check has passed; workspace_bytes is then its size.
+int decode_call(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                int32_t num_q_heads, const int32_t* block_tables_dev,
+                int64_t block_table_stride, const int32_t* seq_lens_dev, int64_t max_seq_len,
+                float softmax_scale, void* out_dev, int32_t out_dtype, void* workspace_dev,
+                size_t workspace_bytes, uint32_t* dev_error_word, hipStream_t stream) {
+  int rc = check_layer(layer);
+  if (rc) return rc;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len < 0) return YRK_EINVAL;
+  if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
+  if (!shape_fits_grid(num_seqs, layer->num_kv_heads, num_q_heads)) return YRK_ENOTSUP;
+  if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
+  if (!q_dev || !seq_lens_dev || !out_dev) return YRK_EINVAL;
+  if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
+  if (!aligned16(q_dev) || !aligned16(workspace_dev)) return YRK_EINVAL;   // null is aligned
+  const int group = num_q_heads / layer->num_kv_heads;
+  if (group != 1 && group != 2 && group != 3 && group != 4 && group != 6)
+    return YRK_ENOTSUP;
+  if (layer->paged) {
+    if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
+  } else if (num_seqs != 1) {
+    return YRK_EINVAL;
+  }
+  if (max_seq_len > INT32_MAX) return YRK_ERANGE;
+  if (!pages_hold(layer->paged ? block_table_stride : layer->num_blocks, max_seq_len))
+    return YRK_ERANGE;
+  yrk::DecodeArgs a;
+  a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len, layer->dtype);
+  const size_t need = yrk::decode_workspace_bytes(num_seqs, num_q_heads, a.plan);
+  if (workspace_bytes < need) return YRK_ENOSPC;
+  if (!workspace_dev) {
+    const hipError_t e = yrk::device_scratch(&workspace_dev);
+    if (e != hipSuccess) return YRK_EDEVICE;
+  }
+  if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
+  a.geo = geometry(layer);
+  a.dtype = layer->dtype;
+  a.group = group;
+  a.num_q_heads = num_q_heads;
+  a.num_seqs = num_seqs;
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.k = layer->k;
+  a.v = layer->v;
+  a.k_scale = static_cast<const uint8_t*>(layer->k_scale);
+  a.v_scale = static_cast<const uint8_t*>(layer->v_scale);
+  a.k_tensor_scale = layer->k_tensor_scale_dev;
+  a.v_tensor_scale = layer->v_tensor_scale_dev;
+  a.block_tables = layer->paged ? block_tables_dev : nullptr;
+  a.block_table_stride = layer->paged ? block_table_stride : 0;
+  a.seq_lens = seq_lens_dev;
+  a.max_seq_len = max_seq_len;
+  a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
+  a.out = out_dev;
+  a.out_f32 = out_dtype == YRK_OUT_F32;
+  const size_t slots = (size_t)num_seqs * num_q_heads * a.plan.num_splits;
+  a.ws_o = static_cast<float*>(workspace_dev);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace_dev) +
+                                      ((slots * yrk::kHeadDim * sizeof(float) + 255) / 256) * 256);
+  a.err = dev_error_word;
+  return launch_status(yrk::launch_decode(a, stream));
+}
+
 
 }  // namespace
 
@@ -271,56 +338,23 @@ int yrk_decode_attention(const yrk_kv_layer* layer, const void* q_dev, int32_t n
                          int64_t max_seq_len, float softmax_scale, void* out_dev,
                          int32_t out_dtype, void* workspace_dev, size_t workspace_bytes,
                          uint32_t* dev_error_word, hipStream_t stream) {
-  int rc = check_layer(layer);
-  if (rc) return rc;
-  if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len < 0) return YRK_EINVAL;
-  if (num_q_heads % layer->num_kv_heads) return YRK_EINVAL;
-  if (!shape_fits_grid(num_seqs, layer->num_kv_heads, num_q_heads)) return YRK_ENOTSUP;
-  if (out_dtype != YRK_OUT_BF16 && out_dtype != YRK_OUT_F32) return YRK_EINVAL;
-  if (!q_dev || !seq_lens_dev || !out_dev || !workspace_dev) return YRK_EINVAL;
-  if (!is_finite(softmax_scale) || softmax_scale < 0.0f) return YRK_EINVAL;
-  if (!aligned16(q_dev) || !aligned16(workspace_dev)) return YRK_EINVAL;
-  const int group = num_q_heads / layer->num_kv_heads;
-  if (group != 1 && group != 2 && group != 3 && group != 4 && group != 6)
-    return YRK_ENOTSUP;
-  if (layer->paged) {
-    if (!block_tables_dev || block_table_stride <= 0) return YRK_EINVAL;
-  } else if (num_seqs != 1) {
-    return YRK_EINVAL;
-  }
-  if (max_seq_len > INT32_MAX) return YRK_ERANGE;
-  if (!pages_hold(layer->paged ? block_table_stride : layer->num_blocks, max_seq_len))
-    return YRK_ERANGE;
-  yrk::DecodeArgs a;
-  a.plan = yrk::plan_decode(num_seqs, layer->num_kv_heads, max_seq_len, layer->dtype);
-  const size_t need = yrk::decode_workspace_bytes(num_seqs, num_q_heads, a.plan);
-  if (workspace_bytes < need) return YRK_ENOSPC;
-  if (softmax_scale == 0.0f) softmax_scale = 1.0f / sqrtf((float)layer->head_dim);
-  a.geo = geometry(layer);
-  a.dtype = layer->dtype;
-  a.group = group;
-  a.num_q_heads = num_q_heads;
-  a.num_seqs = num_seqs;
-  a.q = static_cast<const uint16_t*>(q_dev);
-  a.k = layer->k;
-  a.v = layer->v;
-  a.k_scale = static_cast<const uint8_t*>(layer->k_scale);
-  a.v_scale = static_cast<const uint8_t*>(layer->v_scale);
-  a.k_tensor_scale = layer->k_tensor_scale_dev;
-  a.v_tensor_scale = layer->v_tensor_scale_dev;
-  a.block_tables = layer->paged ? block_tables_dev : nullptr;
-  a.block_table_stride = layer->paged ? block_table_stride : 0;
-  a.seq_lens = seq_lens_dev;
-  a.max_seq_len = max_seq_len;
-  a.scale_log2 = (float)((double)softmax_scale * M_LOG2E);
-  a.out = out_dev;
-  a.out_f32 = out_dtype == YRK_OUT_F32;
-  const size_t slots = (size_t)num_seqs * num_q_heads * a.plan.num_splits;
-  a.ws_o = static_cast<float*>(workspace_dev);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace_dev) +
-                                      ((slots * yrk::kHeadDim * sizeof(float) + 255) / 256) * 256);
-  a.err = dev_error_word;
-  return launch_status(yrk::launch_decode(a, stream));
+  if (!workspace_dev) return YRK_EINVAL;
+  return decode_call(layer, q_dev, num_seqs, num_q_heads, block_tables_dev, block_table_stride,
+                     seq_lens_dev, max_seq_len, softmax_scale, out_dev, out_dtype, workspace_dev,
+                     workspace_bytes, dev_error_word, stream);
+}
+
+int yrk_decode_attention_noalloc(const yrk_kv_layer* layer, const void* q_dev, int32_t num_seqs,
+                                 int32_t num_q_heads, const int32_t* block_tables_dev,
+                                 int64_t block_table_stride, const int32_t* seq_lens_dev,
+                                 int64_t max_seq_len, float softmax_scale, void* out_dev,
+                                 int32_t out_dtype, uint32_t* dev_error_word,
+                                 hipStream_t stream) {
+  // nullptr workspace: decode_call validates everything, then takes the
+  // device scratch of the current device (no allocation anywhere)
+  return decode_call(layer, q_dev, num_seqs, num_q_heads, block_tables_dev, block_table_stride,
+                     seq_lens_dev, max_seq_len, softmax_scale, out_dev, out_dtype, nullptr,
+                     yrk::kNoAllocScratchBytes, dev_error_word, stream);
 }
 
 size_t yrk_verify_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_q_heads,

@@ -123,6 +123,13 @@ struct DecodeArgs {
   DecodePlan plan;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Device scratch of yrk_decode_attention_noalloc: a file-scope device array
+// of kNoAllocScratchBytes per GPU (noalloc.hip).  device_scratch() returns
+// its device address on the current device, looked up on the first call
+// there and kept per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t device_scratch(void** ptr);
 // The log-sum-exp merge of the split partials alone: one output row per
 // (sequence, a.num_q_heads row) from a.ws_o / a.ws_lse.
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
