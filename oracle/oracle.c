@@ -272,6 +272,7 @@ double orc_e4m3_value(int code) {
  */
 float orc_nvfp4_tensor_scale(const uint16_t *x, int64_t n) {
     double amax = 0.0;
+#pragma omp parallel for reduction(max : amax) schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         double a = fabs(orc_bf16_to_f64(x[i]));
         if (a > amax) amax = a;
@@ -340,15 +341,16 @@ void orc_nvfp4_quantize(const uint16_t *x, int64_t ntok, int nheads, int head_di
                 int qs = e4m3_rne_sat(b / (6.0 * Sd));
                 sr[blk] = (uint8_t)qs;
                 double eff = orc_e4m3_value(qs) * Sd;
+                double thr[7]; /* the midpoints of this block, m * eff */
+                for (int k = 0; k < 7; ++k) thr[k] = mid[k] * eff;
                 for (int i = 0; i < 16; ++i) {
                     uint16_t bits = xr[blk * 16 + i];
                     double a = fabs(orc_bf16_to_f64(bits));
                     int mag = 0;
                     if (eff > 0.0) {
                         for (int k = 0; k < 7; ++k) {
-                            double thr = mid[k] * eff;
                             /* between code k and k+1: above the midpoint, or on it when k+1 is even */
-                            if (a > thr || (a == thr && ((k + 1) & 1) == 0)) mag = k + 1;
+                            if (a > thr[k] || (a == thr[k] && ((k + 1) & 1) == 0)) mag = k + 1;
                         }
                     }
                     cr[blk * 16 + i] = (uint8_t)(((bits >> 15) << 3) | mag);
@@ -363,6 +365,7 @@ void orc_nvfp4_quantize(const uint16_t *x, int64_t ntok, int nheads, int head_di
  * and element 2j+1 to the high nibble of byte j of a row.
  */
 void orc_nvfp4_pack(const uint8_t *codes, int64_t n_pairs, uint8_t *packed) {
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n_pairs; ++j)
         packed[j] = (uint8_t)((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4));
 }
@@ -500,7 +503,15 @@ typedef struct {
     const uint8_t *codes;
     const uint8_t *scales;
     double S;
+    /* NVFP4: orc_e2m1_value and orc_e4m3_value of every code, filled once by
+       calling them (the same doubles; the products below are unchanged) */
+    double e2m1[16], e4m3[256];
 } orc_kv_view;
+
+static void kv_view_tables(orc_kv_view *kv) {
+    for (int c = 0; c < 16; ++c) kv->e2m1[c] = orc_e2m1_value(c);
+    for (int c = 0; c < 256; ++c) kv->e4m3[c] = orc_e4m3_value(c);
+}
 
 static void kv_row(const orc_kv_view *kv, int64_t n, int g, int Hkv, int D, double *row) {
     int64_t r = n * Hkv + g;
@@ -511,7 +522,7 @@ static void kv_row(const orc_kv_view *kv, int64_t n, int g, int Hkv, int D, doub
         const uint8_t *c = kv->codes + r * D;
         const uint8_t *s = kv->scales + r * (D / 16);
         for (int d = 0; d < D; ++d)
-            row[d] = orc_e2m1_value(c[d]) * orc_e4m3_value(s[d / 16]) * kv->S;
+            row[d] = kv->e2m1[c[d] & 0xF] * kv->e4m3[s[d / 16]] * kv->S;
     } else {
         const int8_t *c = (const int8_t *)kv->codes + r * D;
         const uint16_t *s = (const uint16_t *)kv->scales + r * (D / 64);
@@ -580,6 +591,8 @@ int orc_decode_attention(const double *q, int Hq, int Hkv, int D, int64_t N, int
     if (kv_kind == 2 && D % 64) return -1;
     orc_kv_view kview = {kv_kind, (const uint16_t *)k, (const uint8_t *)k, k_scales, (double)kS};
     orc_kv_view vview = {kv_kind, (const uint16_t *)v, (const uint8_t *)v, v_scales, (double)vS};
+    kv_view_tables(&kview);
+    kv_view_tables(&vview);
     const int group = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int h = 0; h < Hq; ++h)
@@ -595,17 +608,27 @@ int orc_decode_attention(const double *q, int Hq, int Hkv, int D, int64_t N, int
  * appended).  Row r (query q[r] at position pos[r]) attends to cached tokens
  * 0..pos[r], i.e. it is the decode definition with N = pos[r] + 1.
  * q: [R][Hq][D] fp64; out: [R][Hq][D].  The KV arrays must cover max pos + 1
- * tokens.
+ * tokens.  Every (row, head) pair is independent; they run in parallel.
  */
 int orc_prefill_attention(const double *q, const int64_t *pos, int64_t R, int Hq, int Hkv, int D,
                           int kv_kind, const void *k, const void *v, const uint8_t *k_scales,
                           const uint8_t *v_scales, float kS, float vS, double scale, double *out) {
-    for (int64_t r = 0; r < R; ++r) {
-        int rc = orc_decode_attention(q + r * Hq * (int64_t)D, Hq, Hkv, D, pos[r] + 1, kv_kind, k,
-                                      v, k_scales, v_scales, kS, vS, scale,
-                                      out + r * Hq * (int64_t)D, NULL);
-        if (rc) return rc;
-    }
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || R < 0) return -1;
+    if (kv_kind < 0 || kv_kind > 2) return -1;
+    if (kv_kind == 1 && D % 16) return -1;
+    if (kv_kind == 2 && D % 64) return -1;
+    for (int64_t r = 0; r < R; ++r)
+        if (pos[r] < 0) return -1;
+    orc_kv_view kview = {kv_kind, (const uint16_t *)k, (const uint8_t *)k, k_scales, (double)kS};
+    orc_kv_view vview = {kv_kind, (const uint16_t *)v, (const uint8_t *)v, v_scales, (double)vS};
+    kv_view_tables(&kview);
+    kv_view_tables(&vview);
+    const int group = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r)
+        for (int h = 0; h < Hq; ++h)
+            attend_one_head(q + (r * Hq + h) * (int64_t)D, &kview, &vview, h / group, Hkv, D,
+                            pos[r] + 1, scale, out + (r * Hq + h) * (int64_t)D, NULL);
     return 0;
 }
 

@@ -315,6 +315,43 @@ def _host_case(W, w, u, N=None):
     return q, k, v, p_star
 
 
+def _raw_full(W, w, u, tensor, N, token0=0):
+    """Raw (un-roped) K or V rows [N, hkv, 256] of one layer at full size,
+    drawn by the seeded generator's device twin and copied to the host (the
+    twins are bit-identical: checked here on three slices against host_fill,
+    and on a whole tensor by test_device_generator_matches_host).  No
+    attention kernel is involved in drawing them."""
+    ostream = synth.K_OUTLIER if tensor == synth.K else synth.V_OUTLIER
+    t = torch.empty((N, w.hkv, 256), dtype=torch.bfloat16, device=DEV)
+    W.gen_kv(w, u, tensor, N, t, token0=token0)
+    raw = _bits(t)
+    del t
+    kw = dict(outlier_p=w.elem_outlier_p, outlier_mul=20.0) if w.elem_outlier_p else {}
+    for a in (0, N // 2, max(N - 64, 0)):
+        n = min(64, N - a)
+        host = synth.host_fill(w.seed, synth.stream_id(u, tensor), token0 + a, n, w.hkv, 256,
+                               chan_mul=W.chan_mul(w, u, tensor),
+                               outlier_stream=synth.stream_id(u, ostream), **kw)
+        assert np.array_equal(raw[a:a + n], host)
+    return raw
+
+
+def _host_case_full(W, w, u):
+    """_host_case at full size with the raw K and V from _raw_full."""
+    N = w.n_ctx
+    t = _oracle_table(w)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256)
+    q = O.rope(q_raw, [N], t, bf16_out=True)[0]
+    k = O.rope(_raw_full(W, w, u, synth.K, N), np.arange(N), t, bf16_out=True)
+    v = _raw_full(W, w, u, synth.V, N)
+    p_star = -1
+    if w.needle:
+        p_star = synth.needle_position(w.seed, u, N)
+        for g in range(w.hkv):
+            k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
+    return q, k, v, p_star
+
+
 def _decode_gpu(W, dl, w):
     out, ws = W.decode_outputs(w, dl, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -336,9 +373,18 @@ def test_decode_tiny_contiguous_f32(Y, W):
     _compare_attention("tiny", _f64(out)[0], ref, atol=1e-4, bf16_out=False)
 
 
-@pytest.mark.parametrize("name,units", [("native", [0]), ("long", [0]), ("long", [11]),
-                                        ("long_tp2", [2])])
+def _needle_bound_ok(got, v, p_star, w):
+    """With the planted key the needle's token dominates its group's first
+    head: that head's output is within 0.05 of the needle's value row."""
+    vf = O.bf16_to_f64(v[p_star])
+    return all(np.abs(got[w.group * g] - vf[g]).max() < 0.05 for g in range(w.hkv))
+
+
+@pytest.mark.parametrize("name,units", [("native", [0]), ("long_tp2", [2])] +
+                         [("long", [u]) for u in range(16)])
 def test_decode_bf16_paged(Y, W, name, units):
+    """Native length, one card's share of a two-way head split, and every one
+    of the 16 layers of the 1,048,576-token workload (each with its needle)."""
     w = W.WORKLOADS[name]
     for u in units:
         _say(f"decode {name} layer {u}")
@@ -347,15 +393,13 @@ def test_decode_bf16_paged(Y, W, name, units):
         gq = _bits(dl.q)[0]
         del dl
         torch.cuda.empty_cache()
-        q, k, v, p_star = _host_case(W, w, u)
+        q, k, v, p_star = (_host_case_full if w.n_ctx >= (1 << 20) else _host_case)(W, w, u)
         assert np.array_equal(gq, q)
         ref = O.decode_attention(O.bf16_to_f64(q), k, v)
         got = _f64(out)[0]
         _compare_attention(f"{name}/layer{u}", got, ref)
         if p_star >= 0:
-            vf = O.bf16_to_f64(v[p_star])
-            for g in range(w.hkv):
-                assert np.abs(got[w.group * g] - vf[g]).max() < 0.05
+            assert _needle_bound_ok(got, v, p_star, w)
 
 
 def test_decode_sessions_batched(Y, W):
@@ -365,16 +409,23 @@ def test_decode_sessions_batched(Y, W):
     out = _f64(_decode_gpu(W, dl, w))
     del dl
     torch.cuda.empty_cache()
-    for s in (0, 7, 14):
+    for s in range(w.seqs):                      # every one of the 15 sessions
+        _say(f"sessions: oracle of session {s}")
         q, k, v, _ = _host_case(W, w, s)
         ref = O.decode_attention(O.bf16_to_f64(q), k, v)
         _compare_attention(f"sessions/{s}", out[s], ref)
 
 
-def test_decode_long_nvfp4_sampled_layer(Y, W):
+@pytest.mark.parametrize("u", range(16))
+def test_decode_long_nvfp4_layer(Y, W, u):
+    """Every layer of the 16 x 1,048,576-token NVFP4 workload.  The cache's
+    K codes and scales are compared bit for bit, on every row, with the
+    oracle's quantisation of the K the GPU roped (the tensor the quantiser
+    received; this keeps rope rounding out of the quantiser check), the V
+    codes and scales with the oracle's quantisation of V; attention against
+    the oracle over its own roped and quantised cache."""
     w = W.WORKLOADS["long_fp4"]
-    u = 5
-    _say("decode long_fp4 layer 5")
+    _say(f"decode long_fp4 layer {u}")
     dl = W.build_decode_layer(w, u, device=DEV, keep_raw=True)
     out = _f64(_decode_gpu(W, dl, w))
     out32 = torch.empty((1, 24, 256), dtype=torch.float32, device=DEV)
@@ -392,23 +443,32 @@ def test_decode_long_nvfp4_sampled_layer(Y, W):
     vs = O.gather_paged(L.v_scale.cpu().numpy().reshape(-1), pages, 4, 16, 16, table, w.n_ctx)
     del dl, L
     torch.cuda.empty_cache()
-    q, k, v, _ = _host_case(W, w, u)
+    # the quantiser on the tensor it received: every row bit-exact
+    assert kS == float(O.nvfp4_tensor_scale(kg))
+    kq_codes, kq_scales = O.nvfp4_quantize(kg, np.float32(kS))
+    assert np.array_equal(ks.reshape(kq_scales.shape), kq_scales)
+    assert np.array_equal(kc.reshape(-1, 4, 128), O.nvfp4_pack(kq_codes))
+    del kc, ks
+    q, k, v, _ = _host_case_full(W, w, u)
     same = kg == k
-    _record("long_fp4/rope_k", mismatches=int((~same).sum()))
+    _record(f"long_fp4/layer{u}/rope_k", mismatches=int((~same).sum()))
     assert (~same).sum() <= k.size // 100000
-    del kg
-    assert kS == float(O.nvfp4_tensor_scale(k)) and vS == float(O.nvfp4_tensor_scale(v))
-    k_codes, k_scales = O.nvfp4_quantize(k, np.float32(kS))
+    assert vS == float(O.nvfp4_tensor_scale(v))
     v_codes, v_scales = O.nvfp4_quantize(v, np.float32(vS))
-    rows_ok = same.all(axis=-1)                  # rows whose roped input agrees bit for bit
     assert np.array_equal(vs.reshape(v_scales.shape), v_scales)
     assert np.array_equal(vc.reshape(-1, 4, 128), O.nvfp4_pack(v_codes))
-    assert np.array_equal(ks.reshape(k_scales.shape)[rows_ok], k_scales[rows_ok])
-    assert np.array_equal(kc.reshape(-1, 4, 128)[rows_ok], O.nvfp4_pack(k_codes)[rows_ok])
+    # the oracle's own cache: its rope, then its quantiser (equal to the
+    # above when the two ropes agree on every element)
+    if same.all():
+        k_codes, k_scales, kS_o = kq_codes, kq_scales, kS
+    else:
+        kS_o = float(O.nvfp4_tensor_scale(k))
+        k_codes, k_scales = O.nvfp4_quantize(k, np.float32(kS_o))
+    del kg, kq_codes, kq_scales
     ref = O.decode_attention(O.bf16_to_f64(q), k_codes, v_codes,
-                             nvfp4=(k_scales, v_scales, kS, vS))
-    _compare_attention("long_fp4/layer5", out[0], ref)
-    _compare_attention("long_fp4/layer5/f32", out32[0], ref, bf16_out=False)
+                             nvfp4=(k_scales, v_scales, kS_o, vS))
+    _compare_attention(f"long_fp4/layer{u}", out[0], ref)
+    _compare_attention(f"long_fp4/layer{u}/f32", out32[0], ref, bf16_out=False)
 
 
 def test_decode_long_int8_sampled_layer(Y, W):
@@ -438,7 +498,7 @@ def test_decode_long_int8_sampled_layer(Y, W):
                         table, w.n_ctx)
     del dl, L
     torch.cuda.empty_cache()
-    q, k, v, _ = _host_case(W, w, u)
+    q, k, v, _ = _host_case_full(W, w, u)
     same = kg == k
     _record("long_int8/rope_k", mismatches=int((~same).sum()))
     assert (~same).sum() <= k.size // 100000
@@ -827,12 +887,33 @@ def test_prefill_score_far_above_the_first_tile(Y, paged, mul, flagged):
         assert np.abs(got[40, 6 * g] - vf[500, g]).max() < 0.05
 
 
+def _prefill_sample(w, n_rows=256, seed=77):
+    """(token, head) rows of the chunk to check: per KV head g the kernel's
+    rows are R = 6 token + (head - 6 g), 192 to a workgroup (48 to a wave,
+    16 to a row block); the sample takes the first 64 and the last 64 R and
+    128 seeded ones, dealt round-robin over the KV heads, so every wave and
+    row block of a workgroup and every query head appears."""
+    T, G = w.prefill_chunk, w.group
+    R_all = T * G
+    rng = np.random.default_rng(seed)
+    Rs = np.concatenate([np.arange(64), np.arange(R_all - 64, R_all),
+                         rng.choice(np.arange(64, R_all - 64), n_rows - 128, replace=False)])
+    gs = np.arange(n_rows) % w.hkv
+    toks, heads = Rs // G, gs * G + Rs % G
+    waves = (Rs % 192) // 48
+    assert set(waves.tolist()) == {0, 1, 2, 3}
+    assert set(((Rs % 48) // 16).tolist()) == {0, 1, 2}
+    assert set(heads.tolist()) == set(range(w.hq))
+    return toks, heads
+
+
 @pytest.mark.parametrize("name", ["prefill", "prefill_tp2"])
 def test_prefill_workload_sampled_rows(Y, W, name):
     """The full chunk (8,192 queries at 1,040,384..1,048,575 over a
     1,048,576-token paged cache) in the bench's launch configuration, with
     24 q / 4 KV heads and with one card's share of a two-way head split
-    (12 q / 2 KV heads); rows checked one by one against the oracle."""
+    (12 q / 2 KV heads); 256 stratified (token, head) rows checked one by
+    one against the oracle."""
     w = W.WORKLOADS[name]
     _say(f"{name} workload")
     case = W.build_prefill(w, device=DEV)
@@ -841,19 +922,26 @@ def test_prefill_workload_sampled_rows(Y, W, name):
     Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out, err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    rows = [0, 1, 31, 4097, 8190, 8191]
-    got = _f64(out[rows])
-    qg = _bits(case.q[rows])
+    toks, heads = _prefill_sample(w)
+    ti = torch.from_numpy(toks).to(DEV)
+    hi = torch.from_numpy(heads).to(DEV)
+    got = _f64(out[ti, hi])
+    qg = _bits(case.q[ti, hi])
     del case, out
     torch.cuda.empty_cache()
     N, q0 = w.n_ctx, w.n_ctx - w.prefill_chunk
     t = _oracle_table(w)
-    k = O.rope(synth.host_fill(w.seed, synth.stream_id(0, synth.K), 0, N, w.hkv, 256),
-               np.arange(N), t, bf16_out=True)
-    v = synth.host_fill(w.seed, synth.stream_id(0, synth.V), 0, N, w.hkv, 256)
-    for j, r in enumerate(rows):
-        q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0 + r, 1, w.hq, 256)
-        q = O.rope(q_raw, [q0 + r], t, bf16_out=True)[0]
-        assert np.array_equal(q, qg[j])
-        ref = O.decode_attention(O.bf16_to_f64(q), k[: q0 + r + 1], v[: q0 + r + 1])
-        _compare_attention(f"{name}/row{r}", got[j], ref)
+    k = O.rope(_raw_full(W, w, 0, synth.K, N), np.arange(N), t, bf16_out=True)
+    v = _raw_full(W, w, 0, synth.V, N)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0, w.prefill_chunk, w.hq, 256)
+    q = O.rope(q_raw[toks], q0 + toks, t, bf16_out=True)[np.arange(len(toks)), heads]
+    assert np.array_equal(q, qg)
+    ref = np.empty_like(got)
+    for g in range(w.hkv):                     # rows of KV head g, all in one oracle call
+        sel = np.nonzero(heads // w.group == g)[0]
+        kg_ = np.ascontiguousarray(k[:, g:g + 1])
+        vg_ = np.ascontiguousarray(v[:, g:g + 1])
+        ref[sel] = O.prefill_attention(O.bf16_to_f64(q[sel])[:, None, :], q0 + toks[sel],
+                                       kg_, vg_)[:, 0]
+        del kg_, vg_
+    _compare_attention(f"{name}/256 rows", got, ref)

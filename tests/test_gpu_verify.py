@@ -10,7 +10,8 @@ import pytest
 import oracle as O
 import synth
 
-from test_gpu_parity import DEV, _bits, _compare_attention, _f64, _host_case, _say, _scale_bf16
+from test_gpu_parity import (DEV, _bits, _compare_attention, _f64, _host_case,
+                              _host_case_full, _say, _scale_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -201,14 +202,16 @@ def test_verify_nq1_matches_single_query_oracle(Y):
         _compare_attention(f"verify/nq1/{s}", got[s], refs[s], bf16_out=False)
 
 
-@pytest.mark.parametrize("nq", [4])
-def test_verify_long_layer(Y, W, nq):
-    """The bench's verify step on one layer of the 1,048,576-token workload:
-    nq new tokens appended at 1,048,576 .. +nq-1 (the spare page), queries
-    roped there, every output row checked against the oracle."""
-    w = W.WORKLOADS["long"]
+@pytest.mark.parametrize("name,nq", [("long", 4), ("long_int8", 4)])
+def test_verify_long_layer(Y, W, name, nq):
+    """The bench's verify step on one layer of the 1,048,576-token workload
+    (bf16 cache, and the INT8 group-64 cache): nq new tokens appended at
+    1,048,576 .. +nq-1 (the spare page), queries roped there, every output
+    row checked against the oracle (over its own INT8 quantisation of its
+    roped keys and of the values for the INT8 cache)."""
+    w = W.WORKLOADS[name]
     u = 5
-    _say(f"verify long layer {u} nq={nq}")
+    _say(f"verify {name} layer {u} nq={nq}")
     N = w.n_ctx
     dl = W.build_decode_layer(w, u, device=DEV, spare_page=True)
     q, k_new, v_new = W.verify_inputs(w, u, nq, device=DEV)
@@ -230,7 +233,7 @@ def test_verify_long_layer(Y, W, nq):
     gq = _bits(q)
     del dl, out, ws
     torch.cuda.empty_cache()
-    _, k, v, _ = _host_case(W, w, u)
+    _, k, v, _ = _host_case_full(W, w, u)
     t = O.yarn_table(original_max_position=w.orig)
     qh_raw, kh_raw, vh = W.verify_inputs_host(w, u, nq)
     qh = O.rope(qh_raw, np.arange(N, N + nq), t, bf16_out=True)
@@ -238,6 +241,15 @@ def test_verify_long_layer(Y, W, nq):
     k = np.concatenate([k, O.rope(kh_raw, np.arange(N, N + nq), t, bf16_out=True)])
     v = np.concatenate([v, vh])
     qf = O.bf16_to_f64(qh)
+    if w.int8:
+        kc, ksc = O.int8_quantize(k)
+        del k
+        vc, vsc = O.int8_quantize(v)
+        del v
     for i in range(nq):
-        ref = O.decode_attention(qf[i], k[: N + i + 1], v[: N + i + 1])
-        _compare_attention(f"verify/long/q{i}", got[i], ref, bf16_out=False)
+        if w.int8:
+            n = N + i + 1
+            ref = O.decode_attention(qf[i], kc[:n], vc[:n], int8=(ksc[:n], vsc[:n]))
+        else:
+            ref = O.decode_attention(qf[i], k[: N + i + 1], v[: N + i + 1])
+        _compare_attention(f"verify/{name}/q{i}", got[i], ref, bf16_out=False)
