@@ -9,12 +9,21 @@ resident in HBM before the timed region starts.
 Prints one JSON line.  value = KV token-layers per second (16 x 1,048,576 per
 step / step time).  roofline = the decode attention launches (split + merge),
 timed with HIP events on the stream they run on, against 8 TB/s.
+
+The "configs" object holds one entry per workload the decode path is
+specified on (tiny, native, long, long_fp4, the 15-session batch and the
+prefill chunk): its throughput, the median and mean of the per-launch HIP
+event times, the roofline fraction of the dominant kernel, whether two runs
+gave byte-identical outputs, and the oracle timed on a bounded sample of the
+same workload on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,10 +41,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(record):
-    """HBM bytes per launch from a committed rocprofv3 counter record, or None
-    when the kernel source has changed since the counters were taken."""
-    import hashlib
+def profile_record(record):
+    """A committed rocprofv3 record (profiles/*.json), or None when a kernel
+    source it names has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(path))
@@ -45,31 +53,63 @@ def measured_traffic(record):
                 return None
     except (OSError, ValueError, KeyError):
         return None
+    return rec
+
+
+def measured_traffic(record):
+    """HBM bytes per launch from a committed counter record (FETCH_SIZE and
+    WRITE_SIZE scaled by the plain-copy calibration), or None."""
+    rec = profile_record(record) if record else None
+    if rec is None or "fetch_kib_per_call" not in rec:
+        return None
     return 1024.0 * (rec["fetch_kib_per_call"] * rec["fetch_scale"] +
                      rec["write_kib_per_call"] * rec["write_scale"])
 
 
-def decode_bytes_per_launch(n_ctx, per_token, hq=24):
+def decode_bytes_per_launch(n_ctx, per_token, hq=24, seqs=1):
     # KV stream + q and out (hq heads x 256 x 2 B each) + the page table (4 B / 16 tokens)
-    return per_token * n_ctx + 2 * hq * 256 * 2 + 4 * (n_ctx // 16)
+    return seqs * (per_token * n_ctx + 2 * hq * 256 * 2 + 4 * (n_ctx // 16))
 
 
-def build_step(W, Y, w, torch, dev):
-    """The layers of a decode workload plus the per-step inputs."""
-    layers = []
-    for l in range(w.layers):
-        layers.append(W.build_decode_layer(w, l, device=dev, spare_page=True))
-        if l % 4 == 3:
-            log(f"{w.name}: built layer {l + 1}/{w.layers}")
-    N = w.n_ctx
-    L = w.layers
-    q_in = torch.empty((L, w.hq, 256), dtype=torch.bfloat16, device=dev)
-    k_in = torch.empty((L, w.hkv, 256), dtype=torch.bfloat16, device=dev)
-    v_in = torch.empty((L, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+def launch_stats(ms):
+    ms = sorted(ms)
+    return {"n": len(ms), "median_ms": statistics.median(ms), "mean_ms": sum(ms) / len(ms),
+            "p10_ms": ms[len(ms) // 10], "p90_ms": ms[(9 * len(ms)) // 10]}
+
+
+def hbm_roofline(bytes_per_launch, mean_ms, record=None, extra=None):
+    achieved = bytes_per_launch / (mean_ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(record),
+         "bytes_per_launch": bytes_per_launch, "avg_launch_ms": mean_ms}
+    if extra:
+        r.update(extra)
+    return r
+
+
+# -- decode steps -------------------------------------------------------------------
+
+def build_step(W, Y, w, torch, dev, layers=None):
+    """The layers of a decode workload plus a step over them: per layer (and
+    per sequence) the new query and key roped at position n_ctx and the key
+    and value appended (one fused pass), then one decode call for all the
+    sequences over the n_ctx cached tokens."""
+    if layers is None:
+        layers = []
+        for l in range(w.layers):
+            layers.append(W.build_decode_layer(w, l, device=dev, spare_page=True))
+            if l % 4 == 3:
+                log(f"{w.name}: built layer {l + 1}/{w.layers}")
+    N, L, S = w.n_ctx, w.layers, w.seqs
+    q_in = torch.empty((L, S, w.hq, 256), dtype=torch.bfloat16, device=dev)
+    k_in = torch.empty((L, S, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+    v_in = torch.empty((L, S, w.hkv, 256), dtype=torch.bfloat16, device=dev)
     for l in range(L):
-        q_in[l:l + 1] = W.gen_q(w, l, 1, dev, token0=1)
-        W.gen_kv(w, l, 1, 1, k_in[l:l + 1], token0=N)
-        W.gen_kv(w, l, 2, 1, v_in[l:l + 1], token0=N)
+        for s in range(S):
+            u = l if S == 1 else s
+            q_in[l, s:s + 1] = W.gen_q(w, u, 1, dev, token0=1)
+            W.gen_kv(w, u, 1, 1, k_in[l, s:s + 1], token0=N)
+            W.gen_kv(w, u, 2, 1, v_in[l, s:s + 1], token0=N)
     q_work = torch.empty_like(q_in)
     outs, wss = zip(*[W.decode_outputs(w, dl, device=dev) for dl in layers])
     pos_new = torch.full((1,), N, dtype=torch.int32, device=dev)
@@ -79,21 +119,173 @@ def build_step(W, Y, w, torch, dev):
     def step(timing=False):
         q_work.copy_(q_in)                               # roped in place below
         for l, dl in enumerate(layers):
-            # the new query and key roped at position N, key and value appended
-            Y.rope_append(dl.layer, yp, q_work[l:l + 1], k_in[l:l + 1], v_in[l:l + 1],
-                          dl.block_tables[0], pos_new)
+            for s in range(S):
+                Y.rope_append(dl.layer, yp, q_work[l, s:s + 1], k_in[l, s:s + 1],
+                              v_in[l, s:s + 1],
+                              dl.block_tables[s] if dl.block_tables is not None else None,
+                              pos_new)
             if timing:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            Y.decode_attention(dl.layer, q_work[l:l + 1], dl.block_tables, dl.seq_lens,
+            Y.decode_attention(dl.layer, q_work[l], dl.block_tables, dl.seq_lens,
                                dl.max_seq_len, outs[l], wss[l])
             if timing:
                 e1.record()
                 ev.append((e0, e1))
 
-    return step, ev, layers
+    return step, ev, layers, outs
 
+
+def time_steps(step, ev, steps, warmup, torch):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev.clear()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timing=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def repeat_identical(step, outs, torch):
+    """Two more steps on the same inputs: are all outputs byte-identical?"""
+    step()
+    torch.cuda.synchronize()
+    first = [o.clone() for o in outs]
+    step()
+    torch.cuda.synchronize()
+    return all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(first, outs))
+
+
+def bench_decode_config(W, Y, w, torch, dev, steps, warmup, per_token, desc, record=None,
+                        cpu_seconds=3.0, keep_layers=False):
+    log(f"{w.name}: building")
+    step, ev, layers, outs = build_step(W, Y, w, torch, dev)
+    log(f"{w.name}: timing {steps} steps")
+    wall, ms = time_steps(step, ev, steps, warmup, torch)
+    st = launch_stats(ms)
+    bpl = decode_bytes_per_launch(w.n_ctx, per_token, w.hq, w.seqs)
+    tokens = w.layers * w.seqs * w.n_ctx
+    res = {"workload": desc, "value": tokens / (wall / steps), "unit": "KV token-layers/s",
+           "ms_per_step": wall / steps * 1e3, "steps": steps, "decode_launch": st,
+           "kv_gbs": tokens * per_token / (wall / steps) / 1e9,
+           "roofline": hbm_roofline(bpl, st["mean_ms"], record,
+                                    {"frac_at_median": bpl / (st["median_ms"] * 1e-3) / 1e9 /
+                                     HBM_PEAK_GBS}),
+           "repeat_byte_identical": repeat_identical(step, outs, torch)}
+    kept = layers if keep_layers else None
+    del step, ev, layers, outs
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        log(f"{w.name}: oracle on the host cores")
+        res["cpu_baseline"] = cpu_decode_baseline(W, w, torch, dev, cpu_seconds)
+    return res, kept
+
+
+# -- the oracle on the host cores -----------------------------------------------------
+
+def _raw_host(W, w, u, tensor, n, torch, dev, token0=0):
+    """Raw K or V rows of one layer or session drawn by the generator's device
+    twin (bit-identical to the host generator) and copied to the host."""
+    import numpy as np
+    t = torch.empty((n, w.hkv, 256), dtype=torch.bfloat16, device=dev)
+    W.gen_kv(w, u, tensor, n, t, token0=token0)
+    out = t.view(torch.int16).cpu().numpy().view(np.uint16)
+    del t
+    return out
+
+
+def cpu_decode_baseline(W, w, torch, dev, min_seconds):
+    """The oracle's decode attention on whole layers (or sessions) of the
+    workload, one after another (the first again when a workload has only
+    one) until at least min_seconds of oracle time; inputs (generation, the
+    oracle's rope, its quantiser) are prepared outside the timed calls."""
+    import numpy as np
+    import oracle as O
+    import synth
+
+    N = w.n_ctx
+    t = O.yarn_table(original_max_position=w.orig)
+    units = w.layers if w.seqs == 1 else w.seqs
+
+    def prepare(u):
+        q = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256), [N], t,
+                   bf16_out=True)[0]
+        k = O.rope(_raw_host(W, w, u, synth.K, N, torch, dev), np.arange(N), t, bf16_out=True)
+        v = _raw_host(W, w, u, synth.V, N, torch, dev)
+        if w.needle:
+            p_star = synth.needle_position(w.seed, u, N)
+            for g in range(w.hkv):
+                k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
+        kw = {}
+        if w.nvfp4:
+            kS, vS = O.nvfp4_tensor_scale(k), O.nvfp4_tensor_scale(v)
+            k, ks = O.nvfp4_quantize(k, kS)
+            v, vs = O.nvfp4_quantize(v, vS)
+            kw = dict(nvfp4=(ks, vs, kS, vS))
+        elif w.int8:
+            k, ks = O.int8_quantize(k)
+            v, vs = O.int8_quantize(v)
+            kw = dict(int8=(ks, vs))
+        return O.bf16_to_f64(q), k, v, kw
+
+    total, done, case, seen = 0.0, 0, None, set()
+    while total < min_seconds:
+        u = done % units
+        if case is None or units > 1:
+            case = prepare(u)
+        qf, k, v, kw = case
+        t0 = time.perf_counter()
+        O.decode_attention(qf, k, v, **kw)
+        total += time.perf_counter() - t0
+        done += 1
+        seen.add(u)
+    what = "layers" if w.seqs == 1 else "sessions"
+    return {"value": done * N / total, "unit": "KV token-layers/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} calls over {len(seen)} of {units} {what} of the {w.name} "
+                      f"workload: {N} cached tokens x {w.hq} q heads each, fp64, {total:.2f} s"}
+
+
+def cpu_prefill_baseline(W, w, torch, dev):
+    """The oracle on the stratified 256-row sample of the prefill chunk (the
+    rows the GPU test checks), and the full chunk's time extrapolated from it
+    by visible (query, key) pairs."""
+    import numpy as np
+    import oracle as O
+    import synth
+
+    N, T = w.n_ctx, w.prefill_chunk
+    q0 = N - T
+    t = O.yarn_table(original_max_position=w.orig)
+    toks, heads = W.prefill_sample(w)
+    k = O.rope(_raw_host(W, w, 0, synth.K, N, torch, dev), np.arange(N), t, bf16_out=True)
+    v = _raw_host(W, w, 0, synth.V, N, torch, dev)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), q0, T, w.hq, 256)
+    q = O.rope(q_raw[toks], q0 + toks, t, bf16_out=True)[np.arange(len(toks)), heads]
+    qf = O.bf16_to_f64(q)
+    total = 0.0
+    for g in range(w.hkv):
+        sel = np.nonzero(heads // w.group == g)[0]
+        kg = np.ascontiguousarray(k[:, g:g + 1])
+        vg = np.ascontiguousarray(v[:, g:g + 1])
+        t0 = time.perf_counter()
+        O.prefill_attention(qf[sel][:, None, :], q0 + toks[sel], kg, vg)
+        total += time.perf_counter() - t0
+    sample_pairs = float(np.sum(q0 + toks + 1))
+    full_pairs = float(w.hq) * sum(q0 + i + 1 for i in range(T))
+    flops = 4.0 * 256 * sample_pairs
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"256 stratified (token, head) rows of the chunk (first 64, last 64, 128 "
+                      f"seeded by the kernel's row order), fp64, {total:.2f} s",
+            "full_chunk_s_extrapolated": total * full_pairs / sample_pairs}
+
+
+# -- verify, prefill, append ------------------------------------------------------------
 
 def build_verify_step(W, Y, w, layers, nq, torch, dev):
     """A speculative verify step over a decode workload's layers: per layer,
@@ -139,12 +331,13 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
     res = {}
     for nq in sweep:
         step, ev = build_verify_step(W, Y, w, layers, nq, torch, dev)
-        wall, kms = time_steps(step, ev, steps, warmup, torch)
+        wall, ms = time_steps(step, ev, steps, warmup, torch)
+        st = launch_stats(ms)
         ctx = w.n_ctx + nq
         bpl = decode_bytes_per_launch(ctx, per_token, w.hq * nq)
-        res[nq] = {"value": w.layers * ctx / (wall / steps), "avg_launch_ms": kms,
+        res[nq] = {"value": w.layers * ctx / (wall / steps), "launch": st,
                    "ms_per_step": wall / steps * 1e3, "bytes_per_launch": bpl,
-                   "frac": bpl / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                   "frac": bpl / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del step, ev
         torch.cuda.empty_cache()
     m = res[main_nq]
@@ -152,93 +345,63 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
         "workload": f"speculative verify step, {w.layers} layers x 1,048,576 + {main_nq} cached "
                     f"tokens ({fmt}), {main_nq} causal queries x 24 q / 4 KV heads",
         "value": m["value"], "unit": "KV token-layers/s", "ms_per_step": m["ms_per_step"],
-        "avg_launch_ms": m["avg_launch_ms"],
-        "roofline": {"bound": "hbm", "achieved": m["bytes_per_launch"] / (m["avg_launch_ms"] * 1e-3)
-                     / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["frac"],
-                     "traffic": measured_traffic(record) if record else None,
-                     "bytes_per_launch": m["bytes_per_launch"]},
-        "by_queries": {str(nq): {"avg_launch_ms": r["avg_launch_ms"], "frac": r["frac"]}
+        "launch": m["launch"],
+        "roofline": hbm_roofline(m["bytes_per_launch"], m["launch"]["mean_ms"], record),
+        "by_queries": {str(nq): {"mean_ms": r["launch"]["mean_ms"],
+                                 "median_ms": r["launch"]["median_ms"], "frac": r["frac"]}
                        for nq, r in res.items()},
     }
 
 
-def time_steps(step, ev, steps, warmup, torch):
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev.clear()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(timing=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, sum(kern_ms) / len(kern_ms)
-
-
-def cpu_baseline(W, w, min_seconds=10.0):
-    """The oracle timed on whole layers of the decode workload (all 1,048,576
-    tokens, 24 query heads, the planted needle), one layer after another
-    until at least min_seconds of oracle time; inputs are prepared outside
-    the timed calls."""
-    import numpy as np
-    import oracle as O
-    import synth
-
-    N = w.n_ctx
-    t = O.yarn_table(original_max_position=w.orig)
-    total, done = 0.0, 0
-    for u in range(w.layers):
-        q = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256), [N], t,
-                   bf16_out=True)[0]
-        k = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.K), 0, N, w.hkv, 256),
-                   np.arange(N), t, bf16_out=True)
-        v = synth.host_fill(w.seed, synth.stream_id(u, synth.V), 0, N, w.hkv, 256)
-        if w.needle:
-            p_star = synth.needle_position(w.seed, u, N)
-            for g in range(w.hkv):
-                k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
-        qf = O.bf16_to_f64(q)
-        t0 = time.perf_counter()
-        O.decode_attention(qf, k, v)
-        total += time.perf_counter() - t0
-        done += 1
-        del k, v
-        if total >= min_seconds:
-            break
-    cores = O.num_threads()
-    return {"value": done * N / total, "unit": "KV token-layers/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{done} of {w.layers} layers of the long workload: {N} cached tokens x "
-                      f"{w.hq} q heads each, fp64, {total:.2f} s"}
-
-
-def bench_prefill(W, Y, torch, dev, reps, name="prefill"):
+def bench_prefill(W, Y, torch, dev, reps, name="prefill", cpu=False):
     w = W.WORKLOADS[name]
     case = W.build_prefill(w, device=dev)
     out = torch.empty_like(case.q)
+    ws = torch.empty(Y.prefill_workspace_size(case.q.shape[0], w.hq), dtype=torch.uint8,
+                     device=dev)
     T = case.q.shape[0]
+
+    def run():
+        Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out, ws)
+
     for _ in range(2):
-        Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out)
+        run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
+    ms = []
     for _ in range(reps):
-        Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out)
-    e1.record()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        ms.append((e0, e1))
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    st = launch_stats([a.elapsed_time(b) for a, b in ms])
+    first = out.clone()
+    run()
+    torch.cuda.synchronize()
+    identical = torch.equal(first.view(torch.uint8), out.view(torch.uint8))
     pairs = sum(case.q_start + i + 1 for i in range(T))
     flops = 4.0 * 256 * pairs * w.hq
-    tf = flops / (ms * 1e-3) / 1e12
+    tf = flops / (st["mean_ms"] * 1e-3) / 1e12
     record = "prefill_chunk_8192_over_1m.json" if name == "prefill" else None
-    return {"workload": f"prefill: 8,192-token causal chunk at 1,040,384..1,048,575 over a "
-                        f"1,048,576-token paged cache, {w.hq} q / {w.hkv} KV heads",
-            "ms_per_chunk": ms, "tflops": tf, "flop_per_chunk": flops,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": measured_traffic(record) if record else None}}
+    rec = profile_record(record) if record else None
+    roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(record),
+            "flop_per_launch": flops, "avg_launch_ms": st["mean_ms"]}
+    if rec and "mfma_util_pct" in rec:
+        roof["mfma_util_pct_counter"] = rec["mfma_util_pct"]
+    res = {"workload": f"prefill: 8,192-token causal chunk at 1,040,384..1,048,575 over a "
+                       f"1,048,576-token paged cache, {w.hq} q / {w.hkv} KV heads",
+           "ms_per_chunk": st["mean_ms"], "launch": st, "tflops": tf, "flop_per_chunk": flops,
+           "value": tf, "unit": "TFLOP/s", "roofline": roof,
+           "repeat_byte_identical": identical}
+    del case, out, ws
+    torch.cuda.empty_cache()
+    if cpu:
+        log(f"{name}: oracle on the host cores (256-row sample)")
+        res["cpu_baseline"] = cpu_prefill_baseline(W, w, torch, dev)
+    return res
 
 
 def bench_append(W, Y, torch, dev, reps=3):
@@ -308,6 +471,32 @@ def bench_append(W, Y, torch, dev, reps=3):
     return out
 
 
+def copy_bandwidth(torch, dev, gib=4, reps=10):
+    """A plain device copy (torch) of gib GiB: read + write bytes over the
+    median event time, the practical ceiling next to the 8 TB/s peak."""
+    n = gib << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        ms.append((e0, e1))
+    torch.cuda.synchronize()
+    med = statistics.median(a.elapsed_time(b) for a, b in ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * n / (med * 1e-3) / 1e9
+    return {"GBs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "bytes_read": n, "bytes_written": n,
+            "median_ms": med, "kernel": "torch copy_ of a 4 GiB int32 tensor"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,12 +504,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-nvfp4", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="only the headline workload (skip tiny, native, NVFP4, sessions)")
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-tp2", action="store_true",
                     help="skip one card's share of a two-way KV-head split (12 q / 2 KV heads)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated sections to run for profiling (long, tiny, native, "
+                         "long_fp4, sessions, prefill, int8, verify, append, tp2)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -346,121 +539,115 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": 3}), flush=True)
         return
-    w = W.WORKLOADS["long"]
-    log("building the 16-layer 1,048,576-token bf16 cache")
-    step, ev, layers = build_step(W, Y, w, torch, dev)
-    log("timing decode steps")
-    wall, kern_ms = time_steps(step, ev, args.steps, args.warmup, torch)
-    ms_step = wall / args.steps * 1e3
-    tokens = w.layers * w.n_ctx
-    value = tokens / (wall / args.steps)
-    bpl = decode_bytes_per_launch(w.n_ctx, KV_BYTES_PER_TOKEN_LAYER)
-    achieved = bpl / (kern_ms * 1e-3) / 1e9
+    only = set(filter(None, args.only.split(",")))
+
+    def want(section):
+        return not only or section in only
+
+    cpu = not args.no_cpu_baseline and not only
+    sub_steps = max(10, args.steps // 2)
     result = {
         "metric": "decode-attn KV tokens/s + HBM GB/s at 1,048,576 ctx; prefill attn TFLOP/s",
-        "value": value, "unit": "KV token-layers/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "value": None, "unit": "KV token-layers/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode step, 16 full-attention layers x 1,048,576 cached "
                                "tokens (bf16, 16-token pages, seeded page permutation, planted "
                                "needle), 24 q / 4 KV heads x 256, YaRN x4 from 262,144, batch 1",
-                   "layers": w.layers, "context": w.n_ctx, "batch": 1},
-        "kv_gbs": tokens * KV_BYTES_PER_TOKEN_LAYER / (wall / args.steps) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode_split_bf16_long_1m.json"),
-                     "kernel": "decode_attention (split + merge), per layer",
-                     "bytes_per_launch": bpl, "avg_launch_ms": kern_ms},
+                   "layers": 16, "context": 1048576, "batch": 1},
     }
-    del step, ev
-    if not args.no_verify:
+    configs = {}
+    w = W.WORKLOADS["long"]
+    layers = None
+    if want("long") or want("verify"):
+        res, layers = bench_decode_config(
+            W, Y, w, torch, dev, args.steps, args.warmup, KV_BYTES_PER_TOKEN_LAYER,
+            result["config"]["workload"], record="decode_split_bf16_long_1m.json",
+            cpu_seconds=10.0 if cpu else 0.0, keep_layers=True)
+        configs["3_long_bf16"] = res
+        result.update(value=res["value"], ms_per_step=res["ms_per_step"], kv_gbs=res["kv_gbs"])
+        result["roofline"] = dict(res["roofline"],
+                                  kernel="decode_attention (split + merge), per layer")
+        if "cpu_baseline" in res:
+            result["cpu_baseline"] = res["cpu_baseline"]
+    if layers is not None and not args.no_verify and want("verify"):
         log("timing verify steps")
-        result["verify"] = bench_verify(W, Y, w, layers, torch, dev, max(3, args.steps // 2),
-                                        args.warmup,
+        result["verify"] = bench_verify(W, Y, w, layers, torch, dev, sub_steps, args.warmup,
                                         record="verify_split_bf16_long_q4_1m.json")
     del layers
     torch.cuda.empty_cache()
-    if not args.no_nvfp4:
-        wf = W.WORKLOADS["long_fp4"]
-        log("building the NVFP4 16-layer cache")
-        stepf, evf, lf = build_step(W, Y, wf, torch, dev)
-        wallf, kf = time_steps(stepf, evf, max(3, args.steps // 2), args.warmup, torch)
-        bplf = decode_bytes_per_launch(wf.n_ctx, NVFP4_BYTES_PER_TOKEN_LAYER)
-        result["nvfp4_decode"] = {
-            "value": wf.layers * wf.n_ctx / (wallf / max(3, args.steps // 2)),
-            "unit": "KV token-layers/s", "avg_launch_ms": kf,
-            "roofline": {"bound": "hbm", "achieved": bplf / (kf * 1e-3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bplf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_split_nvfp4_long_fp4_1m.json"),
-                         "bytes_per_launch": bplf}}
-        del lf, stepf, evf
-        torch.cuda.empty_cache()
-    if not args.no_int8:
+    if not args.no_configs:
+        if want("tiny"):
+            wt = W.WORKLOADS["tiny"]
+            configs["1_tiny"], _ = bench_decode_config(
+                W, Y, wt, torch, dev, 200, 20, KV_BYTES_PER_TOKEN_LAYER,
+                "single decode step, 1 layer, 4,096 cached tokens (contiguous), query at 4,096, "
+                "YaRN x4 from 1,024, fp32 output; latency-bound", cpu_seconds=1.0 if cpu else 0)
+            c = configs["1_tiny"]
+            c["latency_us"] = {"decode_median": c["decode_launch"]["median_ms"] * 1e3,
+                               "step": c["ms_per_step"] * 1e3}
+        if want("native"):
+            configs["2_native"], _ = bench_decode_config(
+                W, Y, W.WORKLOADS["native"], torch, dev, 50, 5, KV_BYTES_PER_TOKEN_LAYER,
+                "one layer at native length: 262,144 cached bf16 tokens, paged over a seeded "
+                "permutation, 4 outlier channels x8 per head", cpu_seconds=2.0 if cpu else 0)
+        if want("long_fp4"):
+            rec = profile_record("decode_split_nvfp4_long_fp4_1m.json")
+            configs["4_long_nvfp4"], _ = bench_decode_config(
+                W, Y, W.WORKLOADS["long_fp4"], torch, dev, sub_steps, args.warmup,
+                NVFP4_BYTES_PER_TOKEN_LAYER,
+                "decode step, 16 layers x 1,048,576 cached tokens, NVFP4 cache (1,152 B per "
+                "token-layer), 1% x20 outliers, 24 q / 4 KV heads",
+                record="decode_split_nvfp4_long_fp4_1m.json", cpu_seconds=3.0 if cpu else 0)
+            if rec and "valu_busy_pct" in rec:
+                configs["4_long_nvfp4"]["roofline"]["valu_busy_pct_counter"] = rec["valu_busy_pct"]
+        if want("sessions"):
+            configs["5_sessions_decode"], _ = bench_decode_config(
+                W, Y, W.WORKLOADS["sessions"], torch, dev, 50, 5, KV_BYTES_PER_TOKEN_LAYER,
+                "15 sessions x 131,072 cached bf16 tokens dealt from one shared pool of "
+                "122,880 pages, one batched decode call", cpu_seconds=3.0 if cpu else 0)
+    if not args.no_prefill and want("prefill"):
+        log("prefill")
+        configs["5_prefill"] = bench_prefill(W, Y, torch, dev, reps=10, cpu=cpu)
+        result["prefill"] = configs["5_prefill"]
+    result["configs"] = configs
+    if not args.no_int8 and want("int8"):
         wi = W.WORKLOADS["long_int8"]
-        log("building the INT8 16-layer cache")
-        stepi, evi, li = build_step(W, Y, wi, torch, dev)
-        si = max(3, args.steps // 2)
-        walli, ki = time_steps(stepi, evi, si, args.warmup, torch)
-        bpli = decode_bytes_per_launch(wi.n_ctx, INT8_BYTES_PER_TOKEN_LAYER)
-        result["int8_decode"] = {
-            "workload": "decode step, 16 layers x 1,048,576 cached tokens, INT8 group-64 cache "
-                        "(2,112 B per token-layer), 24 q / 4 KV heads",
-            "value": wi.layers * wi.n_ctx / (walli / si),
-            "unit": "KV token-layers/s", "avg_launch_ms": ki,
-            "roofline": {"bound": "hbm", "achieved": bpli / (ki * 1e-3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bpli / (ki * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_split_int8_long_int8_1m.json"),
-                         "bytes_per_launch": bpli}}
-        del stepi, evi
+        res, li = bench_decode_config(
+            W, Y, wi, torch, dev, sub_steps, args.warmup, INT8_BYTES_PER_TOKEN_LAYER,
+            "decode step, 16 layers x 1,048,576 cached tokens, INT8 group-64 cache (2,112 B "
+            "per token-layer), 24 q / 4 KV heads", record="decode_split_int8_long_int8_1m.json",
+            cpu_seconds=0, keep_layers=True)
+        result["int8_decode"] = res
         if not args.no_verify:
             log("timing INT8 verify steps")
             result["int8_verify"] = bench_verify(
-                W, Y, wi, li, torch, dev, si, args.warmup, per_token=INT8_BYTES_PER_TOKEN_LAYER,
-                fmt="INT8 group-64", record="verify_split_int8_long_int8_q4_1m.json")
+                W, Y, wi, li, torch, dev, sub_steps, args.warmup,
+                per_token=INT8_BYTES_PER_TOKEN_LAYER, fmt="INT8 group-64",
+                record="verify_split_int8_long_int8_q4_1m.json")
         del li
         torch.cuda.empty_cache()
-    if not args.no_append:
+    if not args.no_append and want("append"):
         log("append and rope over one 1M-token layer")
         result["append"] = bench_append(W, Y, torch, dev)
         torch.cuda.empty_cache()
-    if not args.no_prefill:
-        log("prefill")
-        try:
-            result["prefill"] = bench_prefill(W, Y, torch, dev, reps=3)
-        except Y.YrkError as e:
-            result["prefill"] = {"error": str(e)}
-        torch.cuda.empty_cache()
-    if not args.no_tp2:
+    if not args.no_tp2 and want("tp2"):
         # one card's share when the 4 KV heads are split over two cards: the
         # same kernels at 12 query / 2 KV heads (nothing is exchanged inside
         # attention, so this is the whole per-card decode and prefill work)
         wt = W.WORKLOADS["long_tp2"]
-        log("building the 12 q / 2 KV-head share")
-        stept, evt, lt = build_step(W, Y, wt, torch, dev)
-        st = max(3, args.steps // 2)
-        wallt, kt = time_steps(stept, evt, st, args.warmup, torch)
-        bplt = decode_bytes_per_launch(wt.n_ctx, KV_BYTES_PER_TOKEN_LAYER * wt.hkv // 4, wt.hq)
-        share = {"decode": {
-            "workload": f"decode step, {wt.layers} layers x 1,048,576 cached tokens (bf16), "
-                        f"{wt.hq} q / {wt.hkv} KV heads",
-            "value": wt.layers * wt.n_ctx / (wallt / st), "unit": "KV token-layers/s",
-            "avg_launch_ms": kt,
-            "roofline": {"bound": "hbm", "achieved": bplt / (kt * 1e-3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bplt / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_split_bf16_tp2_share_1m.json"),
-                         "bytes_per_launch": bplt}}}
-        del lt, stept, evt
-        torch.cuda.empty_cache()
+        res, _ = bench_decode_config(
+            W, Y, wt, torch, dev, sub_steps, args.warmup, KV_BYTES_PER_TOKEN_LAYER * wt.hkv // 4,
+            f"decode step, {wt.layers} layers x 1,048,576 cached tokens (bf16), "
+            f"{wt.hq} q / {wt.hkv} KV heads", record="decode_split_bf16_tp2_share_1m.json",
+            cpu_seconds=0)
+        share = {"decode": res}
         if not args.no_prefill:
             share["prefill"] = bench_prefill(W, Y, torch, dev, reps=3, name="prefill_tp2")
-            torch.cuda.empty_cache()
         result["tp2_share"] = share
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(W, w)
+    if not only:
+        log("copy bandwidth")
+        result["copy_bandwidth"] = copy_bandwidth(torch, dev)
     print(json.dumps(result), flush=True)
 
 

@@ -887,23 +887,15 @@ def test_prefill_score_far_above_the_first_tile(Y, paged, mul, flagged):
         assert np.abs(got[40, 6 * g] - vf[500, g]).max() < 0.05
 
 
-def _prefill_sample(w, n_rows=256, seed=77):
-    """(token, head) rows of the chunk to check: per KV head g the kernel's
-    rows are R = 6 token + (head - 6 g), 192 to a workgroup (48 to a wave,
-    16 to a row block); the sample takes the first 64 and the last 64 R and
-    128 seeded ones, dealt round-robin over the KV heads, so every wave and
-    row block of a workgroup and every query head appears."""
-    T, G = w.prefill_chunk, w.group
-    R_all = T * G
-    rng = np.random.default_rng(seed)
-    Rs = np.concatenate([np.arange(64), np.arange(R_all - 64, R_all),
-                         rng.choice(np.arange(64, R_all - 64), n_rows - 128, replace=False)])
-    gs = np.arange(n_rows) % w.hkv
-    toks, heads = Rs // G, gs * G + Rs % G
-    waves = (Rs % 192) // 48
-    assert set(waves.tolist()) == {0, 1, 2, 3}
+def _prefill_sample(W, w):
+    """workloads.prefill_sample, checked to reach every wave (48 rows) and
+    row block (16 rows) of a 192-row workgroup and every query head."""
+    toks, heads = W.prefill_sample(w)
+    Rs = toks * w.group + heads % w.group
+    assert set(((Rs % 192) // 48).tolist()) == {0, 1, 2, 3}
     assert set(((Rs % 48) // 16).tolist()) == {0, 1, 2}
     assert set(heads.tolist()) == set(range(w.hq))
+    assert len(set(zip(toks.tolist(), heads.tolist()))) == len(toks)
     return toks, heads
 
 
@@ -922,7 +914,7 @@ def test_prefill_workload_sampled_rows(Y, W, name):
     Y.prefill_attention(case.layer, case.q, case.q_start, case.block_table, out, err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    toks, heads = _prefill_sample(w)
+    toks, heads = _prefill_sample(W, w)
     ti = torch.from_numpy(toks).to(DEV)
     hi = torch.from_numpy(heads).to(DEV)
     got = _f64(out[ti, hi])

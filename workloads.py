@@ -160,8 +160,9 @@ class DecodeLayer:
 def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, spare_page=False):
     """One layer of a decode workload on the GPU: roped query (position n_ctx)
     and a cache filled by rope + append (+ NVFP4 or INT8 quantisation).  spare_page
-    adds one more page per sequence (table column pages_per_seq) so a decode
-    step can append its own token at position n_ctx."""
+    adds one more page per sequence (table column pages_per_seq; for the
+    contiguous layout one more block of capacity) so a decode step can append
+    its own token at position n_ctx."""
     S, N = w.seqs, w.n_ctx
     tables = page_table(w, unit)
     num_blocks = S * w.pages_per_seq
@@ -169,6 +170,8 @@ def build_decode_layer(w: Workload, unit: int, device="cuda", keep_raw=False, sp
         spare = np.arange(num_blocks, num_blocks + S, dtype=np.int32).reshape(S, 1)
         tables = np.ascontiguousarray(np.concatenate([tables, spare], axis=1))
         num_blocks += S
+    elif spare_page:
+        num_blocks += 1
     kv = Y.KV_NVFP4 if w.nvfp4 else (Y.KV_INT8 if w.int8 else Y.KV_BF16)
     layer = Y.KVLayer.allocate(kv, w.hkv, num_blocks,
                                paged=w.paged, device=device)
@@ -247,3 +250,19 @@ def build_prefill(w: Workload, device="cuda", chunk_tokens=1 << 18):
     q = gen_q(w, 0, T, device, token0=q0)
     Y.yarn_rope_apply(yp, q, torch.arange(q0, N, dtype=torch.int32, device=device))
     return PrefillCase(layer, q, bt, q0)
+
+
+def prefill_sample(w: Workload, n_rows=256, seed=77):
+    """A stratified sample of (token, query head) rows of a prefill chunk, the
+    kernel's row order in mind: per KV head g the rows are R = 6 token +
+    (head - 6 g), 192 to a workgroup, 48 to a wave, 16 to a row block.  The
+    sample takes the first 64 and the last 64 R and n_rows - 128 seeded ones,
+    dealt round-robin over the KV heads.  Returns (tokens, heads), int64."""
+    T, G = w.prefill_chunk, w.group
+    R_all = T * G
+    rng = np.random.default_rng(seed)
+    Rs = np.concatenate([np.arange(64), np.arange(R_all - 64, R_all),
+                         rng.choice(np.arange(64, R_all - 64), n_rows - 128, replace=False)])
+    gs = np.arange(n_rows) % w.hkv
+    return (Rs // G).astype(np.int64), (gs * G + Rs % G).astype(np.int64)
+
