@@ -156,5 +156,30 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Issue priority to the waves of a workgroup that are behind.  Two waves
+// share each SIMD, and with equal priority the older one is served first:
+// given equal shares, it finished its share well before the other, and the
+// SIMD then ran the rest with one wave.  After each step a wave publishes in
+// LDS how many steps it has done and takes priority 2 while no wave of the
+// workgroup has done fewer, else priority 0.  The steps each wave computes
+// are fixed, so only the speed depends on this (a stale count read here only
+// delays a change of priority).  progress: NW words, 16-byte aligned.
+template <int NW>
+__device__ __forceinline__ void balance_issue(uint32_t* progress, uint32_t done, int wave,
+                                              int lane) {
+  static_assert(NW % 4 == 0, "progress words are read four at a time");
+  if (lane == 0) reinterpret_cast<volatile uint32_t*>(progress)[wave] = done;
+  uint32_t mn = done;
+#pragma unroll
+  for (int w = 0; w < NW; w += 4) {
+    const u32x4_t p = *reinterpret_cast<volatile u32x4_t*>(progress + w);
+    mn = min(min(mn, min(p[0], p[1])), min(p[2], p[3]));
+  }
+  if (done > mn)
+    __builtin_amdgcn_s_setprio(0);
+  else
+    __builtin_amdgcn_s_setprio(2);
+}
+
 }  // namespace
 }  // namespace yrk

@@ -66,7 +66,18 @@ namespace {
 //             while the current ones are computed.
 
 constexpr int kUnitPages = 2;                            // pages per wave step
-constexpr int kStageBytes = kWaves * kUnitPages * kBlockSize * kRowBytesF16;   // 64 KiB
+// One NVFP4 workgroup per CU, 8 waves (2 per SIMD) whose issue priority
+// favours the waves that are behind (balance_issue).  Two 4-wave workgroups
+// on a CU ran at very different speeds: the first placed on each CU finished
+// its equal share ~12% earlier, and the CU spent the rest of the split at
+// half occupancy.  Measured per 1M-token layer: 230 us as two 4-wave
+// workgroups per CU, 224 us as one 8-wave workgroup, 221 us with the
+// priority balance (a counter handing steps to whichever wave asked first
+// reached 218 us, but the sums then depend on the timing: no longer
+// byte-reproducible).
+constexpr int kWavesF4 = 8;
+constexpr int kThreadsF4 = 64 * kWavesF4;
+constexpr int kStageBytes = kWavesF4 * kUnitPages * kBlockSize * kRowBytesF16;   // 128 KiB
 constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
 constexpr int kVtAhead = 4;                              // V^T operands in flight ahead of their products
 
@@ -146,15 +157,15 @@ __device__ __forceinline__ float load_q_f16(const DecodeArgs& a, int s, int g, i
 // normalised partial + log2-sum-exp per query head.  Lane (lo, hi) holds
 // O^T rows 16 i + 4 hi .. +3 of head lo; l and O carry a factor
 // 2^kPShiftF4; vS multiplies every value (1 for a cache without one).
-template <int G>
+template <int G, int NW = kWaves>
 __device__ __forceinline__ void finish_split_mfma(const DecodeArgs& a, int s, int g, int split,
                                                   uint8_t* stage, const floatx4_t (&o)[16],
                                                   const floatx4_t& lsum, float m, float vS,
                                                   int wave, int lo, int hi) {
   __syncthreads();
-  float* sm_o = reinterpret_cast<float*>(stage);   // [kWaves][G][256]
-  float* sm_m = sm_o + kWaves * G * kHeadDim;      // [kWaves][G]
-  float* sm_l = sm_m + kWaves * G;                 // [kWaves][G]
+  float* sm_o = reinterpret_cast<float*>(stage);   // [NW][G][256]
+  float* sm_m = sm_o + NW * G * kHeadDim;          // [NW][G]
+  float* sm_l = sm_m + NW * G;                     // [NW][G]
   if (lo < G) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -166,15 +177,15 @@ __device__ __forceinline__ void finish_split_mfma(const DecodeArgs& a, int s, in
   }
   __syncthreads();
   const int nsp = a.plan.num_splits;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 64 * NW) {
     const int h = idx / kHeadDim;
     const int d = idx % kHeadDim;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * G + h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * G + h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float sc = fast_exp2(sm_m[w * G + h] - M);
       L += sm_l[w * G + h] * sc;
       O += sm_o[(w * G + h) * kHeadDim + d] * sc;
@@ -187,11 +198,12 @@ __device__ __forceinline__ void finish_split_mfma(const DecodeArgs& a, int s, in
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsF4, 1) void decode_split_nvfp4(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
-  static_assert((kWaves * G * kHeadDim + 2 * kWaves * G) * 4 <= kStageBytes,
+  static_assert((kWavesF4 * G * kHeadDim + 2 * kWavesF4 * G) * 4 <= kStageBytes,
                 "split combine reuses the staging buffer");
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t progress[kWavesF4];   // steps done per wave
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -205,6 +217,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
   if (len < 0) len = 0;
   const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
   const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
+  if (threadIdx.x < kWavesF4) progress[threadIdx.x] = 0;
+  __syncthreads();
 
   floatx4_t o[16];
 #pragma unroll
@@ -368,20 +382,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
       wave_lds_sync();
     };
 
+    // wave w takes steps w, w + kWavesF4, ...; the next one is loaded while
+    // one is computed
     F4Unit R[kAheadF4 + 1];
+    uint32_t done = 0;
 #pragma unroll
-    for (int k = 0; k < kAheadF4; ++k) load_unit(wave + k * kWaves, R[k]);
-    for (int64_t u = wave; u < nunits; u += (kAheadF4 + 1) * kWaves) {
+    for (int k = 0; k < kAheadF4; ++k) load_unit(wave + k * kWavesF4, R[k]);
+    for (int64_t u = wave; u < nunits; u += (kAheadF4 + 1) * kWavesF4) {
 #pragma unroll
       for (int b = 0; b <= kAheadF4; ++b) {
-        const int64_t uu = u + b * kWaves;
-        load_unit(uu + kAheadF4 * kWaves, R[(b + kAheadF4) % (kAheadF4 + 1)]);
+        const int64_t uu = u + b * kWavesF4;
+        load_unit(uu + kAheadF4 * kWavesF4, R[(b + kAheadF4) % (kAheadF4 + 1)]);
         if (uu < nunits) compute_unit(uu, R[b]);
+        balance_issue<kWavesF4>(progress, ++done, wave, lane);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  finish_split_mfma<G>(a, s, g, split, stage, o, lsum, m, vS, wave, lo, hi);
+  finish_split_mfma<G, kWavesF4>(a, s, g, split, stage, o, lsum, m, vS, wave, lo, hi);
 }
 
 // ---- INT8 group-64 on the matrix cores ------------------------------------------
@@ -408,7 +427,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_nvfp4(DecodeArgs a) 
 //             P^T operand, one transposing LDS read per 16 dims is V^T.
 
 
-constexpr int kStageBytesI8 = kWaves * kBlockSize * kRowBytesF16;   // 32 KiB
+// Two 4-wave workgroups per CU: one 8-wave workgroup with the priority
+// balance of the NVFP4 kernel measured 1% slower here (405.7 against
+// 401.8 us per 1M-token layer).
+constexpr int kWavesI8 = 4;
+constexpr int kThreadsI8 = 64 * kWavesI8;
+constexpr int kStageBytesI8 = kWavesI8 * kBlockSize * kRowBytesF16;   // 32 KiB
 // Steps in flight beyond the one computed.  The kernel waits on memory far
 // more than it computes (a page is ~380 vector instructions and 25 MFMAs),
 // so the registers go to a deeper ring: the Q^T operands live in LDS (read
@@ -429,9 +453,9 @@ struct I8Unit {
 };
 
 template <int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsI8, 2) void decode_split_int8(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "heads of a group fill at most one MFMA column block");
-  static_assert((kWaves * G * kHeadDim + 2 * kWaves * G) * 4 <= kStageBytesI8,
+  static_assert((kWavesI8 * G * kHeadDim + 2 * kWavesI8 * G) * 4 <= kStageBytesI8 + kQOpBytesI8,
                 "split combine reuses the staging buffer");
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytesI8 + kQOpBytesI8];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -614,19 +638,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_int8(DecodeArgs a) {
       wave_lds_sync();
     };
 
+    // wave w takes pages w, w + kWavesI8, ...
     I8Unit R[kAheadI8 + 1];
 #pragma unroll
-    for (int k = 0; k < kAheadI8; ++k) load_unit(wave + k * kWaves, R[k]);
-    for (int64_t u = wave; u < npages; u += (kAheadI8 + 1) * kWaves) {
+    for (int k = 0; k < kAheadI8; ++k) load_unit(wave + k * kWavesI8, R[k]);
+    for (int64_t u = wave; u < npages; u += (kAheadI8 + 1) * kWavesI8) {
 #pragma unroll
       for (int b = 0; b <= kAheadI8; ++b) {
-        const int64_t uu = u + b * kWaves;
-        load_unit(uu + kAheadI8 * kWaves, R[(b + kAheadI8) % (kAheadI8 + 1)]);
+        const int64_t uu = u + b * kWavesI8;
+        load_unit(uu + kAheadI8 * kWavesI8, R[(b + kAheadI8) % (kAheadI8 + 1)]);
         if (uu < npages) compute_unit(uu, R[b]);
       }
     }
   }
-  finish_split_mfma<G>(a, s, g, split, stage, o, lsum, m, 1.0f, wave, lo, hi);
+  finish_split_mfma<G, kWavesI8>(a, s, g, split, stage, o, lsum, m, 1.0f, wave, lo, hi);
 }
 
 // ---- merge ------------------------------------------------------------------
@@ -708,8 +733,8 @@ __global__ __launch_bounds__(64 * kMergeGroups) void decode_merge(DecodeArgs a) 
 template <int G>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.plan.num_splits, a.geo.num_kv_heads, a.num_seqs);
-  if (a.dtype == 2) return launch(decode_split_int8<G>, grid, dim3(kThreads), 0, st, a);
-  return launch(decode_split_nvfp4<G>, grid, dim3(kThreads), 0, st, a);
+  if (a.dtype == 2) return launch(decode_split_int8<G>, grid, dim3(kThreadsI8), 0, st, a);
+  return launch(decode_split_nvfp4<G>, grid, dim3(kThreadsF4), 0, st, a);
 }
 
 }  // namespace

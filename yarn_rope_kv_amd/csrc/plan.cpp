@@ -7,14 +7,15 @@
 
 namespace yrk {
 
-// Workgroups a decode launch aims for: the split kernels keep two resident
-// per CU and get a single round of them (measured: 1,024 bf16 workgroups, two
-// rounds, were 1.5% slower at 24 q / 4 KV heads and 10% slower at 12 q / 2
-// KV heads, where each split then holds only 2,048 tokens; 768, 1,024 and
-// 2,048 NVFP4 workgroups were 22%, 5% and 11% slower than 512).  The bf16
-// cache runs the one-query verify kernel, which is planned the same way.
-constexpr int64_t kTargetWgsBf16 = 512;
-constexpr int64_t kTargetWgsF4 = 512;
+// Workgroups a decode launch aims for: one round of them, two waves per
+// SIMD.  The bf16 cache runs the one-query verify kernel (one 8-wave
+// workgroup per CU), NVFP4 one 8-wave workgroup per CU, INT8 two 4-wave
+// workgroups.  Measured: more rounds were slower (two rounds of 4-wave bf16
+// workgroups 1.5% at 24 q / 4 KV heads and 10% at 12 q / 2 KV heads, where a
+// split then holds only 2,048 tokens; NVFP4 8-wave workgroups: 512 and
+// 1,024 of them 6% and 15% slower than 256).
+constexpr int64_t kTargetWgsBf16 = 256;
+constexpr int64_t kTargetWgsF4 = 256;
 constexpr int64_t kTargetWgsI8 = 512;
 constexpr int64_t kComputeUnits = 256;
 

@@ -46,11 +46,7 @@ namespace yrk {
 namespace {
 
 constexpr int kColRows = kVerifyColRows;                            // rows per MFMA column block
-constexpr int kStageBytesV = kWaves * kBlockSize * kRowBytesF16;    // 32 KiB: one V page per wave
 constexpr int kQOpBytes = 8 * 64 * 16;                              // Q^T operands of a block: 8 KiB
-constexpr int kFinishBytes = (kWaves * kColRows * kHeadDim + 2 * kWaves * kColRows) * 4;
-constexpr int kLdsBytes = kFinishBytes;                             // 64.5 KiB
-static_assert(kStageBytesV + 3 * kQOpBytes <= kLdsBytes, "V staging and Q^T fit the buffer");
 constexpr float kRescaleV = 1.0f;
 
 __device__ __forceinline__ floatx4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, floatx4_t c) {
@@ -74,15 +70,19 @@ __device__ __forceinline__ u32x4_t split_weights(const float (&p)[4]) {
 }
 
 // Per column-block count C: pages a wave keeps in flight beyond the one it
-// computes, and workgroups resident per CU (which the registers allow).  Two
-// waves per SIMD matter more than a deeper register ring (measured at 4
-// queries, 1M tokens: 0.755 ms with two workgroups per CU and no ring
-// against 0.815 ms with one workgroup and one page ahead); three column
-// blocks hold 192 accumulator registers and leave room for one workgroup.
+// computes, and waves of the (one per CU) workgroup.  Two waves per SIMD
+// matter more than a deeper register ring (measured at 4 queries, 1M
+// tokens: 0.755 ms with two waves per SIMD and no ring against 0.815 ms with
+// one and one page ahead); three column blocks hold 192 accumulator
+// registers and leave room for one wave per SIMD.  Two waves per SIMD come
+// from one 8-wave workgroup with the priority balance (balance_issue), not
+// two 4-wave workgroups, whose first-placed one ran far ahead of the other:
+// per 1M-token layer at 1, 2 and 4 queries 725, 727 and 731 us against 732,
+// 736 and 752 us.
 template <int C> struct VerifyTune;
-template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(1, 0); };
-template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWgsPerCu = verify_wgs_per_cu(2, 0); };
-template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(3, 0); };
+template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 0); };
+template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWaves = verify_waves(2, 0); };
+template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWaves = verify_waves(3, 0); };
 
 // One lane's share of one page: 16-byte chunks 4 j + kg of key and value
 // row t (head dims 32 j + 8 kg .. +7).
@@ -92,12 +92,18 @@ struct VUnit {
 };
 
 template <int C>
-__global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_split_bf16(
+__global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf16(
     VerifyArgs va) {
   constexpr int AHEAD = VerifyTune<C>::kAhead;
+  constexpr int NW = VerifyTune<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
+  constexpr int NT = 64 * NW;
   static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
+  constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
+  constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
+  constexpr int kLds = kStageV + C * kQOpBytes > kFinish ? kStageV + C * kQOpBytes : kFinish;
   const DecodeArgs& a = va.d;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  __shared__ __attribute__((aligned(16))) uint32_t progress[NW];   // pages done per wave
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -118,8 +124,9 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
   // Q^T operands: block c, step j, lane l at ((c * 8 + j) * 64 + l) * 16
   // bytes: row 16 c + l % 16, head dims 32 j + 8 (l / 16) .. +7 (zero rows
   // beyond R)
-  u32x4_t* qop = reinterpret_cast<u32x4_t*>(lds + kStageBytesV);
-  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+  u32x4_t* qop = reinterpret_cast<u32x4_t*>(lds + kStageV);
+  if (threadIdx.x < NW) progress[threadIdx.x] = 0;
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += NT) {
     const int l = idx & 63, j = (idx >> 6) & 7, c = idx >> 9;
     const int r = kColRows * c + (l & 15);
     u32x4_t v = {0u, 0u, 0u, 0u};
@@ -253,23 +260,27 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
       wave_lds_sync();
     };
 
+    // wave w takes pages w, w + NW, ...
     VUnit U[AHEAD + 1];
+    uint32_t done = 0;
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * kWaves, U[k]);
-    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * kWaves) {
+    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * NW, U[k]);
+    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * NW) {
 #pragma unroll
       for (int b = 0; b <= AHEAD; ++b) {
-        const int64_t uu = u + b * kWaves;
-        load_unit(uu + AHEAD * kWaves, U[(b + AHEAD) % (AHEAD + 1)]);
+        const int64_t uu = u + b * NW;
+        load_unit(uu + AHEAD * NW, U[(b + AHEAD) % (AHEAD + 1)]);
         if (uu < npages) compute_unit(uu, U[b]);
+        if constexpr (NW == 8) balance_issue<NW>(progress, ++done, wave, lane);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  // combine the 4 waves, one column block at a time
-  float* sm_o = reinterpret_cast<float*>(lds);     // [kWaves][16][256]
-  float* sm_m = sm_o + kWaves * kColRows * kHeadDim;
-  float* sm_l = sm_m + kWaves * kColRows;
+  // combine the NW waves, one column block at a time
+  float* sm_o = reinterpret_cast<float*>(lds);     // [NW][16][256]
+  float* sm_m = sm_o + NW * kColRows * kHeadDim;
+  float* sm_l = sm_m + NW * kColRows;
   const int nsp = a.plan.num_splits;
   const int64_t rows_per_seq = (int64_t)nq * a.num_q_heads;
 #pragma unroll
@@ -284,17 +295,17 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
       sm_l[wave * kColRows + lo] = lsum[c][0];
     }
     __syncthreads();
-    // 256 threads: one row of the block per pass, thread = head dim
-    for (int row = 0; row < kColRows; ++row) {
+    // NT / 256 rows of the block per pass, thread % 256 = head dim
+    for (int row = threadIdx.x / kHeadDim; row < kColRows; row += NT / kHeadDim) {
       const int r = kColRows * c + row;
       if (r >= R) break;
-      const int d = threadIdx.x;
+      const int d = threadIdx.x % kHeadDim;
       float M = kNegBig;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
       float L = 0.f, Ov = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float sc = fast_exp2(sm_m[w * kColRows + row] - M);
         L += sm_l[w * kColRows + row] * sc;
         Ov += sm_o[(w * kColRows + row) * kHeadDim + d] * sc;
@@ -320,14 +331,16 @@ __global__ __launch_bounds__(kThreads, VerifyTune<C>::kWgsPerCu) void verify_spl
 // operands are fp16 after one power-of-two prescale shared by the R rows,
 // which puts the largest |q| in [2^14, 2^15) (bf16 values are exact there).
 
-// Measured per 1M-token layer (2, 4, 6 queries at GQA 6): C = 1 0.427 ms
-// with one page ahead (0.443 with two); C = 2 0.464 ms without a ring;
-// C = 3, one workgroup per CU, 0.941 / 0.897 / 0.819 ms with 0 / 1 / 2
-// pages ahead (one wave per SIMD leaves latency exposed).
+// Measured per 1M-token layer (2, 4, 6 queries at GQA 6), as two 4-wave
+// workgroups per CU: C = 1 0.427 ms with one page ahead (0.443 with two);
+// C = 2 0.464 ms without a ring; C = 3, one workgroup per CU, 0.941 / 0.897 /
+// 0.819 ms with 0 / 1 / 2 pages ahead (one wave per SIMD leaves latency
+// exposed).  One 8-wave workgroup with the priority balance: 1 and 2 queries
+// 399 and 407 us against 409 and 413 us; 4 queries the same (476 / 474 us).
 template <int C> struct VerifyTuneI8;
-template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWgsPerCu = verify_wgs_per_cu(1, 2); };
-template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWgsPerCu = verify_wgs_per_cu(2, 2); };
-template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWgsPerCu = verify_wgs_per_cu(3, 2); };
+template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 2); };
+template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWaves = verify_waves(2, 2); };
+template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWaves = verify_waves(3, 2); };
 
 // One lane's share of one page.
 struct I8VUnit {
@@ -338,13 +351,19 @@ struct I8VUnit {
 };
 
 template <int C>
-__global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_split_int8(
+__global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_int8(
     VerifyArgs va) {
   constexpr int AHEAD = VerifyTuneI8<C>::kAhead;
+  constexpr int NW = VerifyTuneI8<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
+  constexpr int NT = 64 * NW;
   static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
-  static_assert(kStageBytesV + 3 * kQOpBytes <= kFinishBytes, "V staging and Q^T fit the buffer");
+  constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
+  constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
+  constexpr int kUse = kStageV + C * kQOpBytes + NW * 4;
+  constexpr int kLds = kUse > kFinish ? kUse : kFinish;
   const DecodeArgs& a = va.d;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kFinishBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  __shared__ __attribute__((aligned(16))) uint32_t progress[NW];   // pages done per wave
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -376,9 +395,10 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
     }
     return v;
   };
-  float* red = reinterpret_cast<float*>(lds + kStageBytesV + C * kQOpBytes);   // [kWaves]
+  float* red = reinterpret_cast<float*>(lds + kStageV + C * kQOpBytes);   // [NW]
+  if (threadIdx.x < NW) progress[threadIdx.x] = 0;
   float qmax = 0.f;
-  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += NT) {
     const u32x4_t v = q_chunk(idx);
 #pragma unroll
     for (int w = 0; w < 4; ++w) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
@@ -387,14 +407,16 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
   for (int sh = 1; sh < 64; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
   if (lane == 0) red[wave] = qmax;
   __syncthreads();
-  qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  qmax = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) qmax = fmaxf(qmax, red[w]);
   // 2^(14 - e): the largest |q| lands in [2^14, 2^15)
   const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
   const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
   const float qpre = __uint_as_float((uint32_t)pe << 23);
   const float cl2 = a.scale_log2 * __uint_as_float((uint32_t)(254 - pe) << 23);
-  uint4* qop = reinterpret_cast<uint4*>(lds + kStageBytesV);
-  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += kThreads) {
+  uint4* qop = reinterpret_cast<uint4*>(lds + kStageV);
+  for (int idx = threadIdx.x; idx < C * 8 * 64; idx += NT) {
     const u32x4_t v = q_chunk(idx);
     uint32_t h4[4];
 #pragma unroll
@@ -571,23 +593,27 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
       wave_lds_sync();
     };
 
+    // wave w takes pages w, w + NW, ...
     I8VUnit U[AHEAD + 1];
+    uint32_t done = 0;
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * kWaves, U[k]);
-    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * kWaves) {
+    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * NW, U[k]);
+    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * NW) {
 #pragma unroll
       for (int b = 0; b <= AHEAD; ++b) {
-        const int64_t uu = u + b * kWaves;
-        load_unit(uu + AHEAD * kWaves, U[(b + AHEAD) % (AHEAD + 1)]);
+        const int64_t uu = u + b * NW;
+        load_unit(uu + AHEAD * NW, U[(b + AHEAD) % (AHEAD + 1)]);
         if (uu < npages) compute_unit(uu, U[b]);
+        if constexpr (NW == 8) balance_issue<NW>(progress, ++done, wave, lane);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // combine the 4 waves, one column block at a time (l and O carry 2^kPShiftF4)
-  float* sm_o = reinterpret_cast<float*>(lds);     // [kWaves][16][256]
-  float* sm_m = sm_o + kWaves * kColRows * kHeadDim;
-  float* sm_l = sm_m + kWaves * kColRows;
+  float* sm_o = reinterpret_cast<float*>(lds);     // [NW][16][256]
+  float* sm_m = sm_o + NW * kColRows * kHeadDim;
+  float* sm_l = sm_m + NW * kColRows;
   const int nsp = a.plan.num_splits;
   const int64_t rows_per_seq = (int64_t)nq * a.num_q_heads;
 #pragma unroll
@@ -602,16 +628,16 @@ __global__ __launch_bounds__(kThreads, VerifyTuneI8<C>::kWgsPerCu) void verify_s
       sm_l[wave * kColRows + lo] = lsum[c][0];
     }
     __syncthreads();
-    for (int row = 0; row < kColRows; ++row) {
+    for (int row = threadIdx.x / kHeadDim; row < kColRows; row += NT / kHeadDim) {
       const int r = kColRows * c + row;
       if (r >= R) break;
-      const int d = threadIdx.x;
+      const int d = threadIdx.x % kHeadDim;
       float M = kNegBig;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * kColRows + row]);
       float L = 0.f, Ov = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float sc = fast_exp2(sm_m[w * kColRows + row] - M);
         L += sm_l[w * kColRows + row] * sc;
         Ov += sm_o[(w * kColRows + row) * kHeadDim + d] * sc;
@@ -634,13 +660,14 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const dim3 grid(d.plan.num_splits, d.geo.num_kv_heads, d.num_seqs);
   hipError_t e;
   const bool i8 = d.dtype == 2;
+  const dim3 block(64 * verify_waves(column_blocks(rows), d.dtype));
   switch (column_blocks(rows)) {
-    case 1: e = i8 ? launch(verify_split_int8<1>, grid, dim3(kThreads), 0, st, a)
-                   : launch(verify_split_bf16<1>, grid, dim3(kThreads), 0, st, a); break;
-    case 2: e = i8 ? launch(verify_split_int8<2>, grid, dim3(kThreads), 0, st, a)
-                   : launch(verify_split_bf16<2>, grid, dim3(kThreads), 0, st, a); break;
-    case 3: e = i8 ? launch(verify_split_int8<3>, grid, dim3(kThreads), 0, st, a)
-                   : launch(verify_split_bf16<3>, grid, dim3(kThreads), 0, st, a); break;
+    case 1: e = i8 ? launch(verify_split_int8<1>, grid, block, 0, st, a)
+                   : launch(verify_split_bf16<1>, grid, block, 0, st, a); break;
+    case 2: e = i8 ? launch(verify_split_int8<2>, grid, block, 0, st, a)
+                   : launch(verify_split_bf16<2>, grid, block, 0, st, a); break;
+    case 3: e = i8 ? launch(verify_split_int8<3>, grid, block, 0, st, a)
+                   : launch(verify_split_bf16<3>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
