@@ -231,9 +231,7 @@ __global__ __launch_bounds__(kThreadsF4, 1) void decode_split_nvfp4(DecodeArgs a
     const float kS = *a.k_tensor_scale;
     vS = *a.v_tensor_scale;
     uint4 qop[8];
-    // scores in log2 units: q.k * softmax scale * log2(e), with the K tensor
-    // scale and the q prescale (a power of two) folded in
-    const float c = a.scale_log2 * kS * load_q_f16<G>(a, s, g, lo, hi, qop);
+    float c = 0.f;   // set once the first step's loads are in flight (below)
 
     const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
     const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
@@ -388,6 +386,10 @@ __global__ __launch_bounds__(kThreadsF4, 1) void decode_split_nvfp4(DecodeArgs a
     uint32_t done = 0;
 #pragma unroll
     for (int k = 0; k < kAheadF4; ++k) load_unit(wave + k * kWavesF4, R[k]);
+    // scores in log2 units: q.k * softmax scale * log2(e), with the K tensor
+    // scale and the q prescale (a power of two) folded in; the query is read
+    // while the first step's loads are in flight
+    c = a.scale_log2 * kS * load_q_f16<G>(a, s, g, lo, hi, qop);
     for (int64_t u = wave; u < nunits; u += (kAheadF4 + 1) * kWavesF4) {
 #pragma unroll
       for (int b = 0; b <= kAheadF4; ++b) {

@@ -158,33 +158,44 @@ __device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, d
   return (uint32_t)B.qs;
 }
 
-// One thread quantises one 16-element block of K and the matching block of V.
+// One wave per token: lane l quantises block l % 16 (16 elements) of K and
+// of V of head h0 + l / 16, four heads per pass; the source loads go out
+// ahead of the token's one destination lookup (position, then page table),
+// and head h's row follows head 0's at a fixed stride.
 __global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
   const int H = a.geo.num_kv_heads;
-  const int64_t total = a.num_tokens * H * kQBlocks;
+  const int lane = threadIdx.x & 63;
+  const int hl = lane >> 4, qb = lane & 15;
   const double kS = (double)*a.k_tensor_scale;
   const double vS = (double)*a.v_tensor_scale;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total; gid += stride) {
-    const int64_t t = gid / (H * kQBlocks);
-    const int rem = (int)(gid - t * H * kQBlocks);
-    const int h = rem / kQBlocks;
-    const int qb = rem % kQBlocks;
-    // source loads first: they overlap the destination lookup
-    const int64_t src = ((t * H + h) * kHeadDim + qb * 16) / 8;  // in uint4 units
-    const uint4* ks = reinterpret_cast<const uint4*>(a.k_src) + src;
-    const uint4* vs = reinterpret_cast<const uint4*>(a.v_src) + src;
-    const uint4 k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
-    const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
-                                  a.err, qb == 0);
-    if (row < 0) continue;
-    uint2 kp, vp;
-    const uint32_t kq = quantize16(k0, k1, kS, &kp);
-    const uint32_t vq = quantize16(v0, v1, vS, &vp);
-    reinterpret_cast<uint2*>(a.k_dst)[row * kQBlocks + qb] = kp;
-    reinterpret_cast<uint2*>(a.v_dst)[row * kQBlocks + qb] = vp;
-    a.k_scale_dst[row * kQBlocks + qb] = (uint8_t)kq;
-    a.v_scale_dst[row * kQBlocks + qb] = (uint8_t)vq;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t hstride = a.geo.paged ? kBlockSize : 1;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       t < a.num_tokens; t += wstride) {
+    const int32_t pos = a.positions[t];
+    for (int h0 = 0; h0 < H; h0 += 4) {
+      const int h = h0 + hl;
+      uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
+      if (h < H) {
+        const int64_t src = ((t * H + h) * kHeadDim + qb * 16) / 8;   // in uint4 units
+        const uint4* ks = reinterpret_cast<const uint4*>(a.k_src) + src;
+        const uint4* vs = reinterpret_cast<const uint4*>(a.v_src) + src;
+        k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
+      }
+      const int64_t row0 = cache_row(a.geo, a.block_table, a.block_table_len, pos, 0, a.err,
+                                     lane == 0 && h0 == 0);
+      if (row0 < 0) break;
+      if (h < H) {
+        const int64_t row = row0 + (int64_t)h * hstride;
+        uint2 kp, vp;
+        const uint32_t kq = quantize16(k0, k1, kS, &kp);
+        const uint32_t vq = quantize16(v0, v1, vS, &vp);
+        reinterpret_cast<uint2*>(a.k_dst)[row * kQBlocks + qb] = kp;
+        reinterpret_cast<uint2*>(a.v_dst)[row * kQBlocks + qb] = vp;
+        a.k_scale_dst[row * kQBlocks + qb] = (uint8_t)kq;
+        a.v_scale_dst[row * kQBlocks + qb] = (uint8_t)vq;
+      }
+    }
   }
 }
 
@@ -192,35 +203,20 @@ __global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
 
 constexpr int kI8Groups = kHeadDim / 64;   // scale groups per row
 
-// Nearest binary16 pattern to q >= 0 (ties to even), saturating at 65504.
-// Works on the binary64 fields of q: keep 1 + 10 significand bits (or the
-// subnormal multiple of 2^-24) and round the dropped bits half-to-even.
-__device__ __forceinline__ uint32_t f16_encode_sat(double q) {
-  if (!(q < 65504.0)) return 0x7BFFu;
-  if (q == 0.0) return 0u;
-  const uint64_t u = (uint64_t)__double_as_longlong(q);
-  const int E = (int)(u >> 52) - 1023;            // q is a normal fp64 here
-  const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-  if (E >= -14) {
-    uint64_t keep = sig >> 42;                      // 1 + 10 bits
-    const uint64_t rest = sig & ((1ull << 42) - 1);
-    const uint64_t half = 1ull << 41;
-    if (rest > half || (rest == half && (keep & 1))) ++keep;   // may carry to 2048
-    const uint32_t code = (uint32_t)(((E + 15) << 10) + (int)(keep - 1024));
-    return code > 0x7BFFu ? 0x7BFFu : code;
-  }
-  const int shift = 28 - E;                         // RNE(q * 2^24) = RNE(sig * 2^(E - 28))
-  if (shift >= 64) return 0u;
-  uint64_t keep = sig >> shift;
-  const uint64_t rest = sig & ((1ull << shift) - 1);
-  const uint64_t half = 1ull << (shift - 1);
-  if (rest > half || (rest == half && (keep & 1))) ++keep;
-  return (uint32_t)keep;                            // 1024 is the smallest normal, 0x0400
-}
-
-__device__ __forceinline__ double f16_decode(uint32_t h) {
-  const int e = (int)((h >> 10) & 31u), m = (int)(h & 1023u);
-  return e ? ldexp((double)(1024 + m), e - 25) : ldexp((double)m, -24);
+// The group scale RNE_binary16(m / 127), saturating at 65504, for a group
+// maximum m (bf16 bits), and its value.  Computed from the correctly
+// rounded fp32 quotient and the hardware conversion to binary16 (nearest
+// even), which gives the rounding of the exact quotient: m = a 2^i with
+// a < 2^8, a binary16 rounding midpoint is c 2^k with c odd and at least
+// 2^11 + 1, so m / 127 is never one (the odd part of a 2^i would be 127 c)
+// and lies at least 2^-19 (relative) from every one, while the fp32
+// quotient is within 2^-24 of it.  Every binary16 value is an fp32 value.
+__device__ __forceinline__ uint32_t i8_group_scale(uint32_t mbits, float* value) {
+  const float q = bf16_to_f32((uint16_t)mbits) / 127.0f;
+  const uint32_t h =
+      q < 65504.0f ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q) : 0x7BFFu;
+  *value = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  return h;
 }
 
 // Largest of x over the 16 lanes of a DPP row (every lane gets it).
@@ -234,77 +230,87 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
 
 // Four bf16 values (one lane's share of a group) -> four packed int8 codes
 // and, in every lane, the group's binary16 scale bits.  The lanes of one DPP
-// row (16 lanes x 4 = 64 elements) hold one group.  The scale is max / 127 in
-// fp64 (correctly rounded), then one rounding to binary16.  Each code is the
-// correctly rounded fp32 quotient x / s, then one rounding to nearest even:
-// with x = a 2^i (a < 2^8) and s = b 2^j (b < 2^11), x / s is either a
-// half-integer exactly (which fp32 holds) or at least 2^-12 away from every
-// half-integer up to 127.5, while the fp32 quotient is within 2^-18 of it, so
-// the code is the one the exact quotient gives.  (Subnormal x only meet
-// scales that make the quotient round to 0 either way.)
+// row (16 lanes x 4 = 64 elements) hold one group.  The scale is
+// i8_group_scale of the group maximum.  Each code is RNE(x / s) clamped to
+// +-127, decided without a division: with x = a 2^i (a < 2^8) and s = b 2^j
+// (b < 2^11), x / s is either a half-integer exactly or at least 2^-12 away
+// from every half-integer up to 127.5, while q = x * rcp(s) (the hardware
+// reciprocal, within 1 ulp) is within 2^-17 of it; so rint(q) is the code
+// unless x / s is a half-integer, which the exact test x - h s == 0 finds
+// (h = floor(q) + 1/2 has 9 significant bits and s 11, so h s is exact in
+// fp32 and the fused multiply-add rounds only a zero or non-zero result);
+// then rint(h) is the even neighbour.  (Subnormal x only meet scales that
+// make the quotient round to 0 either way.)
 __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits) {
   const uint32_t e[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) m = max(m, e[i] & 0x7fffu);   // |x| orders like its bits
   m = row16_max_u32(m);
-  const uint32_t sb = f16_encode_sat((double)bf16_to_f32((uint16_t)m) / 127.0);
-  *scale_bits = sb;
-  const float sv = (float)f16_decode(sb);   // a binary16 value, exact in fp32
+  float sv;
+  *scale_bits = i8_group_scale(m, &sv);
+  // branch-free: a zero scale (an all-zero group) computes with s = 1 and
+  // keeps code 0
+  const bool zero = !(sv > 0.0f);
+  const float s1 = zero ? 1.0f : sv;
+  const float r = __builtin_amdgcn_rcpf(s1);
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int c = 0;
-    if (sv > 0.0f) {
-      float q = rintf(bf16_to_f32((uint16_t)e[i]) / sv);
-      q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
-      c = (int)q;
-    }
+    const float x = bf16_to_f32((uint16_t)e[i]);
+    const float q = x * r;
+    const float h = floorf(q) + 0.5f;
+    const float k = fmaf(-h, s1, x) == 0.0f ? rintf(h) : rintf(q);
+    const float kc = __builtin_amdgcn_fmed3f(k, -127.0f, 127.0f);
+    const int c = zero ? 0 : (int)kc;
     packed |= ((uint32_t)c & 0xffu) << (8 * i);
   }
   return packed;
 }
 
-// One wave per (token, head) row: lane l quantises elements 4l .. 4l+3 of K
-// and of V; group l / 16.  A wave takes kI8RowsInFlight rows of its
-// grid-stride sequence at a time and issues all their source loads before the
-// destination lookups (position, then page table) and the quantisation.
+// One wave per token: lane l quantises elements 4l .. 4l+3 of K and of V of
+// each of the token's head rows (group l / 16).  The source loads of up to
+// kI8RowsInFlight heads go out together, ahead of the one destination
+// lookup per token (position, then page table); head h's row follows head
+// 0's at a fixed stride.
 constexpr int kI8RowsInFlight = 4;
 
 __global__ __launch_bounds__(256) void append_int8_kernel(AppendArgs a) {
   const int H = a.geo.num_kv_heads;
   const int lane = threadIdx.x & 63;
-  const int64_t rows = a.num_tokens * H;
   const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t r0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r0 < rows;
-       r0 += kI8RowsInFlight * wstride) {
-    uint2 kw[kI8RowsInFlight], vw[kI8RowsInFlight];
+  const int64_t hstride = a.geo.paged ? kBlockSize : 1;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       t < a.num_tokens; t += wstride) {
+    for (int h0 = 0; h0 < H; h0 += kI8RowsInFlight) {
+      uint2 kw[kI8RowsInFlight], vw[kI8RowsInFlight];
 #pragma unroll
-    for (int i = 0; i < kI8RowsInFlight; ++i) {
-      const int64_t r = r0 + i * wstride;
-      kw[i] = vw[i] = make_uint2(0u, 0u);
-      if (r < rows) {
-        kw[i] = reinterpret_cast<const uint2*>(a.k_src)[r * (kHeadDim / 4) + lane];
-        vw[i] = reinterpret_cast<const uint2*>(a.v_src)[r * (kHeadDim / 4) + lane];
+      for (int i = 0; i < kI8RowsInFlight; ++i) {
+        kw[i] = vw[i] = make_uint2(0u, 0u);
+        if (h0 + i < H) {
+          const int64_t r = t * H + h0 + i;
+          kw[i] = reinterpret_cast<const uint2*>(a.k_src)[r * (kHeadDim / 4) + lane];
+          vw[i] = reinterpret_cast<const uint2*>(a.v_src)[r * (kHeadDim / 4) + lane];
+        }
       }
-    }
+      const int64_t row0 = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], 0,
+                                     a.err, lane == 0 && h0 == 0);
+      if (row0 < 0) break;
 #pragma unroll
-    for (int i = 0; i < kI8RowsInFlight; ++i) {
-      const int64_t r = r0 + i * wstride;
-      if (r >= rows) break;
-      const int64_t t = r / H;
-      const int h = (int)(r - t * H);
-      const int64_t row = cache_row(a.geo, a.block_table, a.block_table_len, a.positions[t], h,
-                                    a.err, lane == 0);
-      if (row < 0) continue;
-      uint32_t ksb, vsb;
-      const uint32_t kc = quantize_i8x4(kw[i], &ksb);
-      const uint32_t vc = quantize_i8x4(vw[i], &vsb);
-      reinterpret_cast<uint32_t*>(a.k_dst)[row * (kHeadDim / 4) + lane] = kc;
-      reinterpret_cast<uint32_t*>(a.v_dst)[row * (kHeadDim / 4) + lane] = vc;
-      if ((lane & 15) == 0) {
-        reinterpret_cast<uint16_t*>(a.k_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)ksb;
-        reinterpret_cast<uint16_t*>(a.v_scale_dst)[row * kI8Groups + (lane >> 4)] = (uint16_t)vsb;
+      for (int i = 0; i < kI8RowsInFlight; ++i) {
+        if (h0 + i >= H) break;
+        const int64_t row = row0 + (int64_t)(h0 + i) * hstride;
+        uint32_t ksb, vsb;
+        const uint32_t kc = quantize_i8x4(kw[i], &ksb);
+        const uint32_t vc = quantize_i8x4(vw[i], &vsb);
+        reinterpret_cast<uint32_t*>(a.k_dst)[row * (kHeadDim / 4) + lane] = kc;
+        reinterpret_cast<uint32_t*>(a.v_dst)[row * (kHeadDim / 4) + lane] = vc;
+        if ((lane & 15) == 0) {
+          reinterpret_cast<uint16_t*>(a.k_scale_dst)[row * kI8Groups + (lane >> 4)] =
+              (uint16_t)ksb;
+          reinterpret_cast<uint16_t*>(a.v_scale_dst)[row * kI8Groups + (lane >> 4)] =
+              (uint16_t)vsb;
+        }
       }
     }
   }
@@ -477,17 +483,30 @@ __global__ __launch_bounds__(256) void amax_bits_kernel(const uint16_t* x, int64
   if (((uintptr_t)x & 15u) == 0) {
     const int64_t n8 = n / 8;
     const uint4* x8 = reinterpret_cast<const uint4*>(x);
-    for (int64_t i = tid; i < n8; i += stride) {
-      const uint4 w = x8[i];
+    auto take8 = [&](const uint4& w) {
       take(w.x); take(w.x >> 16); take(w.y); take(w.y >> 16);
       take(w.z); take(w.z >> 16); take(w.w); take(w.w >> 16);
+    };
+    // four 16-byte loads in flight per thread
+    int64_t i = tid;
+    for (; i + 3 * stride < n8; i += 4 * stride) {
+      const uint4 w0 = x8[i], w1 = x8[i + stride], w2 = x8[i + 2 * stride], w3 = x8[i + 3 * stride];
+      take8(w0); take8(w1); take8(w2); take8(w3);
     }
-    for (int64_t i = n8 * 8 + tid; i < n; i += stride) take(x[i]);
+    for (; i < n8; i += stride) take8(x8[i]);
+    for (int64_t j = n8 * 8 + tid; j < n; j += stride) take(x[j]);
   } else {
     for (int64_t i = tid; i < n; i += stride) take(x[i]);
   }
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+  // one atomic per workgroup (atomics on one word serialise)
+  __shared__ uint32_t wave_max[4];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    if (m) atomicMax(out, m);
+  }
 }
 
 __global__ void finalize_scale_kernel(float* out) {
@@ -512,14 +531,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     const int64_t work = a.num_tokens * a.geo.num_kv_heads * kChunksPerRow;
     return launch(append_bf16_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
   }
-  if (a.dtype == 2) {
-    // one wave per kI8RowsInFlight rows
-    const int64_t waves = (a.num_tokens * a.geo.num_kv_heads + kI8RowsInFlight - 1) /
-                          kI8RowsInFlight;
-    return launch(append_int8_kernel, dim3(grid_for(waves * 64, 1 << 18)), dim3(256), 0, s, a);
-  }
-  const int64_t work = a.num_tokens * a.geo.num_kv_heads * kQBlocks;
-  return launch(append_nvfp4_kernel, dim3(grid_for(work, 1 << 20)), dim3(256), 0, s, a);
+  if (a.dtype == 2)   // one wave per token
+    return launch(append_int8_kernel, dim3(grid_for(a.num_tokens * 64, 1 << 18)), dim3(256), 0,
+                  s, a);
+  // one wave per token
+  return launch(append_nvfp4_kernel, dim3(grid_for(a.num_tokens * 64, 1 << 18)), dim3(256), 0, s,
+                a);
 }
 
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
@@ -534,7 +551,7 @@ hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStre
   uint32_t* word = reinterpret_cast<uint32_t*>(out);
   hipError_t e = launch(store_word_kernel, dim3(1), dim3(64), 0, s, word, 0u);
   if (e == hipSuccess && n > 0)
-    e = launch(amax_bits_kernel, dim3(grid_for(n / 8 + 1, 8192)), dim3(256), 0, s, x, n, word);
+    e = launch(amax_bits_kernel, dim3(grid_for(n / 8 + 1, 2048)), dim3(256), 0, s, x, n, word);
   if (e == hipSuccess) e = launch(finalize_scale_kernel, dim3(1), dim3(64), 0, s, out);
   return e;
 }
