@@ -92,6 +92,11 @@ constexpr int kNST = 4;                   // tiles in the LDS ring
 // each), 195-198 ms with one group among the PV products.
 constexpr int kLoadStep0 = 0;
 constexpr int kLoadStep1 = 3;
+// Score step after which the next tile's load is planned (fast_plan): its
+// scalar arithmetic issues while the matrix core works.  Planned at the loop
+// head, between the barrier and the first product, the chunk took 188 ms;
+// planned here, 183.5 ms.
+constexpr int kPlanStep = 5;
 
 template <int NK>
 struct Tile {
@@ -267,6 +272,47 @@ __device__ __forceinline__ uint32_t plan_tile(const PrefillArgs& a, int g, int w
   pl.present = b >= 0;
   pl.full = b >= 0 && key0 + kBlockSize <= kend;
   return missing;
+}
+
+// The common case of plan_tile, cheap enough to run among the score products
+// one tile ahead: a tile whose 32 keys are all visible and whose two pages
+// are in the pool (bounds checked as in plan_tile) needs only the source
+// address of this wave's page, `base` + index x `step` (the wave's tensor
+// and KV head folded into `base`; the index is the page id, or the first
+// key of the page in the contiguous layout).  Anything else takes plan_tile.
+struct FastPlan {
+  const uint16_t* src;
+  bool fast;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ FastPlan fast_plan(const PrefillArgs& a, int wave, int32_t j,
+                                              int32_t kend, PageIds ids, const uint16_t* base,
+                                              int64_t step) {
+  FastPlan f;
+  const int p = wave & 1;
+  if constexpr (PAGED) {
+    const uint32_t nb = (uint32_t)min(a.geo.num_blocks, (int64_t)INT32_MAX);
+    const bool ok = (uint32_t)ids.id[0] < nb && (uint32_t)ids.id[1] < nb;
+    f.fast = ok && 32 * j + 32 <= kend;
+    f.src = base + (int64_t)(p ? ids.id[1] : ids.id[0]) * step;
+  } else {
+    const int64_t nkeys = a.geo.num_blocks * kBlockSize;
+    f.fast = 32 * j + 32 <= kend && (int64_t)(32 * j + 32) <= nkeys;
+    f.src = base + (int64_t)(32 * j + kBlockSize * p) * step;
+  }
+  // The values are the same in every lane; saying so keeps them (and the
+  // loop-head branch on `fast`) on the scalar unit.  Left to the compiler,
+  // the plan carried across iterations was taken as per-lane and the kernel
+  // spilled hundreds of registers.
+  // (The builtin returns a signed int: each half goes through uint32_t before
+  // it is widened, or a low half with bit 31 set would fill the high half.)
+  f.fast = __builtin_amdgcn_readfirstlane((uint32_t)f.fast) != 0;
+  const uint64_t u = (uint64_t)f.src;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+  f.src = (const uint16_t*)(((uint64_t)hi << 32) | lo);
+  return f;
 }
 
 // Direct load i (0..7) of a page that is only partly visible or not present.
@@ -635,30 +681,57 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a, in
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) m_run[rb] = fmaxf(mxs[rb], kNegBig);
     make_p(pcur);
+    // Tile t+NST-1 is loaded in iteration t, planned among the score products
+    // of iteration t-1 (fast_plan) from page ids read at the end of iteration
+    // t-2; only tiles that fast_plan declines are planned at the loop head.
+    const int tensor = wave >> 1;
+    const uint16_t* page_base =
+        (tensor ? a.v : a.k) + (int64_t)g * (PAGED ? kBlockSize * kHeadDim : kHeadDim);
+    const int64_t page_step = (int64_t)a.geo.num_kv_heads * (PAGED ? kBlockSize * kHeadDim : kHeadDim);
+    const uint32_t lds_wave = (uint32_t)(uintptr_t)(lds_void_t*)(void*)(
+        &ring[0].kv[tensor][kBlockSize * (wave & 1)][0]);
+    PageIds ids_plan = ids_next;                              // tile NST-1
+    FastPlan fp = fast_plan<PAGED>(a, wave, NST - 1, kend, ids_plan, page_base, page_step);
+    ids_next = load_page_ids<PAGED>(a, NST);                  // tile NST
     __builtin_amdgcn_s_waitcnt(0xC07F);   // pending scalar loads only
     for (; it + 1 < ntiles; ++it) {
       const uint32_t cslot = (uint32_t)it & (NST - 1), nslot = (uint32_t)(it + 1) & (NST - 1),
                      islot = (uint32_t)(it + NST - 1) & (NST - 1);
       wait_tile<NK, NST>(min(NST - 3, ntiles - 2 - it));
       wg_barrier();
-      // plan tile it+NST-1 into the slot tile it-1 used; a full page's 8
+      // the page ids read at the end of the last iteration: waited for here,
+      // where no LDS read is in flight
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      // load tile it+NST-1 into the slot tile it-1 used; a full page's 8
       // loads go out in two groups of four among the score products below
       const bool load = it + NST - 1 < ntiles;
       PageLoad pl;
       if (load) {
-        const uint32_t m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_next,
-                                            ring[islot], pl);
+        uint32_t m = 0;
+        if (fp.fast) {
+          pl.src = fp.src;
+          pl.lds0 = lds_wave + islot * (uint32_t)sizeof(Tile<NK>);
+          pl.present = true;
+          pl.full = true;
+        } else {
+          m = plan_tile<PAGED>(a, g, wave, it + NST - 1, kend, ids_plan, ring[islot], pl);
+          if (!pl.full) load_page(a, pl, voff, stride_b);
+        }
         missing = (missing & ~(3u << (2 * islot))) | (m << (2 * islot));
-        if (!pl.full) load_page(a, pl, voff, stride_b);
       }
       const uint32_t miss = (missing >> (2 * nslot)) & 3u;
       any_missing |= miss;
+      const PageIds ids_new = ids_next;
       scores.template operator()<true>(ring[nslot], (it + 1) * NK, miss, ring[cslot], [&](int ks) {
         if (load && pl.full && (ks == kLoadStep0 || ks == kLoadStep1))
           load_full_half(pl, voff, ks == kLoadStep0 ? 0 : 1);
+        if (ks == kPlanStep) {
+          ids_plan = ids_new;
+          fp = fast_plan<PAGED>(a, wave, it + NST, kend, ids_new, page_base, page_step);
+        }
       });
       pv.template operator()<true>(ring[cslot], pcur, pnext);
-      ids_next = load_page_ids<PAGED>(a, it + NST);   // for the next iteration's load
+      ids_next = load_page_ids<PAGED>(a, it + NST + 1);   // planned in the next iteration
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) pcur[rb] = pnext[rb];
     }
