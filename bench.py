@@ -198,12 +198,41 @@ def _raw_host(W, w, u, tensor, n, torch, dev, token0=0):
     return out
 
 
+def _oracle_cache(W, w, u, torch, dev, q_first=None):
+    """The oracle's cache of layer (or session) u: its rope of the keys, the
+    planted needle (against the decode query q_first, when given), then its
+    quantiser for the workload's format.  Returns k, v and the format
+    keyword of the oracle's attention calls."""
+    import numpy as np
+    import oracle as O
+    import synth
+
+    N = w.n_ctx
+    t = O.yarn_table(original_max_position=w.orig)
+    k = O.rope(_raw_host(W, w, u, synth.K, N, torch, dev), np.arange(N), t, bf16_out=True)
+    v = _raw_host(W, w, u, synth.V, N, torch, dev)
+    if w.needle and q_first is not None:
+        p_star = synth.needle_position(w.seed, u, N)
+        for g in range(w.hkv):
+            k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q_first[w.group * g]))
+    kw = {}
+    if w.nvfp4:
+        kS, vS = O.nvfp4_tensor_scale(k), O.nvfp4_tensor_scale(v)
+        k, ks = O.nvfp4_quantize(k, kS)
+        v, vs = O.nvfp4_quantize(v, vS)
+        kw = dict(nvfp4=(ks, vs, kS, vS))
+    elif w.int8:
+        k, ks = O.int8_quantize(k)
+        v, vs = O.int8_quantize(v)
+        kw = dict(int8=(ks, vs))
+    return k, v, kw
+
+
 def cpu_decode_baseline(W, w, torch, dev, min_seconds):
     """The oracle's decode attention on whole layers (or sessions) of the
     workload, one after another (the first again when a workload has only
     one) until at least min_seconds of oracle time; inputs (generation, the
     oracle's rope, its quantiser) are prepared outside the timed calls."""
-    import numpy as np
     import oracle as O
     import synth
 
@@ -214,22 +243,7 @@ def cpu_decode_baseline(W, w, torch, dev, min_seconds):
     def prepare(u):
         q = O.rope(synth.host_fill(w.seed, synth.stream_id(u, synth.Q), 0, 1, w.hq, 256), [N], t,
                    bf16_out=True)[0]
-        k = O.rope(_raw_host(W, w, u, synth.K, N, torch, dev), np.arange(N), t, bf16_out=True)
-        v = _raw_host(W, w, u, synth.V, N, torch, dev)
-        if w.needle:
-            p_star = synth.needle_position(w.seed, u, N)
-            for g in range(w.hkv):
-                k[p_star, g] = O.round_bf16(2.0 * O.bf16_to_f64(q[w.group * g]))
-        kw = {}
-        if w.nvfp4:
-            kS, vS = O.nvfp4_tensor_scale(k), O.nvfp4_tensor_scale(v)
-            k, ks = O.nvfp4_quantize(k, kS)
-            v, vs = O.nvfp4_quantize(v, vS)
-            kw = dict(nvfp4=(ks, vs, kS, vS))
-        elif w.int8:
-            k, ks = O.int8_quantize(k)
-            v, vs = O.int8_quantize(v)
-            kw = dict(int8=(ks, vs))
+        k, v, kw = _oracle_cache(W, w, u, torch, dev, q_first=q)
         return O.bf16_to_f64(q), k, v, kw
 
     total, done, case, seen = 0.0, 0, None, set()
@@ -248,6 +262,29 @@ def cpu_decode_baseline(W, w, torch, dev, min_seconds):
             "kind": "oracle",
             "sample": f"{done} calls over {len(seen)} of {units} {what} of the {w.name} "
                       f"workload: {N} cached tokens x {w.hq} q heads each, fp64, {total:.2f} s"}
+
+
+def cpu_verify_baseline(W, w, torch, dev, nq=4):
+    """The oracle's causal attention of nq queries (at positions N - nq ..
+    N - 1, seeing keys up to their own) over layer 0's cache, once: the
+    verify step's arithmetic at the workload's size."""
+    import numpy as np
+    import oracle as O
+    import synth
+
+    N = w.n_ctx
+    t = O.yarn_table(original_max_position=w.orig)
+    k, v, kw = _oracle_cache(W, w, 0, torch, dev)
+    pos = np.arange(N - nq, N)
+    q_raw = synth.host_fill(w.seed, synth.stream_id(0, synth.Q), 0, nq, w.hq, 256)
+    qf = O.bf16_to_f64(O.rope(q_raw, pos, t, bf16_out=True))
+    t0 = time.perf_counter()
+    O.prefill_attention(qf, pos, k, v, **kw)
+    total = time.perf_counter() - t0
+    return {"value": N / total, "unit": "KV token-layers/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"one layer of the {w.name} workload: {nq} causal queries x {w.hq} q heads "
+                      f"over {N} cached tokens, fp64, {total:.2f} s"}
 
 
 def cpu_prefill_baseline(W, w, torch, dev):
@@ -325,7 +362,7 @@ def build_verify_step(W, Y, w, layers, nq, torch, dev):
 
 
 def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2, 4, 6),
-                 per_token=KV_BYTES_PER_TOKEN_LAYER, fmt="bf16", record=None):
+                 per_token=KV_BYTES_PER_TOKEN_LAYER, fmt="bf16", record=None, cpu=False):
     """Verify steps at several query counts over the decode layers; the entry
     for main_nq (3 draft tokens) is the headline, the others are listed."""
     res = {}
@@ -341,7 +378,7 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
         del step, ev
         torch.cuda.empty_cache()
     m = res[main_nq]
-    return {
+    out = {
         "workload": f"speculative verify step, {w.layers} layers x 1,048,576 + {main_nq} cached "
                     f"tokens ({fmt}), {main_nq} causal queries x 24 q / 4 KV heads",
         "value": m["value"], "unit": "KV token-layers/s", "ms_per_step": m["ms_per_step"],
@@ -351,6 +388,10 @@ def bench_verify(W, Y, w, layers, torch, dev, steps, warmup, main_nq=4, sweep=(2
                                  "median_ms": r["launch"]["median_ms"], "frac": r["frac"]}
                        for nq, r in res.items()},
     }
+    if cpu:
+        log(f"{w.name}: verify oracle on the host cores")
+        out["cpu_baseline"] = cpu_verify_baseline(W, w, torch, dev, main_nq)
+    return out
 
 
 def bench_prefill(W, Y, torch, dev, reps, name="prefill", cpu=False):
@@ -573,7 +614,7 @@ def main():
     if layers is not None and not args.no_verify and want("verify"):
         log("timing verify steps")
         result["verify"] = bench_verify(W, Y, w, layers, torch, dev, sub_steps, args.warmup,
-                                        record="verify_split_bf16_long_q4_1m.json")
+                                        record="verify_split_bf16_long_q4_1m.json", cpu=cpu)
     del layers
     torch.cuda.empty_cache()
     if not args.no_configs:
@@ -617,14 +658,14 @@ def main():
             W, Y, wi, torch, dev, sub_steps, args.warmup, INT8_BYTES_PER_TOKEN_LAYER,
             "decode step, 16 layers x 1,048,576 cached tokens, INT8 group-64 cache (2,112 B "
             "per token-layer), 24 q / 4 KV heads", record="decode_split_int8_long_int8_1m.json",
-            cpu_seconds=0, keep_layers=True)
+            cpu_seconds=3.0 if cpu else 0, keep_layers=True)
         result["int8_decode"] = res
         if not args.no_verify:
             log("timing INT8 verify steps")
             result["int8_verify"] = bench_verify(
                 W, Y, wi, li, torch, dev, sub_steps, args.warmup,
                 per_token=INT8_BYTES_PER_TOKEN_LAYER, fmt="INT8 group-64",
-                record="verify_split_int8_long_int8_q4_1m.json")
+                record="verify_split_int8_long_int8_q4_1m.json", cpu=cpu)
         del li
         torch.cuda.empty_cache()
     if not args.no_append and want("append"):
@@ -640,7 +681,7 @@ def main():
             W, Y, wt, torch, dev, sub_steps, args.warmup, KV_BYTES_PER_TOKEN_LAYER * wt.hkv // 4,
             f"decode step, {wt.layers} layers x 1,048,576 cached tokens (bf16), "
             f"{wt.hq} q / {wt.hkv} KV heads", record="decode_split_bf16_tp2_share_1m.json",
-            cpu_seconds=0)
+            cpu_seconds=2.0 if cpu else 0)
         share = {"decode": res}
         if not args.no_prefill:
             share["prefill"] = bench_prefill(W, Y, torch, dev, reps=3, name="prefill_tp2")
