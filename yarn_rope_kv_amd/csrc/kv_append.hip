@@ -106,18 +106,30 @@ __device__ __forceinline__ int e4m3_encode(double q) {
 }
 
 // The scale of one 16-element block from its largest magnitude (bf16 bits;
-// |x| orders like the low 15 bits): the e4m3 code and the effective scale
-// e4m3 * S (exact in fp64).
+// |x| orders like the low 15 bits): the e4m3 code and what the element codes
+// are decided with: the effective scale e4m3 * S (exact in fp64) and, for the
+// fp32 path, e4m3 (exact in fp32) and S as fp32.
 struct Fp4Block {
   int qs;
   double eff;
+  float e4, s32;
 };
 __device__ __forceinline__ Fp4Block nvfp4_block(uint32_t bmax_bits, double S) {
   const double b = (double)bf16_to_f32((uint16_t)bmax_bits);
   Fp4Block B;
   B.qs = e4m3_encode(b / (6.0 * S));
-  B.eff = e4m3_value(B.qs) * S;
+  const double e4 = e4m3_value(B.qs);
+  B.eff = e4 * S;
+  B.e4 = (float)e4;
+  B.s32 = (float)S;
   return B;
+}
+
+// Whether the fp32 decisions below are exact for tensor scale S (an fp32
+// value): 2^-109 <= S <= 2^100.  Outside that range (tensor maxima below
+// ~2^-97 or a caller's own extreme scale) the fp64 decisions are taken.
+__device__ __forceinline__ bool nvfp4_f32_exact(double S) {
+  return S >= 0x1p-109 && S <= 0x1p100;
 }
 
 // Code of one bf16 element: sign bit | nearest e2m1 magnitude of |x| / eff.
@@ -135,6 +147,27 @@ __device__ __forceinline__ uint32_t nvfp4_code(uint32_t bits, const Fp4Block& B)
   return (((bits >> 15) & 1u) << 3) | mag;
 }
 
+// The same code from fp32 arithmetic, exact when nvfp4_f32_exact(S).  Each
+// decision compares a = |x| with t e4 S for a decision point t: P = t e4 is
+// exact in fp32 (t has at most 3 significant bits, e4 at most 4), and the
+// fused multiply-add rounds a - P S once, so its sign is the sign of the
+// exact difference unless that difference rounds to zero without being zero.
+// It cannot: a is a multiple of 2^-133 (bf16), P of 2^-11 and S (normal, at
+// least 2^-109) of 2^(e_S - 23) >= 2^-132, so a nonzero difference is at
+// least 2^-143 in magnitude; and with S <= 2^100 nothing overflows.  The
+// 7 monotone decisions are taken as a binary search: 1.75 (>=), then 0.75 or
+// 3.5 (>=), then 0.25, 1.25, 2.5 or 5 (>).
+__device__ __forceinline__ uint32_t nvfp4_code_f32(uint32_t bits, const Fp4Block& B) {
+  const float a = bf16_to_f32((uint16_t)(bits & 0x7fffu));
+  const float e4 = B.e4, S = B.s32;
+  const bool c1 = __builtin_fmaf(-1.75f * e4, S, a) >= 0.0f;
+  const bool c2 = __builtin_fmaf(-(c1 ? 3.5f : 0.75f) * e4, S, a) >= 0.0f;
+  const float t3 = c1 ? (c2 ? 5.0f : 2.5f) : (c2 ? 1.25f : 0.25f);
+  const bool c3 = __builtin_fmaf(-t3 * e4, S, a) > 0.0f;
+  const uint32_t mag = B.qs == 0 ? 0u : (uint32_t)c1 * 4u + (uint32_t)c2 * 2u + (uint32_t)c3;
+  return (((bits >> 15) & 1u) << 3) | mag;
+}
+
 // Quantise 16 bf16 values: returns the scale code and writes 8 packed bytes
 // (element 2j in the low nibble of byte j).
 __device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, double S,
@@ -148,10 +181,18 @@ __device__ __forceinline__ uint32_t quantize16(const uint4 lo, const uint4 hi, d
   }
   const Fp4Block B = nvfp4_block(bmax, S);
   uint32_t out[2] = {0u, 0u};
+  if (nvfp4_f32_exact(S)) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
-    out[i >> 3] |= nvfp4_code(bits, B) << (4 * (i & 7));
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
+      out[i >> 3] |= nvfp4_code_f32(bits, B) << (4 * (i & 7));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
+      out[i >> 3] |= nvfp4_code(bits, B) << (4 * (i & 7));
+    }
   }
   packed->x = out[0];
   packed->y = out[1];
@@ -393,8 +434,13 @@ __device__ __forceinline__ void store_row4(const AppendArgs& a, bool is_k, int64
     for (int i = 0; i < 4; ++i) m = max(m, e[i] & 0x7fffu);
     const Fp4Block B = nvfp4_block(quad_max_u32(m), S);
     uint32_t packed = 0;
+    if (nvfp4_f32_exact(S)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) packed |= nvfp4_code(e[i], B) << (4 * i);
+      for (int i = 0; i < 4; ++i) packed |= nvfp4_code_f32(e[i], B) << (4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= nvfp4_code(e[i], B) << (4 * i);
+    }
     reinterpret_cast<uint16_t*>(dst)[row * (kHeadDim / 4) + c] = (uint16_t)packed;
     if ((c & 3) == 0)
       (is_k ? a.k_scale_dst : a.v_scale_dst)[row * kQBlocks + (c >> 2)] = (uint8_t)B.qs;
