@@ -445,7 +445,7 @@ def bench_prefill(W, Y, torch, dev, reps, name="prefill", cpu=False):
     return res
 
 
-def bench_append(W, Y, torch, dev, reps=3):
+def bench_append(W, Y, torch, dev, reps=10):
     """Filling one 1,048,576-token layer (4 KV heads, paged over a seeded
     permutation): the bf16 copy, the NVFP4 and INT8 quantisers (the NVFP4
     tensor scale included), the plain rope of the keys, and the fused rope +
@@ -463,17 +463,23 @@ def bench_append(W, Y, torch, dev, reps=3):
     yp = w.yarn()
 
     def timed(fn):
+        """Mean of reps calls, each between its own pair of HIP events (the
+        median is reported beside it)."""
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ev = []
         for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
             fn()
-        e1.record()
+            e1.record()
+            ev.append((e0, e1))
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        ms = [a.elapsed_time(b) for a, b in ev]
+        timed.median = statistics.median(ms)
+        return sum(ms) / len(ms)
 
     out = {}
     read = 2 * w.hkv * 256 * 2 * N
@@ -493,20 +499,21 @@ def bench_append(W, Y, torch, dev, reps=3):
             extra = 0
         ms = timed(fn)
         b = read + extra + written * N
-        out[name] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
-                     "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out[name] = {"ms": ms, "median_ms": timed.median, "bytes": b,
+                     "GBs": b / (ms * 1e-3) / 1e9, "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if kv == Y.KV_BF16:
             ms = timed(lambda: Y.rope_append(L, yp, None, k, v, bt, pos))
             b = read + written * N
-            out["bf16_rope_append_fused"] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
+            out["bf16_rope_append_fused"] = {"ms": ms, "median_ms": timed.median, "bytes": b,
+                                             "GBs": b / (ms * 1e-3) / 1e9,
                                              "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del L
         torch.cuda.empty_cache()
     kr = k.clone()
     ms = timed(lambda: Y.yarn_rope_apply(yp, kr, pos))
     b = 2 * w.hkv * 128 * N
-    out["rope_keys"] = {"ms": ms, "bytes": b, "GBs": b / (ms * 1e-3) / 1e9,
-                        "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["rope_keys"] = {"ms": ms, "median_ms": timed.median, "bytes": b,
+                        "GBs": b / (ms * 1e-3) / 1e9, "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     out["workload"] = ("one layer: 1,048,576 tokens x 4 KV heads x 256 (bf16 K and V in HBM), "
                        "paged over a seeded permutation of 65,536 pages")
     return out

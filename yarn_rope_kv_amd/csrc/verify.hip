@@ -78,11 +78,24 @@ __device__ __forceinline__ u32x4_t split_weights(const float (&p)[4]) {
 // from one 8-wave workgroup with the priority balance (balance_issue), not
 // two 4-wave workgroups, whose first-placed one ran far ahead of the other:
 // per 1M-token layer at 1, 2 and 4 queries 725, 727 and 731 us against 732,
-// 736 and 752 us.
+// 736 and 752 us.  Three column blocks leave one wave per SIMD, and there the
+// page loop is pipelined (kPipelined): 6 queries 858 -> 737 us.  (The same
+// pipelining of the INT8 kernel, whose pages carry far more vector work and
+// which then keeps one page ahead instead of two, measured 857 against
+// 828 us.)
 template <int C> struct VerifyTune;
-template <> struct VerifyTune<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 0); };
-template <> struct VerifyTune<2> { static constexpr int kAhead = 0, kWaves = verify_waves(2, 0); };
-template <> struct VerifyTune<3> { static constexpr int kAhead = 1, kWaves = verify_waves(3, 0); };
+template <> struct VerifyTune<1> {
+  static constexpr int kAhead = 1, kWaves = verify_waves(1, 0);
+  static constexpr bool kPipelined = false;
+};
+template <> struct VerifyTune<2> {
+  static constexpr int kAhead = 0, kWaves = verify_waves(2, 0);
+  static constexpr bool kPipelined = false;
+};
+template <> struct VerifyTune<3> {
+  static constexpr int kAhead = 1, kWaves = verify_waves(3, 0);
+  static constexpr bool kPipelined = true;
+};
 
 // One lane's share of one page: 16-byte chunks 4 j + kg of key and value
 // row t (head dims 32 j + 8 kg .. +7).
@@ -98,7 +111,10 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
   constexpr int NW = VerifyTune<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
   constexpr int NT = 64 * NW;
   static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
-  constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
+  // one staged V page per wave; two where the page loop is pipelined
+  constexpr bool PIPE = VerifyTune<C>::kPipelined;
+  constexpr int kStagePages = PIPE ? 2 : 1;
+  constexpr int kStageV = NW * kStagePages * kBlockSize * kRowBytesF16;
   constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
   constexpr int kLds = kStageV + C * kQOpBytes > kFinish ? kStageV + C * kQOpBytes : kFinish;
   const DecodeArgs& a = va.d;
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
     const uint16_t* V = static_cast<const uint16_t*>(a.v);
     const int64_t page0 = tok0 / kBlockSize;
     const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-    uint8_t* my_stage = lds + wave * (kBlockSize * kRowBytesF16);
+    uint8_t* my_stage = lds + wave * (kStagePages * kBlockSize * kRowBytesF16);
     const float cl2 = a.scale_log2;
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
@@ -194,11 +210,19 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
       }
     };
 
-    auto compute_unit = [&](int64_t pi, VUnit& U) {
+    // tokens of page pi that lie in the split (0 for a masked page), and
+    // whether every row sees all of them
+    auto page_extent = [&](int64_t pi, bool ok, int* nv, bool* full) {
       const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
-      const int nv = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
-      // every row sees every token of the page (the same for all lanes)
-      const bool full = nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
+      *nv = ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
+      *full = *nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
+    };
+
+    // stage V of the page into `stage`: row lo, logical chunks 4 j + hi
+    auto stage_v = [&](int64_t pi, VUnit& U, uint8_t* stage) {
+      int nv;
+      bool full;
+      page_extent(pi, U.ok, &nv, &full);
       if (nv < kBlockSize) {
         // rows outside the split or the sequence, or of a masked page, get
         // weight 0; their stale values become zeros (0 * NaN is not 0)
@@ -206,14 +230,14 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 #pragma unroll
         for (int j = 0; j < 8; ++j) U.v[j] = keep ? U.v[j] : u32x4_t{0u, 0u, 0u, 0u};
       }
-      // stage V: row lo, logical chunks 4 j + hi
-      {
-        uint8_t* row = my_stage + lo * kRowBytesF16;
+      uint8_t* row = stage + lo * kRowBytesF16;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<u32x4_t*>(row + ((4 * j + hi) ^ vswz(lo)) * 16) = U.v[j];
-      }
-      floatx4_t sc[C];
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x4_t*>(row + ((4 * j + hi) ^ vswz(lo)) * 16) = U.v[j];
+    };
+
+    // S^T = K Q^T of the page, per column block
+    auto scores = [&](const VUnit& U, floatx4_t (&sc)[C]) {
 #pragma unroll
       for (int c = 0; c < C; ++c) sc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -221,7 +245,14 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 #pragma unroll
         for (int c = 0; c < C; ++c) sc[c] = mfma_bf16(U.k[j], qop[(c * 8 + j) * 64 + lane], sc[c]);
       }
-      u32x4_t pop[C];
+    };
+
+    // masks, the lazy rescale of O and the row sums, and the P^T operands
+    auto softmax = [&](int64_t pi, bool ok, const floatx4_t (&sc)[C], u32x4_t (&pop)[C]) {
+      int nv;
+      bool full;
+      page_extent(pi, ok, &nv, &full);
+      const int64_t pt0 = (page0 + pi) * kBlockSize;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float x[4];
@@ -248,11 +279,14 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
         pop[c] = split_weights(p);
         lsum[c] = mfma_bf16(ones, pop[c], lsum[c]);
       }
-      // O^T += V^T (P_hi + P_lo)^T
+    };
+
+    // O^T += V^T (P_hi + P_lo)^T from the staged page
+    auto pv = [&](const uint8_t* stage, const u32x4_t (&pop)[C]) {
       wave_lds_sync();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint2 vt = vt_operand(my_stage, i, lo, hi);
+        const uint2 vt = vt_operand(stage, i, lo, hi);
         const u32x4_t av = {vt.x, vt.y, vt.x, vt.y};
 #pragma unroll
         for (int c = 0; c < C; ++c) o[c][i] = mfma_bf16(av, pop[c], o[c][i]);
@@ -260,18 +294,72 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
       wave_lds_sync();
     };
 
+    auto compute_unit = [&](int64_t pi, VUnit& U) {
+      stage_v(pi, U, my_stage);
+      floatx4_t sc[C];
+      scores(U, sc);
+      u32x4_t pop[C];
+      softmax(pi, U.ok, sc, pop);
+      pv(my_stage, pop);
+    };
+
     // wave w takes pages w, w + NW, ...
-    VUnit U[AHEAD + 1];
-    uint32_t done = 0;
+    if constexpr (PIPE) {
+      // One wave per SIMD: nothing else fills the matrix core while a page's
+      // chain (scores, then the softmax on the vector ALUs, then the value
+      // products) runs.  So the scores of page n + 1 go to the matrix core
+      // ahead of page n's value products, and its softmax follows them (the
+      // rescale of O after page n's products, as in the plain order), with
+      // page n + 1's V staged in the other half of the wave's staging.  The
+      // operations on O, the row sums and the running maxima are those of
+      // the plain loop, in the same order: the results are the same bits.
+      // Page n + 2 loads while page n + 1 is scored.
+      static_assert(AHEAD == 1, "the pipelined loop keeps one page ahead");
+      VUnit U[2];
+      u32x4_t pop[C];
+      load_unit(wave, U[0]);
+      load_unit(wave + NW, U[1]);
+      {
+        stage_v(wave, U[0], my_stage);
+        floatx4_t sc[C];
+        scores(U[0], sc);
+        softmax(wave, U[0].ok, sc, pop);
+      }
+      // one step: page u's value products, page u + NW's scores and softmax;
+      // Ucur held page u (scored and staged a step ago) and takes page u + 2 NW
+      auto step = [&](int64_t u, VUnit& Ucur, VUnit& Unxt, uint8_t* st_cur, uint8_t* st_nxt) {
+        const int64_t un = u + NW;
+        floatx4_t sc[C];
+        const bool has_next = un < npages;
+        const bool next_ok = Unxt.ok;
+        if (has_next) {
+          stage_v(un, Unxt, st_nxt);
+          scores(Unxt, sc);
+        }
+        load_unit(u + 2 * NW, Ucur);
+        pv(st_cur, pop);
+        if (has_next) softmax(un, next_ok, sc, pop);
+      };
+      uint8_t* st0 = my_stage;
+      uint8_t* st1 = my_stage + kBlockSize * kRowBytesF16;
+      // unrolled by two so that the ring's registers are named statically
+      for (int64_t u = wave; u < npages; u += 2 * NW) {
+        step(u, U[0], U[1], st0, st1);
+        if (u + NW < npages) step(u + NW, U[1], U[0], st1, st0);
+      }
+    } else {
+      VUnit U[AHEAD + 1];
+      uint32_t done = 0;
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * NW, U[k]);
-    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * NW) {
+      for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * NW, U[k]);
+      for (int64_t u = wave; u < npages; u += (AHEAD + 1) * NW) {
 #pragma unroll
-      for (int b = 0; b <= AHEAD; ++b) {
-        const int64_t uu = u + b * NW;
-        load_unit(uu + AHEAD * NW, U[(b + AHEAD) % (AHEAD + 1)]);
-        if (uu < npages) compute_unit(uu, U[b]);
-        if constexpr (NW == 8) balance_issue<NW>(progress, ++done, wave, lane);
+        for (int b = 0; b <= AHEAD; ++b) {
+          const int64_t uu = u + b * NW;
+          load_unit(uu + AHEAD * NW, U[(b + AHEAD) % (AHEAD + 1)]);
+          if (uu < npages) compute_unit(uu, U[b]);
+          if constexpr (NW == 8) balance_issue<NW>(progress, ++done, wave, lane);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
