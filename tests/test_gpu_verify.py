@@ -202,7 +202,7 @@ def test_verify_nq1_matches_single_query_oracle(Y):
         _compare_attention(f"verify/nq1/{s}", got[s], refs[s], bf16_out=False)
 
 
-@pytest.mark.parametrize("name,nq", [("long", 4), ("long_int8", 4)])
+@pytest.mark.parametrize("name,nq", [("long", 4), ("long_int8", 4), ("long_int8", 6)])
 def test_verify_long_layer(Y, W, name, nq):
     """The bench's verify step on one layer of the 1,048,576-token workload
     (bf16 cache, and the INT8 group-64 cache): nq new tokens appended at

@@ -42,6 +42,8 @@
 //             head, split); the decode merge then combines the splits.
 #include "attn_common.h"
 
+#include <type_traits>
+
 namespace yrk {
 namespace {
 
@@ -419,6 +421,7 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 // operands are fp16 after one power-of-two prescale shared by the R rows,
 // which puts the largest |q| in [2^14, 2^15) (bf16 values are exact there).
 
+// Used for 1 and 2 column blocks (three go to the team kernel below).
 // Measured per 1M-token layer (2, 4, 6 queries at GQA 6), as two 4-wave
 // workgroups per CU: C = 1 0.427 ms with one page ahead (0.443 with two);
 // C = 2 0.464 ms without a ring; C = 3, one workgroup per CU, 0.941 / 0.897 /
@@ -428,7 +431,6 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 template <int C> struct VerifyTuneI8;
 template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 2); };
 template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWaves = verify_waves(2, 2); };
-template <> struct VerifyTuneI8<3> { static constexpr int kAhead = 2, kWaves = verify_waves(3, 2); };
 
 // One lane's share of one page.
 struct I8VUnit {
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
   constexpr int AHEAD = VerifyTuneI8<C>::kAhead;
   constexpr int NW = VerifyTuneI8<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
   constexpr int NT = 64 * NW;
-  static_assert(C >= 1 && C <= 3 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
+  static_assert(C >= 1 && C <= 2 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
   constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
   constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
   constexpr int kUse = kStageV + C * kQOpBytes + NW * 4;
@@ -738,6 +740,402 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
   }
 }
 
+// ---- INT8 cache, 2 or 3 column blocks: a team of 4 waves per split --------
+//
+// With two or three column blocks the kernel above keeps every block's
+// accumulators in each wave (128 or 192 registers), so one wave runs a page's
+// whole chain (conversion, score products, softmax on the vector ALUs, value
+// products) with at most two waves per SIMD to cover its latencies.  Here a
+// workgroup of 4 waves walks the split's pages together:
+//
+//   compute   waves 0 .. C-1, one per column block (64 accumulator
+//             registers): score products from the staged K, softmax, value
+//             products from the staged V, for its 16 rows;
+//   loading   each page's 512 16-byte code chunks are 8 groups of 64 (4 of
+//             K rows, 4 of V rows); every wave loads whole groups AHEAD
+//             pages ahead and converts them to fp16 integers into the staged
+//             page, the waves without column block the most of them (C = 3:
+//             5 groups on wave 3, one on each compute wave; C = 2: 3 on each
+//             of waves 2 and 3, one on each compute wave);
+//   staging   two LDS pages: in step p the compute waves read page p while
+//             every wave writes its groups of page p + 1 into the other
+//             buffer (last read in step p - 1); one workgroup barrier ends
+//             each step.  K rows and V rows share one swizzle (tswz).
+//
+// The arithmetic per row is the INT8 kernel's above (same prescale of Q,
+// exact integer codes, K group scales on the per-group partial products, V
+// group scales on the fp16 weights, the V-scale shift of the running
+// maximum); a wave's rows see the split's pages in order, so each compute
+// wave writes its rows' normalised partials itself.
+//
+// Launched for three column blocks (5-8 queries at GQA 6), two teams per CU:
+// 6 queries over a 1M-token layer 826 -> 634 us.  Two column blocks stay on
+// the kernel above (470 us at 4 queries against 624 us here).  Measured on
+// the way: one wave per column block with no loader wave (each wave loading
+// and converting its share, 3-wave teams) 679 us; a single loader wave
+// converting every group 594-614 us (the loader was the slowest wave of each
+// step); the loader filling an LDS ring with direct loads 742 us; the value
+// products of page p issued among the scores of page p + 1, 694 us.
+
+// Staged rows keep 16-byte chunk c of row t at position c ^ tswz(t).  tswz is
+// a bijection of 0..15 (so the 16 rows of one score operand read, one chunk
+// index, fall into 16 distinct bank groups) that gives rows 4r .. 4r + 3
+// distinct bits 1-2 and rows 0..3 / 4..7 (8..11 / 12..15) distinct bit 3, so
+// that each 32-lane half of a transposing V read (8 rows x 32 bytes) covers
+// all 64 banks once.
+__device__ __forceinline__ int tswz(int t) {
+  return ((t & 3) << 1) | ((t >> 3) & 1) | (((t >> 2) & 1) << 3);
+}
+
+// A buffer resource over nbytes from p (raw addressing, no stride): loads
+// at offsets past nbytes return zeros without touching memory.  The
+// arguments are uniform; they are read from the first lane so that the
+// descriptor is built in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* p, uint32_t nbytes) {
+  const uint64_t addr = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  void* base = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+}
+
+constexpr int kTeamWaves = 4;
+constexpr int kTeamAhead = 2;   // pages a wave's loads run ahead of the page it stages
+
+// Code-chunk groups (of 8 per page) that wave w loads and converts: groups
+// team_group(C, w, 0 .. team_groups(C, w) - 1).
+constexpr int team_groups(int C, int w) { return w < C ? 1 : (C == 3 ? 5 : 3); }
+constexpr int team_group(int C, int w, int i) {
+  return w < C ? 8 - C + w : (C == 3 ? i : 3 * (w - C) + i);
+}
+
+// One wave's share of one page: NG groups (16 codes per lane each) and, on
+// the first wave without column block, lanes 0..15, row lane's K and V
+// group scales.
+template <int NG>
+struct TeamShare {
+  u32x4_t code[NG];
+  u32x2_t ks, vs;
+  bool ok;   // page present and inside the split
+};
+
+template <int C>
+__global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu(2))) void verify_team_int8(
+    VerifyArgs va) {
+  constexpr int NW = kTeamWaves;
+  constexpr int NU = kTeamAhead + 1;
+  constexpr int kChunks = 2 * kBlockSize * kHeadDim / 16;   // 512: K rows' chunks, then V's
+  constexpr int kStK = 0;
+  constexpr int kStV = kBlockSize * kRowBytesF16;
+  constexpr int kStS = 2 * kBlockSize * kRowBytesF16;       // K scale rows, then V's (8 B each)
+  constexpr int kStN = kStS + 2 * kBlockSize * 8;           // the page's valid rows (int)
+  constexpr int kStage = kStN + 16;                          // 16,656 B per staged page
+  constexpr int kDummy = 2 * kStage;                         // writes that are not kept
+  static_assert(C >= 2 && C <= 3, "team kernel shape");
+  static_assert(team_groups(C, 0) * C + team_groups(C, C) * (NW - C) == kChunks / 64,
+                "every code group has one wave");
+  const DecodeArgs& a = va.d;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDummy + 64 * 16];
+  __shared__ float red[NW];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo = lane & 15, hi = lane >> 4;
+  const int G = a.group, nq = va.num_queries, R = nq * G;
+
+  int64_t len = a.seq_lens[s];
+  if (len > a.max_seq_len) {
+    if (threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+    len = a.max_seq_len;
+  }
+  if (len < va.min_len && threadIdx.x == 0 && split == 0 && g == 0) err_flag(a.err, kErrPosition);
+  if (len < 0) len = 0;
+  const int64_t qpos0 = len - nq;
+  const int64_t tok0 = (int64_t)split * a.plan.tokens_per_split;
+  const int64_t tok1 = min(len, tok0 + a.plan.tokens_per_split);
+  const int npages = tok1 > tok0 ? (int)((tok1 - tok0 + kBlockSize - 1) / kBlockSize) : 0;
+  const int64_t page0 = tok0 / kBlockSize;
+  const bool paged = a.geo.paged;
+  const int64_t ts = paged ? 1 : a.geo.num_kv_heads;   // rows between a page's tokens
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.k);
+  const uint8_t* Vc = static_cast<const uint8_t*>(a.v);
+  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(a.k_scale);
+  const uint16_t* Vs = reinterpret_cast<const uint16_t*>(a.v_scale);
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const const_i32* trow =
+      (const const_i32*)(const void*)(a.block_tables + (int64_t)s * a.block_table_stride);
+  const bool has_scale = wave == C && lane < kBlockSize;
+  const uint32_t sc_off = has_scale ? (uint32_t)(lane * ts * 8) : 0xFFFFFFF0u;
+
+  auto team_barrier = []() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // The step loop shared by both roles.  Step p stages this wave's groups of
+  // page p + 1 into buffer (p + 1) % 2, issues the loads of its groups of page
+  // p + 1 + AHEAD into the unit page p + 1 came from (U[q % NU] holds page q),
+  // then runs body(p) and the barrier.  The loop starts 2 NU steps early, with
+  // steps on pages before the first (empty ranges, staged into a buffer that
+  // is not read), so that every step is alike and the waits for a page's loads
+  // leave the later pages' loads in flight; body does nothing for p < 0.  The
+  // table entries of a block of 2 NU steps are scalar loads at the block's
+  // start (the scalar counter, which each step's barrier drains).  The loop is
+  // unrolled over a block so that units and buffers are named statically.
+  auto run_steps = [&](auto tag, auto loader, auto&& body) {
+    constexpr int NG = decltype(tag)::value;
+    constexpr bool LOADER = decltype(loader)::value;   // the waves without column block
+    uint32_t code_off[NG], st_off[NG][2];
+    const uint8_t* code_base[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int grp = team_group(C, wave < C ? 0 : C, i) + (wave < C ? wave : (C == 3 ? 0 : 3 * (wave - C)));
+      const int ci = (64 * grp + lane) & 255;
+      const int t = ci >> 4, c16 = ci & 15;
+      code_off[i] = (uint32_t)(t * ts * kHeadDim + 16 * c16);
+      code_base[i] = grp < 4 ? Kc : Vc;
+      const uint32_t row = (grp < 4 ? kStK : kStV) + t * kRowBytesF16;
+      st_off[i][0] = row + (((2 * c16) ^ tswz(t)) * 16);
+      st_off[i][1] = row + (((2 * c16 + 1) ^ tswz(t)) * 16);
+    }
+    auto load_share = [&](int pi, int32_t entry, TeamShare<NG>& U) {
+      const int nv = min(kBlockSize, (int)(tok1 - tok0) - kBlockSize * pi);
+      const int32_t blk = __builtin_amdgcn_readfirstlane(entry);
+      const bool in = pi >= 0 && pi < npages;
+      const bool blk_ok = !paged || (blk >= 0 && blk < a.geo.num_blocks);
+      if (in && !blk_ok && threadIdx.x == 0) err_flag(a.err, kErrBlockId);
+      const bool ok = in && blk_ok;
+      const int64_t base = paged ? ((int64_t)blk * a.geo.num_kv_heads + g) * kBlockSize
+                                 : (page0 + pi) * kBlockSize * a.geo.num_kv_heads + g;
+      U.ok = ok;
+      // the ranges end after row nv - 1: rows past the split load as zeros
+      const uint32_t rows = ok ? (uint32_t)((nv - 1) * ts + 1) : 0u;
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        U.code[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         byte_range(code_base[i] + base * kHeadDim, rows * kHeadDim), code_off[i], 0, 0));
+      if constexpr (LOADER) {
+        // (on every loader wave, so that their loads count alike; only the
+        // first one's lanes 0..15 have offsets inside the range)
+        U.ks = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                               byte_range(Ks + base * 4, rows * 8), sc_off, 0, 0));
+        U.vs = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                               byte_range(Vs + base * 4, rows * 8), sc_off, 0, 0));
+      }
+    };
+    auto stage_share = [&](const TeamShare<NG>& U, int pi, uint8_t* st) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        *reinterpret_cast<uint4*>(st + st_off[i][0]) = i8x8_to_f16(U.code[i][0], U.code[i][1]);
+        *reinterpret_cast<uint4*>(st + st_off[i][1]) = i8x8_to_f16(U.code[i][2], U.code[i][3]);
+      }
+      if constexpr (LOADER) {
+        // scale rows and the page's valid rows (0 for a masked page) from the
+        // first loader wave; the other lanes write to the dummy area
+        *reinterpret_cast<u32x2_t*>(has_scale ? st + kStS + 8 * lane : lds + kDummy + 8 * lane) = U.ks;
+        *reinterpret_cast<u32x2_t*>(has_scale ? st + kStS + 8 * (kBlockSize + lane)
+                                              : lds + kDummy + 8 * lane) = U.vs;
+        *reinterpret_cast<int*>(wave == C && lane == 0 ? st + kStN : lds + kDummy + 8 * lane) =
+            U.ok ? min(kBlockSize, (int)(tok1 - tok0) - kBlockSize * pi) : 0;
+      }
+    };
+    // (the units start as values the compiler cannot see through, so that it
+    // does not fold the first steps into a prologue of their own)
+    TeamShare<NG> U[NU];
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        u32x4_t z = {0u, 0u, 0u, 0u};
+        asm volatile("" : "+v"(z));
+        U[k].code[i] = z;
+      }
+      u32x2_t z2 = {0u, 0u};
+      asm volatile("" : "+v"(z2));
+      U[k].ks = U[k].vs = z2;
+      U[k].ok = false;
+    }
+    for (int p0 = -2 * NU;; p0 += 2 * NU) {
+      int32_t ids[2 * NU];
+#pragma unroll
+      for (int b = 0; b < 2 * NU; ++b) {
+        const int q = min(max(p0 + b + 1 + NU, 0), max(npages - 1, 0));
+        ids[b] = paged && npages > 0 ? trow[page0 + q] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < 2 * NU; ++b) {
+        const int pi = p0 + b;
+        if (pi >= npages) return;
+        stage_share(U[(b + 1) % NU], pi + 1, lds + ((b + 1) & 1) * kStage);
+        load_share(pi + 1 + NU, ids[b], U[(b + 1) % NU]);
+        body(pi, lds + (b & 1) * kStage);
+        team_barrier();
+      }
+    }
+  };
+
+  if (wave >= C) {
+    red[wave] = 0.f;
+    __syncthreads();   // the Q maxima
+    run_steps(std::integral_constant<int, team_groups(C, C)>{}, std::true_type{},
+              [](int, const uint8_t*) {});
+  } else {
+    // Q^T operand of block `wave`, step j: row 16 wave + lo, head dims
+    // 32 j + 8 hi .. +7 (zero beyond R); the prescale is shared by all R
+    // rows, so every wave's maximum goes through LDS
+    const int r = kColRows * wave + lo;
+    u32x4_t qraw[8];
+    float qmax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qraw[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (r < R) {
+        const int64_t h = (int64_t)g * G + r % G;
+        const uint16_t* qrow = a.q + (((int64_t)s * nq + r / G) * a.num_q_heads + h) * kHeadDim;
+        qraw[j] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * j + 8 * hi);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(qraw[j][w])), fabsf(bf16_hi(qraw[j][w]))));
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh));
+    if (lane == 0) red[wave] = qmax;
+    __syncthreads();   // the Q maxima
+    qmax = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) qmax = fmaxf(qmax, red[w]);
+    const int qe = (int)((__float_as_uint(qmax) >> 23) & 0xFF);
+    const int pe = qmax > 0.f ? min(max(268 - qe, 1), 254) : 127;
+    const float qpre = __uint_as_float((uint32_t)pe << 23);
+    const float cl2 = a.scale_log2 * __uint_as_float((uint32_t)(254 - pe) << 23);
+    uint4 qf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t h4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) h4[w] = pk_f16(bf16_lo(qraw[j][w]) * qpre, bf16_hi(qraw[j][w]) * qpre);
+      qf[j] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+    }
+    const int64_t last = qpos0 + (r < R ? r / G : nq - 1);
+    // last key of this lane's row relative to the split's first token
+    const int last_rel = (int)max((int64_t)-1, min(last - tok0, (int64_t)INT32_MAX));
+    const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
+    floatx4_t o[16], lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // the V^T operand for head dims 16 i .. 16 i + 15 (as vt_operand, rows in
+    // the tswz layout): lane (lo, hi) gets dim 16 i + lo at tokens 4 hi .. +3
+    const int vt_row = 4 * hi + (lo >> 2);
+    const uint32_t vt_base = kStV + vt_row * kRowBytesF16 + 8 * (lo & 1);
+    auto vt_read = [&](const uint8_t* st, int i) {
+      const int chunk = 2 * i + ((lo & 3) >> 1);
+      const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t*)(void*)(st + vt_base + ((chunk ^ tswz(vt_row)) * 16)));
+      return __builtin_bit_cast(uint2, v);
+    };
+
+    auto compute_page = [&](int pi, const uint8_t* st) {
+      if (pi < 0) return;
+      // rows of the page inside the split, 0 for a masked page
+      const int nv = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(st + kStN));
+      // tokens 4 hi + e this lane's row sees: those below lim
+      const int lim = min(nv, max(0, last_rel - kBlockSize * pi + 1));
+      // group scales of tokens 4 hi .. 4 hi + 3 (K, then V)
+      const u32x4_t* srow = reinterpret_cast<const u32x4_t*>(st + kStS + 32 * hi);
+      const u32x4_t k01 = srow[0], k23 = srow[1];
+      const u32x4_t v01 = srow[8], v23 = srow[9];
+      u32x2_t ksr[4] = {{k01[0], k01[1]}, {k01[2], k01[3]}, {k23[0], k23[1]}, {k23[2], k23[3]}};
+      u32x2_t vsr[4] = {{v01[0], v01[1]}, {v01[2], v01[3]}, {v23[0], v23[1]}, {v23[2], v23[3]}};
+      // T_g = K_g Q_g^T per scale group
+      floatx4_t tg[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = st + kStK + lo * kRowBytesF16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(krow + (((4 * j + hi) ^ tswz(lo)) * 16));
+        tg[j >> 1] = mfma_f16(kf, qf[j], tg[j >> 1]);
+      }
+      const float vsh = vscale_shift(vsr);
+      float x[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // copy the vector elements out first: a bit cast of a vector element
+        // lvalue reads the vector's first element whatever the index
+        const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;
+        const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
+        const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
+        float v = tg[0][e] * (float)s01[0];
+        v = fmaf(tg[1][e], (float)s01[1], v);
+        v = fmaf(tg[2][e], (float)s23[0], v);
+        v = fmaf(tg[3][e], (float)s23[1], v);
+        x[e] = 4 * hi + e < lim ? v * cl2 : -INFINITY;
+        mx = fmaxf(mx, x[e]);
+      }
+      mx = max_over_row_groups(mx) + vsh;
+      const bool grow = mx > m + kRescaleF4;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] *= alpha;
+        lsum *= alpha;
+      }
+      const float mp = m - kPShiftF4;
+      uint2 pop;
+      pop.x = pk_f16(fast_exp2(x[0] - mp), fast_exp2(x[1] - mp));
+      pop.y = pk_f16(fast_exp2(x[2] - mp), fast_exp2(x[3] - mp));
+      lsum = mfma_f16_k16(ones, pop, lsum);
+      // P^T operands with the V group scales of tokens 4 hi .. 4 hi + 3
+      const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop.x);
+      const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop.y);
+      uint2 pg[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int dw = gg >> 1;
+        const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
+        const f16x2_t s01 =
+            __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel));
+        const f16x2_t s23 =
+            __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[3][dw], vsr[2][dw], sel));
+        pg[gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
+                            __builtin_bit_cast(uint32_t, p23 * s23));
+      }
+      // O^T += V^T (P o s_g)^T; 16 output dims lie in one scale group
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = mfma_f16_k16(vt_read(st, i), pg[i >> 2], o[i]);
+    };
+    run_steps(std::integral_constant<int, team_groups(C, 0)>{}, std::false_type{}, compute_page);
+
+    // this wave's rows: normalised partial and log2-sum-exp (l and O carry 2^kPShiftF4)
+    if (r < R) {
+      const int nsp = a.plan.num_splits;
+      const int64_t rows_per_seq = (int64_t)nq * a.num_q_heads;
+      const int64_t hh = (int64_t)(r / G) * a.num_q_heads + (int64_t)g * G + r % G;
+      const int64_t slot = ((int64_t)s * rows_per_seq + hh) * nsp + split;
+      const float L = lsum[0];
+      float* dst = a.ws_o + slot * kHeadDim + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        floatx4_t v = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        if (L > 0.f) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[i][e] / L;
+        }
+        *reinterpret_cast<floatx4_t*>(dst + 16 * i) = v;
+      }
+      if (hi == 0) a.ws_lse[slot] = L > 0.f ? (m - kPShiftF4) + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
 int column_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
 }  // namespace
@@ -754,7 +1152,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
                    : launch(verify_split_bf16<1>, grid, block, 0, st, a); break;
     case 2: e = i8 ? launch(verify_split_int8<2>, grid, block, 0, st, a)
                    : launch(verify_split_bf16<2>, grid, block, 0, st, a); break;
-    case 3: e = i8 ? launch(verify_split_int8<3>, grid, block, 0, st, a)
+    case 3: e = i8 ? launch(verify_team_int8<3>, grid, block, 0, st, a)
                    : launch(verify_split_bf16<3>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }

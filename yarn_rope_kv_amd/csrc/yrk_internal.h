@@ -17,18 +17,17 @@ constexpr int kMaxRotaryHalf = 128;
 // Launch shapes that the host planners (plan.cpp) and the kernels share.
 constexpr int kAttnWaves = 4;          // waves per split-K attention workgroup
 constexpr int kVerifyColRows = 16;     // query rows per MFMA column block of the verify kernels
-// Waves per workgroup of the verify kernels by column blocks (1..3), one
-// workgroup per CU: two waves per SIMD where the registers allow; three
-// column blocks hold 192 accumulator registers and leave room for one wave
-// per SIMD.  (The cache format is an argument for kernels that may differ.)
+// Waves per workgroup of the verify kernels by column blocks (1..3) and
+// cache format: one workgroup per CU with two waves per SIMD where the
+// registers allow; three column blocks hold 192 accumulator registers and
+// leave room for one wave per SIMD (bf16), while over the INT8 cache they run
+// as teams of 4 waves, one per column block plus a loader, two per CU.
 constexpr int verify_waves(int column_blocks, int32_t dtype) {
   (void)dtype;
   return column_blocks <= 2 ? 8 : 4;
 }
 constexpr int verify_wgs_per_cu(int column_blocks, int32_t dtype) {
-  (void)column_blocks;
-  (void)dtype;
-  return 1;
+  return column_blocks == 3 && dtype == 2 ? 2 : 1;
 }
 constexpr int kPrefillGroup = 6;       // query heads per KV head of the prefill kernel
 constexpr int kPrefillWaves = 4;
