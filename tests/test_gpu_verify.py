@@ -121,8 +121,8 @@ def test_verify_ragged_shapes(Y, hq, hkv, nq):
         _compare_attention(f"verify/{hq}x{hkv}/q{nq}/len{n}", got[s], refs[s], bf16_out=False)
 
 
-_SHAPES_I8 = [(24, 4, 1), (24, 4, 2), (24, 4, 4), (24, 4, 6), (4, 4, 6), (8, 4, 6), (12, 4, 5),
-              (16, 4, 12), (12, 2, 4)]
+_SHAPES_I8 = [(24, 4, 1), (24, 4, 2), (24, 4, 4), (24, 4, 6), (24, 4, 8), (4, 4, 6), (8, 4, 6),
+              (12, 4, 5), (16, 4, 12), (12, 2, 4)]
 
 
 @pytest.mark.parametrize("hq,hkv,nq", _SHAPES_I8)
@@ -140,18 +140,22 @@ def test_verify_int8_ragged_shapes(Y, hq, hkv, nq):
                            bf16_out=False)
 
 
+@pytest.mark.parametrize("nq", [4, 6])
 @pytest.mark.parametrize("v_mul", [2.0 ** 10, 2.0 ** -20])
-def test_verify_int8_value_magnitude_bad_page_and_contiguous(Y, v_mul):
-    _say(f"verify int8 v x {v_mul}, bad page, contiguous")
-    got, refs, err = _verify_batch(Y, [300, 77], 4, 24, 4, seed=970, bad_page=(0, 5),
+def test_verify_int8_value_magnitude_bad_page_and_contiguous(Y, v_mul, nq):
+    """Large and tiny values (the V-scale shift), a planted bad page (flagged,
+    its keys masked) and the contiguous layout, at two and three column
+    blocks."""
+    _say(f"verify int8 v x {v_mul}, nq={nq}, bad page, contiguous")
+    got, refs, err = _verify_batch(Y, [300, 77], nq, 24, 4, seed=970 + nq, bad_page=(0, 5),
                                    kv=Y.KV_INT8, v_mul=v_mul)
     assert err == Y.DEVERR_BLOCK_ID
     for s in range(2):
         assert np.all(np.isfinite(got[s]))
-        _compare_attention(f"verify_int8/v_mul{v_mul:g}/bad_page/{s}", got[s] / v_mul,
+        _compare_attention(f"verify_int8/v_mul{v_mul:g}/q{nq}/bad_page/{s}", got[s] / v_mul,
                            refs[s] / v_mul, bf16_out=False)
-    a, refs, _ = _verify_batch(Y, [1234], 6, 24, 4, seed=975, kv=Y.KV_INT8, v_mul=v_mul)
-    b, _, _ = _verify_batch(Y, [1234], 6, 24, 4, seed=975, paged=False, kv=Y.KV_INT8,
+    a, refs, _ = _verify_batch(Y, [1234], nq, 24, 4, seed=975, kv=Y.KV_INT8, v_mul=v_mul)
+    b, _, _ = _verify_batch(Y, [1234], nq, 24, 4, seed=975, paged=False, kv=Y.KV_INT8,
                             v_mul=v_mul)
     assert np.array_equal(a, b)
 

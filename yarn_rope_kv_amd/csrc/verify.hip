@@ -746,36 +746,47 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
 // accumulators in each wave (128 or 192 registers), so one wave runs a page's
 // whole chain (conversion, score products, softmax on the vector ALUs, value
 // products) with at most two waves per SIMD to cover its latencies.  Here a
-// workgroup of 4 waves walks the split's pages together:
+// workgroup of 4 waves walks the split's pages together, two pages a step:
 //
 //   compute   waves 0 .. C-1, one per column block (64 accumulator
-//             registers): score products from the staged K, softmax, value
-//             products from the staged V, for its 16 rows;
+//             registers): score products from the staged K, one softmax
+//             over the step's 32 tokens, value products from the staged V
+//             on the 32-long inner dimension, for its 16 rows;
 //   loading   each page's 512 16-byte code chunks are 8 groups of 64 (4 of
-//             K rows, 4 of V rows); every wave loads whole groups AHEAD
-//             pages ahead and converts them to fp16 integers into the staged
-//             page, the waves without column block the most of them (C = 3:
-//             5 groups on wave 3, one on each compute wave; C = 2: 3 on each
-//             of waves 2 and 3, one on each compute wave);
-//   staging   two LDS pages: in step p the compute waves read page p while
-//             every wave writes its groups of page p + 1 into the other
-//             buffer (last read in step p - 1); one workgroup barrier ends
-//             each step.  K rows and V rows share one swizzle (tswz).
+//             K rows, 4 of V rows); every wave loads whole groups of the
+//             pages kTeamAhead + 1 steps ahead and converts them to fp16
+//             integers into the staged pages, the waves without column
+//             block the most of them (C = 3: 5 groups on wave 3, one on each
+//             compute wave; C = 2: 3 on each of waves 2 and 3, one on each
+//             compute wave); the first wave without column block also
+//             stages the group scales, the page's valid rows and its
+//             largest V scale;
+//   staging   two LDS buffers of two pages: in step p the compute waves read
+//             the pages of step p while every wave writes its groups of step
+//             p + 1 into the other buffer (last read in step p - 1); one
+//             workgroup barrier ends each step.  K rows and V rows share one
+//             swizzle (tswz).
 //
 // The arithmetic per row is the INT8 kernel's above (same prescale of Q,
 // exact integer codes, K group scales on the per-group partial products, V
 // group scales on the fp16 weights, the V-scale shift of the running
-// maximum); a wave's rows see the split's pages in order, so each compute
-// wave writes its rows' normalised partials itself.
+// maximum), with the running maximum and the rescale taken once per two
+// pages; a wave's rows see the split's pages in order, so each compute wave
+// writes its rows' normalised partials itself.
 //
-// Launched for three column blocks (5-8 queries at GQA 6), two teams per CU:
-// 6 queries over a 1M-token layer 826 -> 634 us.  Two column blocks stay on
-// the kernel above (470 us at 4 queries against 624 us here).  Measured on
-// the way: one wave per column block with no loader wave (each wave loading
-// and converting its share, 3-wave teams) 679 us; a single loader wave
-// converting every group 594-614 us (the loader was the slowest wave of each
-// step); the loader filling an LDS ring with direct loads 742 us; the value
-// products of page p issued among the scores of page p + 1, 694 us.
+// Launched for three column blocks (5-8 queries at GQA 6), two teams per CU.
+// 6 queries over a 1M-token layer: 826 us on the kernel above, 634 us here
+// with one page a step, 550 us with two, 520 us with the V-scale maximum
+// taken once per page by the loader and the scores masked by a select
+// instead of a branch per element.  Two column blocks stay on the kernel
+// above (both about 470 us at 4 queries).  Measured on the way: one wave per
+// column block with no loader wave (each wave loading and converting its
+// share, 3-wave teams) 679 us; a single loader wave converting every group,
+// 594-614 us with one page a step and 563 us with two (the loader is then
+// the slowest wave of each step); the loader filling an LDS ring with direct
+// loads 742 us; the value products of page p issued among the scores of page
+// p + 1, 694 us; loads two to four steps ahead instead of one, slower (more
+// registers, longer unrolled code).
 
 // Staged rows keep 16-byte chunk c of row t at position c ^ tswz(t).  tswz is
 // a bijection of 0..15 (so the 16 rows of one score operand read, one chunk
@@ -801,7 +812,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* p, uint
 }
 
 constexpr int kTeamWaves = 4;
-constexpr int kTeamAhead = 2;   // pages a wave's loads run ahead of the page it stages
+constexpr int kTeamAhead = 0;   // further steps a wave's loads run ahead of the step it stages
 
 // Code-chunk groups (of 8 per page) that wave w loads and converts: groups
 // team_group(C, w, 0 .. team_groups(C, w) - 1).
@@ -829,9 +840,11 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int kStK = 0;
   constexpr int kStV = kBlockSize * kRowBytesF16;
   constexpr int kStS = 2 * kBlockSize * kRowBytesF16;       // K scale rows, then V's (8 B each)
-  constexpr int kStN = kStS + 2 * kBlockSize * 8;           // the page's valid rows (int)
+  constexpr int kStN = kStS + 2 * kBlockSize * 8;           // valid rows, largest V scale bits (2 ints)
   constexpr int kStage = kStN + 16;                          // 16,656 B per staged page
-  constexpr int kDummy = 2 * kStage;                         // writes that are not kept
+  constexpr int kPP = 2;                                     // pages per step
+  constexpr int kStep = kPP * kStage;                        // one staged step (kPP pages)
+  constexpr int kDummy = 2 * kStep;                          // writes that are not kept
   static_assert(C >= 2 && C <= 3, "team kernel shape");
   static_assert(team_groups(C, 0) * C + team_groups(C, C) * (NW - C) == kChunks / 64,
                 "every code group has one wave");
@@ -874,16 +887,17 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
     asm volatile("" ::: "memory");
   };
 
-  // The step loop shared by both roles.  Step p stages this wave's groups of
-  // page p + 1 into buffer (p + 1) % 2, issues the loads of its groups of page
-  // p + 1 + AHEAD into the unit page p + 1 came from (U[q % NU] holds page q),
-  // then runs body(p) and the barrier.  The loop starts 2 NU steps early, with
-  // steps on pages before the first (empty ranges, staged into a buffer that
-  // is not read), so that every step is alike and the waits for a page's loads
-  // leave the later pages' loads in flight; body does nothing for p < 0.  The
-  // table entries of a block of 2 NU steps are scalar loads at the block's
-  // start (the scalar counter, which each step's barrier drains).  The loop is
-  // unrolled over a block so that units and buffers are named statically.
+  // The step loop shared by both roles; step u covers pages 2u and 2u + 1.
+  // Step u stages this wave's groups of step u + 1 into buffer (u + 1) % 2,
+  // issues the loads of its groups of step u + 1 + kTeamAhead into the units
+  // step u + 1 came from (U[q % NU] holds step q), then runs body(u) and the
+  // barrier.  The loop starts 2 NU steps early, with steps on pages before
+  // the first (empty ranges, staged into a buffer that is not read), so that
+  // every step is alike and the waits for a step's loads leave the later
+  // steps' loads in flight; body does nothing for u < 0.  The table entries
+  // of a block of 2 NU steps are scalar loads at the block's start (the
+  // scalar counter, which each step's barrier drains).  The loop is unrolled
+  // over a block so that units and buffers are named statically.
   auto run_steps = [&](auto tag, auto loader, auto&& body) {
     constexpr int NG = decltype(tag)::value;
     constexpr bool LOADER = decltype(loader)::value;   // the waves without column block
@@ -938,40 +952,58 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
         *reinterpret_cast<u32x2_t*>(has_scale ? st + kStS + 8 * lane : lds + kDummy + 8 * lane) = U.ks;
         *reinterpret_cast<u32x2_t*>(has_scale ? st + kStS + 8 * (kBlockSize + lane)
                                               : lds + kDummy + 8 * lane) = U.vs;
-        *reinterpret_cast<int*>(wave == C && lane == 0 ? st + kStN : lds + kDummy + 8 * lane) =
-            U.ok ? min(kBlockSize, (int)(tok1 - tok0) - kBlockSize * pi) : 0;
+        // the largest V group scale of the page's rows, as binary16 bits
+        // (non-negative binary16 bits order like their values; rows past the
+        // page's end and other lanes hold zeros)
+        uint32_t vm = max(max(U.vs[0] & 0xffffu, U.vs[0] >> 16), max(U.vs[1] & 0xffffu, U.vs[1] >> 16));
+        vm = max(vm, (uint32_t)__builtin_amdgcn_mov_dpp((int)vm, 0x128, 0xf, 0xf, false));
+        vm = max(vm, (uint32_t)__builtin_amdgcn_mov_dpp((int)vm, 0x124, 0xf, 0xf, false));
+        vm = max(vm, (uint32_t)__builtin_amdgcn_mov_dpp((int)vm, 0x4e, 0xf, 0xf, false));
+        vm = max(vm, (uint32_t)__builtin_amdgcn_mov_dpp((int)vm, 0xb1, 0xf, 0xf, false));
+        *reinterpret_cast<int2*>(wave == C && lane == 0 ? st + kStN : lds + kDummy + 8 * lane) =
+            make_int2(U.ok ? min(kBlockSize, (int)(tok1 - tok0) - kBlockSize * pi) : 0, (int)vm);
       }
     };
     // (the units start as values the compiler cannot see through, so that it
     // does not fold the first steps into a prologue of their own)
-    TeamShare<NG> U[NU];
+    TeamShare<NG> U[NU][kPP];
 #pragma unroll
-    for (int k = 0; k < NU; ++k) {
+    for (int k = 0; k < NU; ++k)
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        asm volatile("" : "+v"(z));
-        U[k].code[i] = z;
+      for (int pp = 0; pp < kPP; ++pp) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          u32x4_t z = {0u, 0u, 0u, 0u};
+          asm volatile("" : "+v"(z));
+          U[k][pp].code[i] = z;
+        }
+        u32x2_t z2 = {0u, 0u};
+        asm volatile("" : "+v"(z2));
+        U[k][pp].ks = U[k][pp].vs = z2;
+        U[k][pp].ok = false;
       }
-      u32x2_t z2 = {0u, 0u};
-      asm volatile("" : "+v"(z2));
-      U[k].ks = U[k].vs = z2;
-      U[k].ok = false;
-    }
+    const int nsteps = (npages + kPP - 1) / kPP;
     for (int p0 = -2 * NU;; p0 += 2 * NU) {
-      int32_t ids[2 * NU];
+      int32_t ids[2 * NU][kPP];
+#pragma unroll
+      for (int b = 0; b < 2 * NU; ++b)
+#pragma unroll
+        for (int pp = 0; pp < kPP; ++pp) {
+          const int q = min(max(kPP * (p0 + b + 1 + NU) + pp, 0), max(npages - 1, 0));
+          ids[b][pp] = paged && npages > 0 ? trow[page0 + q] : 0;
+        }
 #pragma unroll
       for (int b = 0; b < 2 * NU; ++b) {
-        const int q = min(max(p0 + b + 1 + NU, 0), max(npages - 1, 0));
-        ids[b] = paged && npages > 0 ? trow[page0 + q] : 0;
-      }
+        const int ui = p0 + b;   // step: pages kPP ui .. kPP ui + kPP - 1
+        if (ui >= nsteps) return;
 #pragma unroll
-      for (int b = 0; b < 2 * NU; ++b) {
-        const int pi = p0 + b;
-        if (pi >= npages) return;
-        stage_share(U[(b + 1) % NU], pi + 1, lds + ((b + 1) & 1) * kStage);
-        load_share(pi + 1 + NU, ids[b], U[(b + 1) % NU]);
-        body(pi, lds + (b & 1) * kStage);
+        for (int pp = 0; pp < kPP; ++pp)
+          stage_share(U[(b + 1) % NU][pp], kPP * (ui + 1) + pp,
+                      lds + ((b + 1) & 1) * kStep + pp * kStage);
+#pragma unroll
+        for (int pp = 0; pp < kPP; ++pp)
+          load_share(kPP * (ui + 1 + NU) + pp, ids[b][pp], U[(b + 1) % NU][pp]);
+        body(ui, lds + (b & 1) * kStep);
         team_barrier();
       }
     }
@@ -1023,7 +1055,6 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
     const int64_t last = qpos0 + (r < R ? r / G : nq - 1);
     // last key of this lane's row relative to the split's first token
     const int last_rel = (int)max((int64_t)-1, min(last - tok0, (int64_t)INT32_MAX));
-    const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
     floatx4_t o[16], lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
     float m = kNegBig;
 #pragma unroll
@@ -1039,45 +1070,66 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
       return __builtin_bit_cast(uint2, v);
     };
 
-    auto compute_page = [&](int pi, const uint8_t* st) {
-      if (pi < 0) return;
-      // rows of the page inside the split, 0 for a masked page
-      const int nv = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(st + kStN));
-      // tokens 4 hi + e this lane's row sees: those below lim
-      const int lim = min(nv, max(0, last_rel - kBlockSize * pi + 1));
-      // group scales of tokens 4 hi .. 4 hi + 3 (K, then V)
-      const u32x4_t* srow = reinterpret_cast<const u32x4_t*>(st + kStS + 32 * hi);
-      const u32x4_t k01 = srow[0], k23 = srow[1];
-      const u32x4_t v01 = srow[8], v23 = srow[9];
-      u32x2_t ksr[4] = {{k01[0], k01[1]}, {k01[2], k01[3]}, {k23[0], k23[1]}, {k23[2], k23[3]}};
-      u32x2_t vsr[4] = {{v01[0], v01[1]}, {v01[2], v01[3]}, {v23[0], v23[1]}, {v23[2], v23[3]}};
-      // T_g = K_g Q_g^T per scale group
-      floatx4_t tg[4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = st + kStK + lo * kRowBytesF16;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(krow + (((4 * j + hi) ^ tswz(lo)) * 16));
-        tg[j >> 1] = mfma_f16(kf, qf[j], tg[j >> 1]);
-      }
-      const float vsh = vscale_shift(vsr);
-      float x[4];
+    // one step: pages A = kPP ui (staged at st) and B = A + 1 (at st + kStage),
+    // one softmax over their 32 tokens, the value products on the 32-long
+    // inner dimension (k order: tokens 4 hi .. 4 hi + 3 of A, then of B)
+    auto compute_step = [&](int ui, const uint8_t* st) {
+      if (ui < 0) return;
+      float x[kPP][4];
+      u32x2_t vsr[kPP][4];
       float mx = -INFINITY;
+      uint32_t vsb = 0;   // largest V scale bits of the step's tokens (this lane's rows)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // copy the vector elements out first: a bit cast of a vector element
-        // lvalue reads the vector's first element whatever the index
-        const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;
-        const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
-        const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
-        float v = tg[0][e] * (float)s01[0];
-        v = fmaf(tg[1][e], (float)s01[1], v);
-        v = fmaf(tg[2][e], (float)s23[0], v);
-        v = fmaf(tg[3][e], (float)s23[1], v);
-        x[e] = 4 * hi + e < lim ? v * cl2 : -INFINITY;
-        mx = fmaxf(mx, x[e]);
+      for (int pp = 0; pp < kPP; ++pp) {
+        const uint8_t* sp = st + pp * kStage;
+        const int pi = kPP * ui + pp;
+        // rows of the page inside the split, 0 for a masked page
+        const int2 hdr = *reinterpret_cast<const int2*>(sp + kStN);
+        const int nv = __builtin_amdgcn_readfirstlane(hdr.x);
+        vsb = max(vsb, (uint32_t)__builtin_amdgcn_readfirstlane(hdr.y));
+        // tokens 4 hi + e this lane's row sees: those below lim
+        const int lim = min(nv, max(0, last_rel - kBlockSize * pi + 1));
+        // group scales of tokens 4 hi .. 4 hi + 3 (K, then V)
+        const u32x4_t* srow = reinterpret_cast<const u32x4_t*>(sp + kStS + 32 * hi);
+        const u32x4_t k01 = srow[0], k23 = srow[1];
+        const u32x4_t v01 = srow[8], v23 = srow[9];
+        const u32x2_t ksr[4] = {{k01[0], k01[1]}, {k01[2], k01[3]}, {k23[0], k23[1]}, {k23[2], k23[3]}};
+        vsr[pp][0] = u32x2_t{v01[0], v01[1]};
+        vsr[pp][1] = u32x2_t{v01[2], v01[3]};
+        vsr[pp][2] = u32x2_t{v23[0], v23[1]};
+        vsr[pp][3] = u32x2_t{v23[2], v23[3]};
+        // T_g = K_g Q_g^T per scale group
+        floatx4_t tg[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) tg[gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* krow = sp + kStK + lo * kRowBytesF16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(krow + (((4 * j + hi) ^ tswz(lo)) * 16));
+          tg[j >> 1] = mfma_f16(kf, qf[j], tg[j >> 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // copy the vector elements out first: a bit cast of a vector element
+          // lvalue reads the vector's first element whatever the index
+          const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;
+          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
+          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
+          // (every term a mixed multiply-add; the score is computed on every
+          // lane and the mask selects, with no branch per element)
+          float v = fmaf(tg[0][e], (float)s01[0], 0.f);
+          v = fmaf(tg[1][e], (float)s01[1], v);
+          v = fmaf(tg[2][e], (float)s23[0], v);
+          v = fmaf(tg[3][e], (float)s23[1], v);
+          v *= cl2;
+          asm volatile("" : "+v"(v));
+          x[pp][e] = 4 * hi + e < lim ? v : -INFINITY;
+          mx = fmaxf(mx, x[pp][e]);
+        }
       }
+      // the V-scale shift of the running maximum over the step's tokens (as
+      // vscale_shift: non-negative binary16 bits order like their values)
+      const float vsh = (float)max(0, (int)((vsb >> 10) & 31u) - 14);
       mx = max_over_row_groups(mx) + vsh;
       const bool grow = mx > m + kRescaleF4;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -1089,30 +1141,42 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
         lsum *= alpha;
       }
       const float mp = m - kPShiftF4;
-      uint2 pop;
-      pop.x = pk_f16(fast_exp2(x[0] - mp), fast_exp2(x[1] - mp));
-      pop.y = pk_f16(fast_exp2(x[2] - mp), fast_exp2(x[3] - mp));
-      lsum = mfma_f16_k16(ones, pop, lsum);
+      uint2 pop[kPP];
+#pragma unroll
+      for (int pp = 0; pp < kPP; ++pp) {
+        pop[pp].x = pk_f16(fast_exp2(x[pp][0] - mp), fast_exp2(x[pp][1] - mp));
+        pop[pp].y = pk_f16(fast_exp2(x[pp][2] - mp), fast_exp2(x[pp][3] - mp));
+      }
+      lsum = mfma_f16(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u),
+                      make_uint4(pop[0].x, pop[0].y, pop[1].x, pop[1].y), lsum);
       // P^T operands with the V group scales of tokens 4 hi .. 4 hi + 3
-      const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop.x);
-      const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop.y);
-      uint2 pg[4];
+      uint4 pg[4];
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int dw = gg >> 1;
         const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
-        const f16x2_t s01 =
-            __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel));
-        const f16x2_t s23 =
-            __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[3][dw], vsr[2][dw], sel));
-        pg[gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
-                            __builtin_bit_cast(uint32_t, p23 * s23));
+        uint32_t w[4];
+#pragma unroll
+        for (int pp = 0; pp < kPP; ++pp) {
+          const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop[pp].x);
+          const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop[pp].y);
+          const f16x2_t s01 = __builtin_bit_cast(
+              f16x2_t, __builtin_amdgcn_perm(vsr[pp][1][dw], vsr[pp][0][dw], sel));
+          const f16x2_t s23 = __builtin_bit_cast(
+              f16x2_t, __builtin_amdgcn_perm(vsr[pp][3][dw], vsr[pp][2][dw], sel));
+          w[2 * pp] = __builtin_bit_cast(uint32_t, p01 * s01);
+          w[2 * pp + 1] = __builtin_bit_cast(uint32_t, p23 * s23);
+        }
+        pg[gg] = make_uint4(w[0], w[1], w[2], w[3]);
       }
       // O^T += V^T (P o s_g)^T; 16 output dims lie in one scale group
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = mfma_f16_k16(vt_read(st, i), pg[i >> 2], o[i]);
+      for (int i = 0; i < 16; ++i) {
+        const uint2 va = vt_read(st, i), vb = vt_read(st + kStage, i);
+        o[i] = mfma_f16(make_uint4(va.x, va.y, vb.x, vb.y), pg[i >> 2], o[i]);
+      }
     };
-    run_steps(std::integral_constant<int, team_groups(C, 0)>{}, std::false_type{}, compute_page);
+    run_steps(std::integral_constant<int, team_groups(C, 0)>{}, std::false_type{}, compute_step);
 
     // this wave's rows: normalised partial and log2-sum-exp (l and O carry 2^kPShiftF4)
     if (r < R) {
