@@ -1,9 +1,13 @@
-"""The INT8 append kernel rounds the correctly rounded fp32 quotient x / s to
-the nearest integer (ties to even) where the definition divides exactly.
-For bf16 x and a binary16 group scale s = RNE16(max|x| / 127) both give the
-same code: x / s is a half-integer exactly or at least 2^-12 from one, and
-the fp32 quotient is within 2^-18 of it.  This checks that on the host for
-every bf16 value below sampled group maxima (no GPU)."""
+"""The INT8 append kernel's decisions against the exact arithmetic of the
+definition (group scale s = RNE16(max|x| / 127), codes RNE(x / s)), on the
+host for every bf16 value below sampled group maxima (no GPU):
+  - rounding the correctly rounded fp32 quotient x / s to the nearest
+    integer (ties to even) gives the exact code: x / s is a half-integer
+    exactly or at least 2^-12 from one, and the fp32 quotient is within
+    2^-18 of it;
+  - the group scale from the product with the fp32 1/127 equals the
+    oracle's for every maximum;
+  - the kernels' division-free code decision equals the exact code."""
 import numpy as np
 
 
@@ -30,17 +34,25 @@ def test_fp32_quotient_gives_the_exact_code():
 
 
 def test_fp32_group_scale_equals_the_oracle_scale_for_every_maximum():
-    """The append kernels take the group scale RNE16(m / 127) from the
-    correctly rounded fp32 quotient (then the round-to-nearest-even
-    conversion to binary16, saturating at 65504).  For every bf16 magnitude
-    m that gives the oracle's scale, which rounds the fp64 quotient once."""
+    """The append kernels take the group scale RNE16(m / 127) as m times the
+    fp32 nearest 1/127, converted to binary16 (nearest even, saturating at
+    65504), either through the rounded fp32 product or, where the compiler
+    fuses the two into a mixed-precision multiply-add, from the exact
+    product rounded once.  For every bf16 magnitude m both give the oracle's
+    scale, which rounds the fp64 quotient once; so does the correctly
+    rounded fp32 quotient."""
     import oracle as O
     m = (np.arange(0x0000, 0x7F80, dtype=np.uint32) << 16).view(np.float32)   # 0 and all finite
-    q32 = m / np.float32(127.0)
-    gpu = np.where(q32 >= np.float32(65504.0), np.uint16(0x7BFF),
-                   np.minimum(q32, np.float32(65504.0)).astype(np.float16).view(np.uint16))
     ref = np.array([O.f64_to_f16_sat(float(x) / 127.0) for x in m], dtype=np.uint16)
-    assert np.array_equal(gpu, ref)
+
+    def to16(q):
+        return np.where(q >= 65504.0, np.uint16(0x7BFF),
+                        np.minimum(q, 65504.0).astype(np.float16).view(np.uint16))
+
+    r = np.float32(1.0) / np.float32(127.0)
+    assert np.array_equal(to16(m * r), ref)                                  # fp32 product, then binary16
+    assert np.array_equal(to16(m.astype(np.float64) * np.float64(r)), ref)   # exact product, rounded once
+    assert np.array_equal(to16(m / np.float32(127.0)), ref)                  # fp32 quotient
     assert (ref == 0x7BFF).sum() > 1000 and ((ref > 0) & (ref < 0x0400)).sum() > 100
 
 

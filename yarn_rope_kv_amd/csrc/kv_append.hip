@@ -245,15 +245,21 @@ __global__ __launch_bounds__(256) void append_nvfp4_kernel(AppendArgs a) {
 constexpr int kI8Groups = kHeadDim / 64;   // scale groups per row
 
 // The group scale RNE_binary16(m / 127), saturating at 65504, for a group
-// maximum m (bf16 bits), and its value.  Computed from the correctly
-// rounded fp32 quotient and the hardware conversion to binary16 (nearest
-// even), which gives the rounding of the exact quotient: m = a 2^i with
-// a < 2^8, a binary16 rounding midpoint is c 2^k with c odd and at least
-// 2^11 + 1, so m / 127 is never one (the odd part of a 2^i would be 127 c)
-// and lies at least 2^-19 (relative) from every one, while the fp32
-// quotient is within 2^-24 of it.  Every binary16 value is an fp32 value.
+// maximum m (bf16 bits), and its value.  Computed as m times the fp32
+// nearest 1/127 (no division) and the conversion to binary16 (nearest even;
+// the compiler may fuse the two into one mixed-precision multiply-add, which
+// rounds the exact product once), which gives the rounding of the exact
+// quotient: m = a 2^i with a < 2^8, a normal binary16 rounding midpoint is
+// c 2^k with c odd and at least 2^11 + 1, so m / 127 is never one (the odd
+// part of a 2^i would be 127 c) and lies at least 2^-19 (relative) from
+// every one, while the product is within 2^-23 of it, rounded or not.  The
+// one subnormal midpoint m / 127 reaches, 2^-25 from m = 127 2^-25, is
+// approached from below (the fp32 1/127 is below 1/127) and rounds to 0 as
+// the quotient does.  A host test checks every bf16 magnitude both ways.
+// Every binary16 value is an fp32 value.
 __device__ __forceinline__ uint32_t i8_group_scale(uint32_t mbits, float* value) {
-  const float q = bf16_to_f32((uint16_t)mbits) / 127.0f;
+  constexpr float kInv127 = 1.0f / 127.0f;   // the fp32 nearest 1/127
+  const float q = bf16_to_f32((uint16_t)mbits) * kInv127;
   const uint32_t h =
       q < 65504.0f ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q) : 0x7BFFu;
   *value = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -290,8 +296,8 @@ __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits)
   m = row16_max_u32(m);
   float sv;
   *scale_bits = i8_group_scale(m, &sv);
-  // branch-free: a zero scale (an all-zero group) computes with s = 1 and
-  // keeps code 0
+  // branch-free: a zero scale (an all-zero group) computes with s = 1; its
+  // elements are all +-0, whose codes are then 0
   const bool zero = !(sv > 0.0f);
   const float s1 = zero ? 1.0f : sv;
   const float r = __builtin_amdgcn_rcpf(s1);
@@ -303,7 +309,7 @@ __device__ __forceinline__ uint32_t quantize_i8x4(uint2 w, uint32_t* scale_bits)
     const float h = floorf(q) + 0.5f;
     const float k = fmaf(-h, s1, x) == 0.0f ? rintf(h) : rintf(q);
     const float kc = __builtin_amdgcn_fmed3f(k, -127.0f, 127.0f);
-    const int c = zero ? 0 : (int)kc;
+    const int c = (int)kc;
     packed |= ((uint32_t)c & 0xffu) << (8 * i);
   }
   return packed;
