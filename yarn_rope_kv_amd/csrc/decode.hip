@@ -665,7 +665,10 @@ __global__ __launch_bounds__(kThreadsI8, 2) void decode_split_int8(DecodeArgs a)
 // 15 us long), and the 16 partial (max, sum, weighted output) triples are
 // combined through LDS:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
-// Splits that saw no token carry lse = -inf and weigh nothing.
+// Splits that saw no token carry lse = -inf and weigh nothing.  With at most
+// 4 splits per wave (64 in all, as in the 1M-token decode), a wave loads its
+// maxima and outputs in one round instead of waiting for the maxima first
+// (about 1 us of a 219 us NVFP4 decode call).
 constexpr int kMergeGroups = 16;
 constexpr int kMergeDims = kHeadDim / 4;
 
@@ -680,8 +683,30 @@ __global__ __launch_bounds__(64 * kMergeGroups) void decode_merge(DecodeArgs a) 
   const float* lse = a.ws_lse + slot0;
   const float* o = a.ws_o + slot0 * kHeadDim + d;
   float M = -INFINITY;
-  for (int sp = grp; sp < nsp; sp += kMergeGroups) M = fmaxf(M, lse[sp]);
   float L = 0.f, O = 0.f;
+  if (nsp <= 4 * kMergeGroups) {
+    // at most 4 splits per wave: their maxima and outputs are loaded in one
+    // round (the sums below run in the same order as the general loop's,
+    // with weight 0 for the slots past nsp, so the result is the same)
+    float lv[4], ov[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = grp + u * kMergeGroups;
+      lv[u] = sp < nsp ? lse[sp] : -INFINITY;
+      ov[u] = sp < nsp ? o[(int64_t)sp * kHeadDim] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, lv[u]);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = fast_exp2(lv[u] - M);
+        L += w;
+        O = fmaf(w, ov[u], O);
+      }
+    }
+  } else {
+  for (int sp = grp; sp < nsp; sp += kMergeGroups) M = fmaxf(M, lse[sp]);
   if (M != -INFINITY) {
     int sp = grp;
     for (; sp + 3 * kMergeGroups < nsp; sp += 4 * kMergeGroups) {
@@ -702,6 +727,7 @@ __global__ __launch_bounds__(64 * kMergeGroups) void decode_merge(DecodeArgs a) 
       L += w;
       O = fmaf(w, o[(int64_t)sp * kHeadDim], O);
     }
+  }
   }
   if (dl == 0) {
     sm_m[grp] = M;
