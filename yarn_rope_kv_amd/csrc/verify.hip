@@ -421,16 +421,18 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 // operands are fp16 after one power-of-two prescale shared by the R rows,
 // which puts the largest |q| in [2^14, 2^15) (bf16 values are exact there).
 
-// Used for 1 and 2 column blocks (three go to the team kernel below).
-// Measured per 1M-token layer (2, 4, 6 queries at GQA 6), as two 4-wave
-// workgroups per CU: C = 1 0.427 ms with one page ahead (0.443 with two);
-// C = 2 0.464 ms without a ring; C = 3, one workgroup per CU, 0.941 / 0.897 /
-// 0.819 ms with 0 / 1 / 2 pages ahead (one wave per SIMD leaves latency
-// exposed).  One 8-wave workgroup with the priority balance: 1 and 2 queries
-// 399 and 407 us against 409 and 413 us; 4 queries the same (476 / 474 us).
+// Used for one column block (up to 2 queries at GQA 6; two and three go to
+// the team kernel below).  Measured per 1M-token layer (2, 4, 6 queries at
+// GQA 6), as two 4-wave workgroups per CU: C = 1 0.427 ms with one page ahead
+// (0.443 with two); C = 2 0.464 ms without a ring; C = 3, one workgroup per
+// CU, 0.941 / 0.897 / 0.819 ms with 0 / 1 / 2 pages ahead (one wave per SIMD
+// leaves latency exposed).  One 8-wave workgroup with the priority balance:
+// 1 and 2 queries 399 and 407 us against 409 and 413 us; 4 queries the same
+// (476 / 474 us).  With two pages a step (one softmax per 32 tokens, as in
+// the team kernel) C = 1 measured 406 against 416 us and C = 2 spilled 28
+// registers (995 us).
 template <int C> struct VerifyTuneI8;
 template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 2); };
-template <> struct VerifyTuneI8<2> { static constexpr int kAhead = 0, kWaves = verify_waves(2, 2); };
 
 // One lane's share of one page.
 struct I8VUnit {
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
   constexpr int AHEAD = VerifyTuneI8<C>::kAhead;
   constexpr int NW = VerifyTuneI8<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
   constexpr int NT = 64 * NW;
-  static_assert(C >= 1 && C <= 2 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
+  static_assert(C == 1 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
   constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
   constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
   constexpr int kUse = kStageV + C * kQOpBytes + NW * 4;
@@ -742,10 +744,11 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
 
 // ---- INT8 cache, 2 or 3 column blocks: a team of 4 waves per split --------
 //
-// With two or three column blocks the kernel above keeps every block's
-// accumulators in each wave (128 or 192 registers), so one wave runs a page's
-// whole chain (conversion, score products, softmax on the vector ALUs, value
-// products) with at most two waves per SIMD to cover its latencies.  Here a
+// Keeping two or three column blocks' accumulators in each wave, as the
+// kernel above does for one (128 or 192 registers), leaves one wave to run a
+// page's whole chain (conversion, score products, softmax on the vector ALUs,
+// value products) with at most two waves per SIMD to cover its latencies.
+// Here a
 // workgroup of 4 waves walks the split's pages together, two pages a step:
 //
 //   compute   waves 0 .. C-1, one per column block (64 accumulator
@@ -757,8 +760,8 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
 //             pages kTeamAhead + 1 steps ahead and converts them to fp16
 //             integers into the staged pages, the waves without column
 //             block the most of them (C = 3: 5 groups on wave 3, one on each
-//             compute wave; C = 2: 3 on each of waves 2 and 3, one on each
-//             compute wave); the first wave without column block also
+//             compute wave; C = 2: 4 on each of waves 2 and 3, none on the
+//             compute waves); the first wave without column block also
 //             stages the group scales, the page's valid rows and its
 //             largest V scale;
 //   staging   two LDS buffers of two pages: in step p the compute waves read
@@ -774,12 +777,16 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
 // pages; a wave's rows see the split's pages in order, so each compute wave
 // writes its rows' normalised partials itself.
 //
-// Launched for three column blocks (5-8 queries at GQA 6), two teams per CU.
+// Launched for two and three column blocks (3-8 queries at GQA 6), two teams
+// per CU.
 // 6 queries over a 1M-token layer: 826 us on the kernel above, 634 us here
 // with one page a step, 550 us with two, 520 us with the V-scale maximum
 // taken once per page by the loader and the scores masked by a select
-// instead of a branch per element.  Two column blocks stay on the kernel
-// above (both about 470 us at 4 queries).  Measured on the way: one wave per
+// instead of a branch per element.  Two column blocks (3-4 queries) run here
+// too, with the two waves without column block converting every group: 4
+// queries 478 -> 450-459 us against the kernel above (with one group on each
+// compute wave and 3 on each of the others, the same as the kernel above,
+// 465-476 us).  Measured on the way: one wave per
 // column block with no loader wave (each wave loading and converting its
 // share, 3-wave teams) 679 us; a single loader wave converting every group,
 // 594-614 us with one page a step and 563 us with two (the loader is then
@@ -816,9 +823,9 @@ constexpr int kTeamAhead = 0;   // further steps a wave's loads run ahead of the
 
 // Code-chunk groups (of 8 per page) that wave w loads and converts: groups
 // team_group(C, w, 0 .. team_groups(C, w) - 1).
-constexpr int team_groups(int C, int w) { return w < C ? 1 : (C == 3 ? 5 : 3); }
+constexpr int team_groups(int C, int w) { return w < C ? (C == 3 ? 1 : 0) : (C == 3 ? 5 : 4); }
 constexpr int team_group(int C, int w, int i) {
-  return w < C ? 8 - C + w : (C == 3 ? i : 3 * (w - C) + i);
+  return w < C ? 8 - C + w : (C == 3 ? i : 4 * (w - C) + i);
 }
 
 // One wave's share of one page: NG groups (16 codes per lane each) and, on
@@ -826,7 +833,7 @@ constexpr int team_group(int C, int w, int i) {
 // group scales.
 template <int NG>
 struct TeamShare {
-  u32x4_t code[NG];
+  u32x4_t code[NG > 0 ? NG : 1];
   u32x2_t ks, vs;
   bool ok;   // page present and inside the split
 };
@@ -901,11 +908,12 @@ __global__ __launch_bounds__(64 * kTeamWaves) __attribute__((amdgpu_waves_per_eu
   auto run_steps = [&](auto tag, auto loader, auto&& body) {
     constexpr int NG = decltype(tag)::value;
     constexpr bool LOADER = decltype(loader)::value;   // the waves without column block
-    uint32_t code_off[NG], st_off[NG][2];
-    const uint8_t* code_base[NG];
+    constexpr int NA = NG > 0 ? NG : 1;   // (no zero-length arrays in device code)
+    uint32_t code_off[NA], st_off[NA][2];
+    const uint8_t* code_base[NA];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int grp = team_group(C, wave < C ? 0 : C, i) + (wave < C ? wave : (C == 3 ? 0 : 3 * (wave - C)));
+      const int grp = team_group(C, wave < C ? 0 : C, i) + (wave < C ? wave : (C == 3 ? 0 : 4 * (wave - C)));
       const int ci = (64 * grp + lane) & 255;
       const int t = ci >> 4, c16 = ci & 15;
       code_off[i] = (uint32_t)(t * ts * kHeadDim + 16 * c16);
@@ -1214,7 +1222,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   switch (column_blocks(rows)) {
     case 1: e = i8 ? launch(verify_split_int8<1>, grid, block, 0, st, a)
                    : launch(verify_split_bf16<1>, grid, block, 0, st, a); break;
-    case 2: e = i8 ? launch(verify_split_int8<2>, grid, block, 0, st, a)
+    case 2: e = i8 ? launch(verify_team_int8<2>, grid, block, 0, st, a)
                    : launch(verify_split_bf16<2>, grid, block, 0, st, a); break;
     case 3: e = i8 ? launch(verify_team_int8<3>, grid, block, 0, st, a)
                    : launch(verify_split_bf16<3>, grid, block, 0, st, a); break;

@@ -20,14 +20,14 @@ constexpr int kVerifyColRows = 16;     // query rows per MFMA column block of th
 // Waves per workgroup of the verify kernels by column blocks (1..3) and
 // cache format: one workgroup per CU with two waves per SIMD where the
 // registers allow; three column blocks hold 192 accumulator registers and
-// leave room for one wave per SIMD (bf16), while over the INT8 cache they run
-// as teams of 4 waves, one per column block plus a loader, two per CU.
+// leave room for one wave per SIMD (bf16), while over the INT8 cache two and
+// three column blocks run as teams of 4 waves (one per column block, the
+// rest loading), two per CU.
 constexpr int verify_waves(int column_blocks, int32_t dtype) {
-  (void)dtype;
-  return column_blocks <= 2 ? 8 : 4;
+  return column_blocks <= 1 || (column_blocks == 2 && dtype != 2) ? 8 : 4;
 }
 constexpr int verify_wgs_per_cu(int column_blocks, int32_t dtype) {
-  return column_blocks == 3 && dtype == 2 ? 2 : 1;
+  return column_blocks >= 2 && dtype == 2 ? 2 : 1;
 }
 constexpr int kPrefillGroup = 6;       // query heads per KV head of the prefill kernel
 constexpr int kPrefillWaves = 4;
