@@ -412,8 +412,8 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 //
 // The same rows, column blocks, masks and combine over an INT8 group-64
 // cache, with the INT8 decode kernel's exact integer path: the codes enter
-// the matrix cores as fp16 integers (v_mfma_f32_16x16x32_f16 for the scores,
-// 16x16x16 for the values), each key step covers 32 dims of one scale group
+// the matrix cores as fp16 integers (v_mfma_f32_16x16x32_f16 for the scores
+// and for the values of two pages), each key step covers 32 dims of one scale group
 // so that a group's partial products T_g are scaled by the token's key group
 // scale in fp32, and the value group scales ride on the fp16 weights
 // (p = 2^(s - m + 14), the page counted higher in the running maximum by 1 +
@@ -428,11 +428,13 @@ __global__ __launch_bounds__(64 * VerifyTune<C>::kWaves, 1) void verify_split_bf
 // CU, 0.941 / 0.897 / 0.819 ms with 0 / 1 / 2 pages ahead (one wave per SIMD
 // leaves latency exposed).  One 8-wave workgroup with the priority balance:
 // 1 and 2 queries 399 and 407 us against 409 and 413 us; 4 queries the same
-// (476 / 474 us).  With two pages a step (one softmax per 32 tokens, as in
-// the team kernel) C = 1 measured 406 against 416 us and C = 2 spilled 28
-// registers (995 us).
+// (476 / 474 us).  A wave step now covers two pages, with no step ahead:
+// one softmax over their 32 tokens and the value products on the 32-long
+// inner dimension, as in the team kernel (C = 1: 406 against 416 us with
+// one page a step and one page ahead; at C = 2 the two-page step spilled 28
+// registers, 995 us).
 template <int C> struct VerifyTuneI8;
-template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 1, kWaves = verify_waves(1, 2); };
+template <> struct VerifyTuneI8<1> { static constexpr int kAhead = 0, kWaves = verify_waves(1, 2); };
 
 // One lane's share of one page.
 struct I8VUnit {
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
   constexpr int NW = VerifyTuneI8<C>::kWaves;   // one workgroup per CU, NW / 4 waves per SIMD
   constexpr int NT = 64 * NW;
   static_assert(C == 1 && AHEAD >= 0 && AHEAD <= 2, "verify kernel shape");
-  constexpr int kStageV = NW * kBlockSize * kRowBytesF16;     // one V page per wave
+  constexpr int kStageV = NW * 2 * kBlockSize * kRowBytesF16; // two V pages per wave
   constexpr int kFinish = (NW * kColRows * kHeadDim + 2 * NW * kColRows) * 4;
   constexpr int kUse = kStageV + C * kQOpBytes + NW * 4;
   constexpr int kLds = kUse > kFinish ? kUse : kFinish;
@@ -540,8 +542,8 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
     const uint16_t* Vs = reinterpret_cast<const uint16_t*>(a.v_scale);
     const int64_t page0 = tok0 / kBlockSize;
     const int64_t npages = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-    uint8_t* my_stage = lds + wave * (kBlockSize * kRowBytesF16);
-    const uint2 ones = make_uint2(0x3C003C00u, 0x3C003C00u);
+    uint8_t* my_stage = lds + wave * (2 * kBlockSize * kRowBytesF16);
+    const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 
     auto load_unit = [&](int64_t pi, I8VUnit& U) {
       int64_t base = 0, ts = 0;   // in rows
@@ -579,71 +581,93 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
       U.vs = vs;
     };
 
-    auto compute_unit = [&](int64_t pi, I8VUnit& U) {
-      const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
-      const int nv = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
-      // every row sees every token of the page (the same for all lanes)
-      const bool full = nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
-      if (nv < kBlockSize) {
-        // rows outside the split or the sequence, or of a masked page, get
-        // weight 0; their stale codes and scales become zeros (0 * NaN is not 0)
-        const bool keep = lo < nv;
+    // one step: pages 2 uu and 2 uu + 1, one softmax over their 32 tokens,
+    // the value products on the 32-long inner dimension (k order: tokens
+    // 4 hi .. 4 hi + 3 of the first page, then of the second)
+    auto compute_pair = [&](int64_t uu, I8VUnit (&U2)[2]) {
+      float x[C][2][4];
+      u32x2_t vsr[2][4];
+      float vsh = 0.f;
+      int nvp[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
-        U.ks = keep ? U.ks : u32x2_t{0u, 0u};
-        U.vs = keep ? U.vs : u32x2_t{0u, 0u};
-      }
-      // the group scales of rows 4 hi .. 4 hi + 3 (row r's are in lane r)
-      u32x2_t ksr[4], vsr[4];
+      for (int p = 0; p < 2; ++p) {
+        I8VUnit& U = U2[p];
+        const int64_t pt0 = (page0 + 2 * uu + p) * kBlockSize;
+        nvp[p] = U.ok ? (int)max((int64_t)0, min((int64_t)kBlockSize, tok1 - pt0)) : 0;
+        if (nvp[p] < kBlockSize) {
+          // rows outside the split or the sequence, or of a masked page, get
+          // weight 0; their stale codes and scales become zeros (0 * NaN is not 0)
+          const bool keep = lo < nvp[p];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int src = 4 * (4 * hi + e);
-        ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.x),
-                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.y)};
-        vsr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.x),
-                         (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.y)};
-      }
-      // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
-      {
-        uint8_t* row = my_stage + lo * kRowBytesF16;
+          for (int i = 0; i < 4; ++i) U.vc[i] = keep ? U.vc[i] : u32x4_t{0u, 0u, 0u, 0u};
+          U.ks = keep ? U.ks : u32x2_t{0u, 0u};
+          U.vs = keep ? U.vs : u32x2_t{0u, 0u};
+        }
+        // stage V codes as fp16 integers: row lo, logical chunks 8 hi .. 8 hi + 7
+        uint8_t* row = my_stage + (p * kBlockSize + lo) * kRowBytesF16;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) =
               i8x8_to_f16(U.vc[j >> 1][2 * (j & 1)], U.vc[j >> 1][2 * (j & 1) + 1]);
       }
-      // T_g = K_g Q_g^T per scale group and column block (each key step's
-      // codes are converted once for all blocks)
-      floatx4_t tg[C][4];
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) tg[c][gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 kf = i8x8_to_f16(U.kc[j][0], U.kc[j][1]);
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          tg[c][j >> 1] = mfma_f16(kf, qop[(c * 8 + j) * 64 + lane], tg[c][j >> 1]);
-      }
-      const float vsh = vscale_shift(vsr);
-      uint2 pg[C][4];
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        float x[4];
-        float mx = -INFINITY;
+      for (int p = 0; p < 2; ++p) {
+        I8VUnit& U = U2[p];
+        const int64_t pi = 2 * uu + p;
+        const int64_t pt0 = (page0 + pi) * kBlockSize;   // first token of the page
+        const int nv = nvp[p];
+        // every row sees every token of the page (the same for all lanes)
+        const bool full = nv == kBlockSize && pt0 + kBlockSize - 1 <= qpos0;
+        // the group scales of rows 4 hi .. 4 hi + 3 (row r's are in lane r)
+        u32x2_t ksr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;   // copies: see the INT8 decode kernel
-          const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
-          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
-          float v = tg[c][0][e] * (float)s01[0];
-          v = fmaf(tg[c][1][e], (float)s01[1], v);
-          v = fmaf(tg[c][2][e], (float)s23[0], v);
-          v = fmaf(tg[c][3][e], (float)s23[1], v);
-          const bool vis = full || (4 * hi + e < nv && pt0 + 4 * hi + e <= last[c]);
-          x[e] = vis ? v * cl2 : -INFINITY;
-          mx = fmaxf(mx, x[e]);
+          const int src = 4 * (4 * hi + e);
+          ksr[e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.x),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.ks.y)};
+          vsr[p][e] = u32x2_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.x),
+                              (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.vs.y)};
         }
+        // T_g = K_g Q_g^T per scale group and column block (each key step's
+        // codes are converted once for all blocks)
+        floatx4_t tg[C][4];
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) tg[c][gg] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 kf = i8x8_to_f16(U.kc[j][0], U.kc[j][1]);
+#pragma unroll
+          for (int c = 0; c < C; ++c)
+            tg[c][j >> 1] = mfma_f16(kf, qop[(c * 8 + j) * 64 + lane], tg[c][j >> 1]);
+        }
+        vsh = fmaxf(vsh, vscale_shift(vsr[p]));
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w01 = ksr[e].x, w23 = ksr[e].y;   // copies: see the INT8 decode kernel
+            const f16x2_t s01 = __builtin_bit_cast(f16x2_t, w01);
+            const f16x2_t s23 = __builtin_bit_cast(f16x2_t, w23);
+            float v = fmaf(tg[c][0][e], (float)s01[0], 0.f);
+            v = fmaf(tg[c][1][e], (float)s01[1], v);
+            v = fmaf(tg[c][2][e], (float)s23[0], v);
+            v = fmaf(tg[c][3][e], (float)s23[1], v);
+            v *= cl2;
+            asm volatile("" : "+v"(v));
+            const bool vis = full || (4 * hi + e < nv && pt0 + 4 * hi + e <= last[c]);
+            x[c][p][e] = vis ? v : -INFINITY;
+          }
+      }
+      uint4 pg[C][4];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[c][p][e]);
         mx = max_over_row_groups(mx) + vsh;
         const bool grow = mx > m[c] + kRescaleF4;
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -655,47 +679,62 @@ __global__ __launch_bounds__(64 * VerifyTuneI8<C>::kWaves, 1) void verify_split_
           lsum[c] *= alpha;
         }
         const float mp = m[c] - kPShiftF4;
-        uint2 pop;
-        pop.x = pk_f16(fast_exp2(x[0] - mp), fast_exp2(x[1] - mp));
-        pop.y = pk_f16(fast_exp2(x[2] - mp), fast_exp2(x[3] - mp));
-        lsum[c] = mfma_f16_k16(ones, pop, lsum[c]);
+        uint2 pop[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          pop[p].x = pk_f16(fast_exp2(x[c][p][0] - mp), fast_exp2(x[c][p][1] - mp));
+          pop[p].y = pk_f16(fast_exp2(x[c][p][2] - mp), fast_exp2(x[c][p][3] - mp));
+        }
+        lsum[c] = mfma_f16(ones, make_uint4(pop[0].x, pop[0].y, pop[1].x, pop[1].y), lsum[c]);
         // P^T operands with the V group scales of tokens 4 hi .. 4 hi + 3
-        const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop.x);
-        const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop.y);
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int dw = gg >> 1;
           const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
-          const f16x2_t s01 =
-              __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel));
-          const f16x2_t s23 =
-              __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(vsr[3][dw], vsr[2][dw], sel));
-          pg[c][gg] = make_uint2(__builtin_bit_cast(uint32_t, p01 * s01),
-                                 __builtin_bit_cast(uint32_t, p23 * s23));
+          uint32_t w[4];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const f16x2_t p01 = __builtin_bit_cast(f16x2_t, pop[p].x);
+            const f16x2_t p23 = __builtin_bit_cast(f16x2_t, pop[p].y);
+            const f16x2_t s01 = __builtin_bit_cast(
+                f16x2_t, __builtin_amdgcn_perm(vsr[p][1][dw], vsr[p][0][dw], sel));
+            const f16x2_t s23 = __builtin_bit_cast(
+                f16x2_t, __builtin_amdgcn_perm(vsr[p][3][dw], vsr[p][2][dw], sel));
+            w[2 * p] = __builtin_bit_cast(uint32_t, p01 * s01);
+            w[2 * p + 1] = __builtin_bit_cast(uint32_t, p23 * s23);
+          }
+          pg[c][gg] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
       // O^T += V^T (P o s_g)^T; 16 output dims lie in one scale group
       wave_lds_sync();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint2 vt = vt_operand(my_stage, i, lo, hi);
+        const uint2 va = vt_operand(my_stage, i, lo, hi);
+        const uint2 vb = vt_operand(my_stage + kBlockSize * kRowBytesF16, i, lo, hi);
+        const uint4 vt = make_uint4(va.x, va.y, vb.x, vb.y);
 #pragma unroll
-        for (int c = 0; c < C; ++c) o[c][i] = mfma_f16_k16(vt, pg[c][i >> 2], o[c][i]);
+        for (int c = 0; c < C; ++c) o[c][i] = mfma_f16(vt, pg[c][i >> 2], o[c][i]);
       }
       wave_lds_sync();
     };
 
-    // wave w takes pages w, w + NW, ...
-    I8VUnit U[AHEAD + 1];
+    // wave w takes page pairs w, w + NW, ...
+    const int64_t npairs = (npages + 1) / 2;
+    I8VUnit U[AHEAD + 1][2];
     uint32_t done = 0;
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_unit(wave + k * NW, U[k]);
-    for (int64_t u = wave; u < npages; u += (AHEAD + 1) * NW) {
+    for (int k = 0; k < AHEAD; ++k) {
+      load_unit(2 * (wave + k * NW), U[k][0]);
+      load_unit(2 * (wave + k * NW) + 1, U[k][1]);
+    }
+    for (int64_t u = wave; u < npairs; u += (AHEAD + 1) * NW) {
 #pragma unroll
       for (int b = 0; b <= AHEAD; ++b) {
         const int64_t uu = u + b * NW;
-        load_unit(uu + AHEAD * NW, U[(b + AHEAD) % (AHEAD + 1)]);
-        if (uu < npages) compute_unit(uu, U[b]);
+        load_unit(2 * (uu + AHEAD * NW), U[(b + AHEAD) % (AHEAD + 1)][0]);
+        load_unit(2 * (uu + AHEAD * NW) + 1, U[(b + AHEAD) % (AHEAD + 1)][1]);
+        if (uu < npairs) compute_pair(uu, U[b]);
         if constexpr (NW == 8) balance_issue<NW>(progress, ++done, wave, lane);
       }
     }
