@@ -81,22 +81,27 @@ constexpr int kStageBytes = kWavesF4 * kUnitPages * kBlockSize * kRowBytesF16;  
 constexpr int kAheadF4 = 1;                              // wave steps in flight beyond the one computed
 constexpr int kVtAhead = 4;                              // V^T operands in flight ahead of their products
 
-// Block scale (e4m3 byte SEL of w) as a packed fp16 pair.  The hardware fp8
-// conversion decodes OCP E4M3FN exactly, and every e4m3 value (0 and
-// 2^-9 .. 448) is an fp16 value, so the second conversion is exact too.
-template <int SEL>
-__device__ __forceinline__ uint32_t block_scale_f16x2(uint32_t w) {
-  const float sc = __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
-  return pk_f16(sc, sc);
+// Block scales (e4m3 bytes 2 H and 2 H + 1 of w) as an fp16 pair, one packed
+// conversion.  The hardware fp8 conversion decodes OCP E4M3FN exactly, and
+// every e4m3 value (0 and 2^-9 .. 448) is an fp16 value.  (Two scales per
+// instruction: one per block, converted to fp32 and repacked, took two
+// instructions per block, 48 more per kernel and ~1 us more per 1M-token
+// layer.)
+template <bool H>
+__device__ __forceinline__ uint32_t block_scale_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, H));
 }
 
 // Eight e2m1 codes (one dword; element 2j in the low nibble of byte j) ->
-// eight fp16 values code x q_s, exactly: the unit-scale fp4 conversion gives
-// the e2m1 value (the scaled form multiplies by a power of two only, so the
-// block scale is applied separately), and e2m1 x q_s has at most 6
-// significant bits in [2^-10, 2688], which fp16 holds.
-__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, uint32_t qs2) {
-  const f16x2_t m = __builtin_bit_cast(f16x2_t, qs2);
+// eight fp16 values code x q_s, exactly, q_s being half `which` of a scale
+// pair (the packed multiply selects that half for both lanes of the pair):
+// the unit-scale fp4 conversion gives the e2m1 value (the scaled form
+// multiplies by a power of two only, so the block scale is applied
+// separately), and e2m1 x q_s has at most 6 significant bits in
+// [2^-10, 2688], which fp16 holds.
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, uint32_t pair, int which) {
+  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, pair);
+  const f16x2_t m = which ? __builtin_shufflevector(p2, p2, 1, 1) : __builtin_shufflevector(p2, p2, 0, 0);
   const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m;
   const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m;
   const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m;
@@ -301,33 +306,31 @@ __global__ __launch_bounds__(kThreadsF4, 1) void decode_split_nvfp4(DecodeArgs a
       // stage V as fp16: row lo, logical chunks 8 hi .. 8 hi + 7
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) {
-        const uint32_t bs[4] = {block_scale_f16x2<0>(U.vs[p]), block_scale_f16x2<1>(U.vs[p]),
-                                block_scale_f16x2<2>(U.vs[p]), block_scale_f16x2<3>(U.vs[p])};
+        const uint32_t bs[2] = {block_scale_pair<false>(U.vs[p]), block_scale_pair<true>(U.vs[p])};
         const uint32_t w[8] = {U.vc[p][0][0], U.vc[p][0][1], U.vc[p][0][2], U.vc[p][0][3],
                                U.vc[p][1][0], U.vc[p][1][1], U.vc[p][1][2], U.vc[p][1][3]};
         uint8_t* row = my_stage + (p * kBlockSize + lo) * kRowBytesF16;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) = fp4x8_to_f16(w[j], bs[j >> 1]);
+          *reinterpret_cast<uint4*>(row + ((8 * hi + j) ^ vswz(lo)) * 16) =
+              fp4x8_to_f16(w[j], bs[j >> 2], (j >> 1) & 1);
       }
       // S^T = K Q^T, one accumulator chain per page
       floatx4_t sacc[kUnitPages];
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) sacc[p] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      uint32_t kb[kUnitPages][4];
+      uint32_t kb[kUnitPages][2];
 #pragma unroll
       for (int p = 0; p < kUnitPages; ++p) {
-        kb[p][0] = block_scale_f16x2<0>(U.ks[p]);
-        kb[p][1] = block_scale_f16x2<1>(U.ks[p]);
-        kb[p][2] = block_scale_f16x2<2>(U.ks[p]);
-        kb[p][3] = block_scale_f16x2<3>(U.ks[p]);
+        kb[p][0] = block_scale_pair<false>(U.ks[p]);
+        kb[p][1] = block_scale_pair<true>(U.ks[p]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int p = 0; p < kUnitPages; ++p) {
           const uint32_t w = U.kc[p][j >> 2][j & 3];
-          sacc[p] = mfma_f16(fp4x8_to_f16(w, kb[p][j >> 1]), qop[j], sacc[p]);
+          sacc[p] = mfma_f16(fp4x8_to_f16(w, kb[p][j >> 2], (j >> 1) & 1), qop[j], sacc[p]);
         }
       // online softmax over the unit's 32 tokens (lane: head lo, tokens 4hi..4hi+3 of each page)
       float x[kUnitPages][4];
