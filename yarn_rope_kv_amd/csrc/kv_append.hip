@@ -464,8 +464,13 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
     kS = (double)*a.k_tensor_scale;
     vS = (double)*a.v_tensor_scale;
   }
-  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < a.num_tokens;
+  // W waves share a token (W divides the workgroup's 4 waves): wave share
+  // takes every W-th pass of the token's query heads and of its cache items
+  const int W = ra.waves_per_token;
+  const int wave = threadIdx.x >> 6;
+  const int share = wave % W;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6) / W;
+  for (int64_t t = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) / W; t < a.num_tokens;
        t += wstride) {
     const int32_t pos = a.positions[t];
     double cl, sl;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
       sn[j] = bpermute_f64(4 * (lane & 7) + j, sl);
     }
     if (ra.q && pos >= 0) {         // a negative position is flagged below, q left as it is
-      for (int h0 = 0; h0 < ra.num_q_heads; h0 += 4) {
+      for (int h0 = 4 * share; h0 < ra.num_q_heads; h0 += 4 * W) {
         const int h = h0 + (lane >> 4);
         const int hl = h < ra.num_q_heads ? h : ra.num_q_heads - 1;   // every lane shuffles
         uint2* p = reinterpret_cast<uint2*>(ra.q + t * ra.q_token_stride +
@@ -489,12 +494,12 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs ra) {
     }
     // the token's row for head 0; head h's row follows at a fixed stride
     const int64_t row0 = cache_row(a.geo, a.block_table, a.block_table_len, pos, 0, a.err,
-                                   lane == 0);
+                                   lane == 0 && share == 0);
     if (row0 < 0) continue;
     const int64_t hstride = a.geo.paged ? kBlockSize : 1;
     const int items = H * (kHeadDim / 64);          // (group, head), group-major
     const int sub = lane >> 4, el = lane & 15;      // this lane's item in a pass, element quad
-    for (int i0 = 0; i0 < items; i0 += 4) {
+    for (int i0 = 4 * share; i0 < items; i0 += 4 * W) {
       const int it = i0 + sub < items ? i0 + sub : items - 1;   // every lane shuffles
       const int grp = it / H, h = it % H;
       const int e = grp * 16 + el;                  // uint2 index within the row
@@ -596,10 +601,17 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
   if (a.ap.num_tokens == 0) return hipSuccess;
-  const dim3 grid(grid_for(a.ap.num_tokens * 64, 1 << 18));   // one wave per token
-  if (a.ap.dtype == 0) return launch(rope_append_kernel<0>, grid, dim3(256), 0, s, a);
-  if (a.ap.dtype == 2) return launch(rope_append_kernel<2>, grid, dim3(256), 0, s, a);
-  return launch(rope_append_kernel<1>, grid, dim3(256), 0, s, a);
+  // One wave per token; a launch of few tokens (a decode step appends one per
+  // sequence) gives each token a workgroup of 4 waves instead, each taking a
+  // quarter of its passes, so that their load-rotate-store chains overlap:
+  // one token with 24 query and 4 KV heads went from 6 query and 4 cache
+  // passes in one wave to at most 2 and 1 per wave.
+  RopeAppendArgs k = a;
+  k.waves_per_token = a.ap.num_tokens <= 512 ? 4 : 1;
+  const dim3 grid(grid_for(a.ap.num_tokens * 64 * k.waves_per_token, 1 << 18));
+  if (a.ap.dtype == 0) return launch(rope_append_kernel<0>, grid, dim3(256), 0, s, k);
+  if (a.ap.dtype == 2) return launch(rope_append_kernel<2>, grid, dim3(256), 0, s, k);
+  return launch(rope_append_kernel<1>, grid, dim3(256), 0, s, k);
 }
 
 hipError_t launch_tensor_scale(const uint16_t* x, int64_t n, float* out, hipStream_t s) {

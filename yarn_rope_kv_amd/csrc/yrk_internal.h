@@ -85,6 +85,7 @@ struct RopeAppendArgs {
   int64_t q_token_stride;    // elements
   double mscale;
   double inv_freq[kFusedRopePairs];
+  int32_t waves_per_token;   // set by launch_rope_append: 1, or 4 for a few tokens
 };
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 
