@@ -43,10 +43,13 @@ def _case(seed, T, paged, hq=24, hkv=4):
         # the first and last positions of the original window and of 2^20,
         # then distinct random pages
         special = np.array([0, 262143, 262144, (1 << 20) - 1])
-        rest = rng.choice(np.setdiff1d(np.arange(1 << 16), special // 16), size=T - 4,
+        if T < len(special):               # fewer tokens: the largest positions
+            special = special[len(special) - T:]
+        nrest = T - len(special)
+        rest = rng.choice(np.setdiff1d(np.arange(1 << 16), special // 16), size=nrest,
                           replace=False)
         pages = np.concatenate([special // 16, rest])
-        pos = np.concatenate([special, rest * 16 + rng.integers(0, 16, size=T - 4)])
+        pos = np.concatenate([special, rest * 16 + rng.integers(0, 16, size=nrest)])
         table = np.full(1 << 16, -1, dtype=np.int32)
         table[pages] = rng.permutation(T).astype(np.int32)
         blocks = T
@@ -129,14 +132,16 @@ def test_rope_append_matches_oracle(Y, fmt, paged, hq, hkv):
             assert np.array_equal(gc.reshape(-1).view(np.int8).reshape(c_ref.shape), c_ref)
 
 
+@pytest.mark.parametrize("T", [1, 257, 1000])
 @pytest.mark.parametrize("fmt", ["bf16", "nvfp4", "int8"])
-def test_rope_append_equals_separate_passes_bitwise(Y, fmt):
+def test_rope_append_equals_separate_passes_bitwise(Y, fmt, T):
     """The fused pass against rope (q, then k) and append on the same
-    inputs: every byte of the queries, the codes and the scales."""
+    inputs: every byte of the queries, the codes and the scales.  Up to 512
+    tokens a launch gives each token four waves (one token: a decode step),
+    beyond that one wave per token; both are covered."""
     kv = _FMT[fmt]
-    T = 257
-    _say(f"rope_append vs separate {fmt}")
-    q, k, v, pos, table, blocks = _case(1300 + kv, T, True)
+    _say(f"rope_append vs separate {fmt} T={T}")
+    q, k, v, pos, table, blocks = _case(1300 + kv + T, T, True)
     kS = vS = 0.0123 if kv == Y.KV_NVFP4 else None
     A = _layer(Y, kv, blocks, True, kS, vS)
     B = _layer(Y, kv, blocks, True, kS, vS)
